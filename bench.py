@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X sigmoid-routed MoE layer at the GLM-5 shape (one GPU).
+
+A step is one pass of the whole layer (router, top-k and gates, permutation, SwiGLU routed experts, shared
+expert, combine) over one batch of seeded synthetic tokens already resident in HBM. The default workload
+is the GLM-5-shape prefill (T = 8192 tokens, H 6144, 256 experts top-8, I = Is = 2048, scale 2.5); the
+GLM-5 decode step (T = 16) is measured in the same run and reported under "decode".
+
+Prints one JSON line. `value` is prefill tokens/s. `roofline` is the dominant kernel (the routed gate/up
+SwiGLU grouped GEMM): algorithmic FLOPs per launch / its mean launch time from HIP events recorded on the
+kernel's stream inside the timed region. `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at GLM-5 shape (prefill & decode); % peak MFMA / HBM BW"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+WEIGHT_NAMES = ("w1", "w3", "w2", "ws1", "ws3", "ws2")
+STAGES = ("shared", "router", "permute", "gate_up", "down", "combine")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(a, device):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+class Runner:
+    def __init__(self, m, cfg, dev_weights, host_tokens, device, two_streams):
+        import torch
+
+        self.m, self.cfg, self.w = m, cfg, dev_weights
+        self.x = to_dev_bf16(host_tokens["x"], device)
+        self.wr = to_dev_bf16(host_tokens["wr"], device)
+        self.b = torch.from_numpy(host_tokens["b"]).to(device)
+        T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+        self.out = torch.empty(T, H, dtype=torch.float32, device=device)
+        self.ids = torch.empty(T, k, dtype=torch.int32, device=device)
+        self.gates = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, dtype=torch.int32, device=device)
+        nbytes = m.moe_workspace_bytes(T, H, E, k, cfg.I, cfg.Is)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.s1 = torch.cuda.Stream(device) if two_streams else None
+
+    def step(self, events=None):
+        w = self.w
+        args = (self.x, self.wr, self.b, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"], self.cfg.k,
+                self.cfg.scale, self.out, self.ws, self.ids, self.gates, self.counts)
+        if events is None:
+            self.m.moe_forward(*args, stream_shared=self.s1)
+        else:
+            self.m.moe_forward_profiled(*args, events=events, stream_shared=self.s1)
+
+    def time(self, steps, warmup):
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        for row in ev:  # materialise the HIP events before the timed region
+            for e in row:
+                e.record()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            self.step(events=ev[i])
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        stages = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+                  for j, name in enumerate(STAGES)}
+        return ms, stages
+
+
+def gate_up_flops(cfg):
+    return 4 * cfg.T * cfg.k * cfg.H * cfg.I
+
+
+def layer_bytes(cfg, active):
+    """Algorithmic bytes of one layer pass: weights of the experts that got tokens, the shared expert, router
+    weight and bias, x once, out (fp32), ids and gates."""
+    return (active * 3 * cfg.H * cfg.I * 2 + 3 * cfg.H * cfg.Is * 2 + cfg.E * cfg.H * 2 + 4 * cfg.E
+            + 2 * cfg.T * cfg.H + 4 * cfg.T * cfg.H + 8 * cfg.T * cfg.k)
+
+
+def gate_up_bytes(cfg, active):
+    """Algorithmic bytes of one routed gate/up launch: W1 and W3 of the active experts, x once, h written."""
+    return active * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * cfg.T * cfg.k * cfg.I
+
+
+def cpu_baseline(cfg, host, budget_s):
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = np.arange(cfg.T, dtype=np.int32)
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    oracle.forward(host, cfg.k, cfg.scale, rows=rows[:1])
+    t1 = time.perf_counter() - t0
+    n = max(threads, int(budget_s / max(t1, 1e-3)) * threads)
+    n = min(n, cfg.T)
+    sample = np.sort(rng.choice(cfg.T, size=n, replace=False)).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.run_sharded(lambda rows: oracle.forward(host, cfg.k, cfg.scale, rows=rows), sample, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d seeded random tokens of the %s workload (T=%d), fp64 plain C, %d threads, %.1f s"
+                      % (n, cfg.name, cfg.T, threads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--single-stream", action="store_true", help="run the shared expert on the main stream")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this layer's hot path has no multi-GPU mode (see the sharding "
+              "design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sigmoid_routed_mixture_amd as m
+    import workloads as wl
+
+    device = torch.device("cuda", 0)
+    cfg_p = wl.BY_NAME["glm5_prefill"]
+    cfg_d = wl.BY_NAME["glm5_decode"]
+    log("generating GLM-5 expert weights on the host (%d threads)" % wl.host_threads())
+    t0 = time.perf_counter()
+    host_w = {n: wl.weight(cfg_p, n) for n in WEIGHT_NAMES}
+    dev_w = {n: to_dev_bf16(a, device) for n, a in host_w.items()}
+    torch.cuda.synchronize()
+    log("weights ready in %.1f s" % (time.perf_counter() - t0))
+    two = not args.single_stream
+
+    results = {}
+    for cfg, steps in ((cfg_p, args.steps), (cfg_d, args.decode_steps)):
+        host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
+        r = Runner(m, cfg, dev_w, host_t, device, two)
+        ms, stages = r.time(steps, args.warmup)
+        active = int((r.counts.cpu().numpy() > 0).sum())
+        results[cfg.name] = (ms, stages, active, host_t)
+        log("%s: %.4f ms/step, stages %s, active experts %d" % (cfg.name, ms, stages, active))
+        del r
+        torch.cuda.empty_cache()
+
+    ms_p, st_p, act_p, host_tp = results[cfg_p.name]
+    ms_d, st_d, act_d, _ = results[cfg_d.name]
+    gu_ms = st_p["gate_up"]
+    achieved = gate_up_flops(cfg_p) / (gu_ms * 1e-3) / 1e12
+    layer_tflops = cfg_p.flops() / (ms_p * 1e-3) / 1e12
+    dec_gbs = layer_bytes(cfg_d, act_d) / (ms_d * 1e-3) / 1e9
+    dec_gu_gbs = gate_up_bytes(cfg_d, act_d) / (st_d["gate_up"] * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": cfg_p.T / (ms_p * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_p,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg_p.name, "T": cfg_p.T, "H": cfg_p.H, "E": cfg_p.E, "k": cfg_p.k, "I": cfg_p.I,
+                   "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "kernel": "routed gate/up SwiGLU grouped GEMM", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None, "launch_ms": gu_ms},
+        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_BF16_TFLOPS,
+                  "gbs": layer_bytes(cfg_p, act_p) / (ms_p * 1e-3) / 1e9, "active_experts": act_p,
+                  "stages_ms": st_p},
+        "decode": {"workload": cfg_d.name, "T": cfg_d.T, "steps": args.decode_steps, "ms_per_step": ms_d,
+                   "tokens_per_s": cfg_d.T / (ms_d * 1e-3), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS,
+                   "active_experts": act_d, "stages_ms": st_d,
+                   "gate_up_roofline": {"bound": "hbm", "achieved": dec_gu_gbs, "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s", "frac": dec_gu_gbs / PEAK_HBM_GBS}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        host = dict(host_tp)
+        host.update(host_w)
+        log("timing the CPU oracle on a sample of %s" % cfg_p.name)
+        line["cpu_baseline"] = cpu_baseline(cfg_p, host, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

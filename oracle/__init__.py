@@ -38,8 +38,7 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build()
+            build()  # no-op unless the source is newer than the built library
             L = ctypes.CDLL(_LIB_PATH)
             p, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]

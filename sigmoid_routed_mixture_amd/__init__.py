@@ -1,0 +1,179 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) sigmoid-routed mixture-of-experts layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind the C ABI of
+include/moe.h. PyTorch supplies device memory and streams. The functions keep the C names:
+
+    moe_workspace_bytes(T, H, E, k, I, Is)
+    moe_permute_workspace_bytes(T, E)
+    moe_route(x, w_router, bias, k, scale, topk_ids, topk_gates, logits=None, stream=None)
+    moe_permute(topk_ids, E, counts, offsets, row_token, slot_row, workspace, x=None, x_perm=None, stream=None)
+    moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids=None,
+                topk_gates=None, expert_counts=None, stream=None, stream_shared=None)
+
+bf16 tensors are torch.bfloat16; ids and counts int32; gates, bias, logits and out float32. All tensors
+must be contiguous and on the same HIP device. A non-OK status raises MoEError with the library's text.
+If libmoe.so is missing this module raises at import: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoe.so is not built; run `python -m sigmoid_routed_mixture_amd._build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.moe_workspace_bytes.argtypes = [_i] * 6
+_lib.moe_workspace_bytes.restype = _sz
+_lib.moe_permute_workspace_bytes.argtypes = [_i, _i]
+_lib.moe_permute_workspace_bytes.restype = _sz
+_lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _f, _p, _p, _p, _p]
+_lib.moe_route.restype = _i
+_lib.moe_permute.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.moe_permute.restype = _i
+_lib.moe_forward.argtypes = [_p] * 9 + [_i] * 6 + [_f] + [_p] * 5 + [_sz, _p, _p]
+_lib.moe_forward.restype = _i
+_lib.moe_forward_profiled.argtypes = [_p] * 9 + [_i] * 6 + [_f] + [_p] * 5 + [_sz, _p, _p, _p]
+_lib.moe_forward_profiled.restype = _i
+_lib.moe_status_string.argtypes = [_i]
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_last_error.argtypes = []
+_lib.moe_last_error.restype = ctypes.c_char_p
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_route", "moe_permute",
+                    "moe_forward", "moe_forward_profiled", "moe_status_string", "moe_last_error")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = _lib.moe_status_string(status).decode()
+        detail = _lib.moe_last_error().decode()
+        super().__init__("%s (status %d)%s" % (msg, status, ": " + detail if detail else ""))
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(status)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    return t.data_ptr()
+
+
+def _stream(s, device):
+    if s is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def moe_workspace_bytes(T: int, H: int, E: int, k: int, I: int, Is: int) -> int:
+    return _lib.moe_workspace_bytes(T, H, E, k, I, Is)
+
+
+def moe_permute_workspace_bytes(T: int, E: int) -> int:
+    return _lib.moe_permute_workspace_bytes(T, E)
+
+
+def moe_route(x, w_router, bias, k, scale, topk_ids, topk_gates, logits=None, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    _check(_lib.moe_route(_ptr(x, torch.bfloat16, "x"), _ptr(w_router, torch.bfloat16, "w_router"),
+                          _ptr(bias, torch.float32, "bias"), T, H, E, k, float(scale),
+                          _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_gates, torch.float32, "topk_gates"),
+                          _ptr(logits, torch.float32, "logits"), _stream(stream, x.device)))
+
+
+def moe_permute(topk_ids, E, counts, offsets, row_token, slot_row, workspace, x=None, x_perm=None, stream=None):
+    T, k = topk_ids.shape
+    H = x.shape[1] if x is not None else (x_perm.shape[1] if x_perm is not None else 64)
+    _check(_lib.moe_permute(_ptr(x, torch.bfloat16, "x"), _ptr(topk_ids, torch.int32, "topk_ids"), T, H, E, k,
+                            _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+                            _ptr(row_token, torch.int32, "row_token"), _ptr(slot_row, torch.int32, "slot_row"),
+                            _ptr(x_perm, torch.bfloat16, "x_perm"), _ptr(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream, topk_ids.device)))
+
+
+def _forward(fn, extra, x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids,
+             topk_gates, expert_counts, stream, stream_shared):
+    T, H = x.shape
+    E, I, _ = w1.shape
+    Is = 0 if ws1 is None else ws1.shape[0]
+    bf = torch.bfloat16
+    s1 = None if stream_shared is None else _stream(stream_shared, x.device)
+    _check(fn(
+        _ptr(x, bf, "x"), _ptr(w_router, bf, "w_router"), _ptr(bias, torch.float32, "bias"), _ptr(w1, bf, "w1"),
+        _ptr(w3, bf, "w3"), _ptr(w2, bf, "w2"), _ptr(ws1, bf, "ws1"), _ptr(ws3, bf, "ws3"), _ptr(ws2, bf, "ws2"),
+        T, H, E, k, I, Is, float(scale), _ptr(out, torch.float32, "out"), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_gates, torch.float32, "topk_gates"), _ptr(expert_counts, torch.int32, "expert_counts"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, x.device), s1, *extra))
+
+
+def moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids=None,
+                topk_gates=None, expert_counts=None, stream=None, stream_shared=None):
+    _forward(_lib.moe_forward, (), x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids,
+             topk_gates, expert_counts, stream, stream_shared)
+
+
+def moe_forward_profiled(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, events,
+                         topk_ids=None, topk_gates=None, expert_counts=None, stream=None, stream_shared=None):
+    """moe_forward that also records seven torch.cuda.Event objects (timing enabled, already recorded once so
+    their HIP events exist) at the stage boundaries; see include/moe_profile.h."""
+    if len(events) != 7:
+        raise ValueError("moe_forward_profiled takes 7 events")
+    handles = (ctypes.c_void_p * 7)(*[e.cuda_event for e in events])
+    _forward(_lib.moe_forward_profiled, (handles,), x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out,
+             workspace, topk_ids, topk_gates, expert_counts, stream, stream_shared)
+
+
+class MoELayer:
+    """Convenience holder: weights plus a workspace sized for up to T_max tokens."""
+
+    def __init__(self, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k: int, scale: float, T_max: int):
+        self.w_router, self.bias = w_router, bias
+        self.w1, self.w3, self.w2 = w1, w3, w2
+        self.ws1, self.ws3, self.ws2 = ws1, ws3, ws2
+        self.k, self.scale = k, scale
+        E, I, H = w1.shape
+        Is = 0 if ws1 is None else ws1.shape[0]
+        nbytes = moe_workspace_bytes(T_max, H, E, k, I, Is)
+        if nbytes == 0:
+            raise ValueError("unsupported sizes")
+        self.T_max = T_max
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=w1.device)
+
+    def __call__(self, x, out=None, topk_ids=None, topk_gates=None, expert_counts=None, stream=None,
+                 stream_shared=None):
+        T, H = x.shape
+        if T > self.T_max:
+            raise ValueError("T exceeds the workspace's T_max")
+        if out is None:
+            out = torch.empty(T, H, dtype=torch.float32, device=x.device)
+        moe_forward(x, self.w_router, self.bias, self.w1, self.w3, self.w2, self.ws1, self.ws3, self.ws2, self.k,
+                    self.scale, out, self.workspace, topk_ids, topk_gates, expert_counts, stream, stream_shared)
+        return out

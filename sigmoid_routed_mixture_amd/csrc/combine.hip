@@ -1,0 +1,62 @@
+// Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t], in fp32 with
+// the k slots added in slot order, then the shared expert. One workgroup per token; each thread owns
+// 8-column chunks (16-byte bf16 loads, two 16-byte fp32 stores).
+// Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (y_routed = sum_i G_i E_i,
+// delta_ffn = y_routed + y_shared); nnterp encyclopedia glm_moe_dsa, "The mixture" (routed + shared == out).
+#include "common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ y_shared, int T, int H, int k,
+                                                      float* __restrict__ out) {
+    __shared__ float g[kMaxK];
+    __shared__ int rr[kMaxK];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < k) {
+        g[tid] = gates[(size_t)t * k + tid];
+        rr[tid] = slot_row[(size_t)t * k + tid];
+    }
+    __syncthreads();
+    for (int c = tid; c < H / 8; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int r = rr[j];
+            if (r < 0) continue;
+            const Pack16 v = load16(y + (size_t)r * H + c * 8);
+            const float gj = g[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += gj * __uint_as_float(v.w[i] << 16);
+                acc[2 * i + 1] += gj * __uint_as_float(v.w[i] & 0xFFFF0000u);
+            }
+        }
+        float* o = out + (size_t)t * H + c * 8;
+        if (y_shared) {
+            const float4 s0 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8);
+            const float4 s1 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8 + 4);
+            acc[0] += s0.x; acc[1] += s0.y; acc[2] += s0.z; acc[3] += s0.w;
+            acc[4] += s1.x; acc[5] += s1.y; acc[6] += s1.z; acc[7] += s1.w;
+        }
+        *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+} // namespace
+
+hipError_t launch_combine(const uint16_t* y, const float* gates, const int32_t* slot_row, const float* y_shared,
+                          int T, int H, int k, float* out, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    combine_kernel<<<T, 256, 0, stream>>>(y, gates, slot_row, y_shared, T, H, k, out);
+    return hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,50 @@
+// Launchers of the gfx950 kernels (host side). Each enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router: logits, sigmoid, biased top-k, gates. S > 1 with `partial` [S, T, E] fp32 splits the logit
+// GEMM over K (for few tokens); otherwise one fused kernel does everything.
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
+                         float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
+                         hipStream_t stream);
+
+// Permutation: per-chunk expert histograms, the prefix sums (and, when `tiles` is non-null, the list of
+// BM-row grouped-GEMM tiles), then the stable scatter of slots into expert-contiguous rows.
+// chunk_scratch holds ceil(T / 256) * E ints.
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
+                          int32_t* ntiles, int BM, hipStream_t stream);
+
+// x_perm[r] = x[row_token[r]] for r < offsets[E].
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* row_token, const int32_t* offsets, int E, int T,
+                              int H, int rows_max, uint16_t* x_perm, hipStream_t stream);
+
+// One grouped GEMM over the tile list (or, with counts == nullptr, one dense group of dense_rows rows).
+struct GemmArgs {
+    const uint16_t* act;       // activations [*, K] bf16
+    const int32_t* row_token;  // gather map row -> activation row (gate/up GEMM of routed experts), or null
+    const uint16_t* w_a;       // weights [groups][N][K] (down: W2; gate/up: W1)
+    const uint16_t* w_b;       // gate/up only: W3 [groups][N][K]
+    void* out;                 // [rows, N]: bf16 (h or per-slot outputs) or fp32
+    const int32_t* counts;     // rows per group, or null for one dense group
+    const int32_t* offsets;    // first row of each group
+    const int2* tiles;         // {group, first row in group} per tile
+    const int32_t* ntiles;     // number of valid tiles
+    int dense_rows;            // rows of the dense group
+    int N, K;                  // output width (gate/up: I, h columns), reduction length
+};
+enum class GemmKind { GateUp, Down, DownF32 };
+hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
+
+// out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]), fp32, slot order.
+hipError_t launch_combine(const uint16_t* y, const float* gates, const int32_t* slot_row, const float* y_shared,
+                          int T, int H, int k, float* out, hipStream_t stream);
+
+// Fills n ints with v.
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+
+} // namespace moe

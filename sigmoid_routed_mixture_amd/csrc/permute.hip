@@ -1,0 +1,165 @@
+// Permutation stage on gfx950: the T * k routing slots become expert-contiguous rows, ordered by token
+// within each expert (a stable counting sort). Work is split in chunks of 256 tokens: each chunk builds
+// an LDS bit matrix (expert x token-in-chunk), whose popcounts give the chunk's per-expert histogram and,
+// below a token's bit, that token's rank inside the chunk. One workgroup then turns the histograms into
+// per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles.
+// Pages: the routed experts receive (hidden, indices, weights) (nnterp encyclopedia glm_moe_dsa, support():
+// expert_indices and expert_weights are the experts' inputs); grouping rows by expert is how this build
+// hands each expert its tokens.
+#include "common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = kPermChunk;
+static_assert(kChunk == 256, "one thread per token of a chunk");
+
+__device__ __forceinline__ void build_mask(uint32_t (*mask)[8], const int32_t* __restrict__ ids, int T, int E,
+                                           int k) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kMaxE * 8; i += 256) mask[i >> 3][i & 7] = 0u;
+    __syncthreads();
+    const int t = blockIdx.x * kChunk + tid;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[(size_t)t * k + j];
+            if (e >= 0 && e < E) atomicOr(&mask[e][tid >> 5], 1u << (tid & 31));
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                         int32_t* __restrict__ chunk_counts) {
+    __shared__ uint32_t mask[kMaxE][8];
+    build_mask(mask, ids, T, E, k);
+    const int e = threadIdx.x;
+    if (e < E) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) c += __popc(mask[e][w]);
+        chunk_counts[(size_t)blockIdx.x * E + e] = c;
+    }
+}
+
+// Exclusive prefix sum over the 256 threads of a workgroup.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
+    const int tid = threadIdx.x;
+    sh[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int a = tid >= off ? sh[tid - off] : 0;
+        __syncthreads();
+        sh[tid] += a;
+        __syncthreads();
+    }
+    const int incl = sh[tid];
+    *total = sh[255];
+    __syncthreads();
+    return incl - v;
+}
+
+__global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int chunks, int E,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                        int BM) {
+    __shared__ int sh[256];
+    const int e = threadIdx.x;
+    int n = 0;
+    if (e < E) {
+        for (int c = 0; c < chunks; ++c) {
+            int32_t* p = chunk_counts + (size_t)c * E + e;
+            const int v = *p;
+            *p = n; // in place: becomes the chunk's base row inside expert e
+            n += v;
+        }
+        counts[e] = n;
+    }
+    int total = 0;
+    const int off = block_exclusive_scan(e < E ? n : 0, sh, &total);
+    if (e < E) offsets[e] = off;
+    if (e == 0) offsets[E] = total;
+    if (tiles == nullptr) return;
+    const int nt = (e < E && BM > 0) ? (n + BM - 1) / BM : 0;
+    int tiles_total = 0;
+    const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
+    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e, i * BM);
+    if (e == 0) ntiles[0] = tiles_total;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ row_token,
+                                                           int32_t* __restrict__ slot_row) {
+    __shared__ uint32_t mask[kMaxE][8];
+    build_mask(mask, ids, T, E, k);
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x * kChunk + tid;
+    if (t >= T) return;
+    const int w = tid >> 5;
+    const uint32_t below = (1u << (tid & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        if (e < 0 || e >= E) {
+            slot_row[(size_t)t * k + j] = -1;
+            continue;
+        }
+        int rank = __popc(mask[e][w] & below);
+        for (int v = 0; v < w; ++v) rank += __popc(mask[e][v]);
+        const int row = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e] + rank;
+        row_token[row] = t;
+        slot_row[(size_t)t * k + j] = row;
+    }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ offsets, int E, int T, int H,
+                                                          uint16_t* __restrict__ x_perm) {
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= offsets[E]) return;
+    const int t = row_token[r];
+    if (t < 0 || t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* src = x + (size_t)t * H;
+    uint16_t* dst = x_perm + (size_t)r * H;
+    for (int c = lane; c < H / 8; c += 64) store16(dst + c * 8, load16(src + c * 8));
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+} // namespace
+
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
+                          int32_t* ntiles, int BM, hipStream_t stream) {
+    const int chunks = (T + kChunk - 1) / kChunk;
+    perm_count_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, chunk_scratch);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    perm_scan_kernel<<<1, 256, 0, stream>>>(chunk_scratch, chunks, E, counts, offsets, tiles, ntiles, BM);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    perm_scatter_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, offsets, chunk_scratch, row_token, slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* row_token, const int32_t* offsets, int E, int T,
+                              int H, int rows_max, uint16_t* x_perm, hipStream_t stream) {
+    gather_rows_kernel<<<(rows_max + 3) / 4, 256, 0, stream>>>(x, row_token, offsets, E, T, H, x_perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(p, n, v);
+    return hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,87 @@
+// Host-side argument checks, launch planning and workspace layout (no HIP dependency).
+#include "plan.h"
+
+#include <algorithm>
+
+namespace moe {
+
+namespace {
+Check fail(moe_status s, std::string m) { return Check{s, std::move(m)}; }
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+} // namespace
+
+Check check_sizes(int T, int H, int E, int k, int I, int Is, bool need_I) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (H <= 0) return fail(MOE_ERR_INVALID_ARG, "H <= 0");
+    if (E <= 0) return fail(MOE_ERR_INVALID_ARG, "E <= 0");
+    if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k < 1");
+    if (k > E) return fail(MOE_ERR_INVALID_ARG, "k > E");
+    if (need_I && I <= 0) return fail(MOE_ERR_INVALID_ARG, "I <= 0");
+    if (need_I && Is < 0) return fail(MOE_ERR_INVALID_ARG, "Is < 0");
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E > 256");
+    if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k > 32");
+    if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "H is not a multiple of 64");
+    if (need_I && I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I is not a multiple of 64");
+    if (need_I && Is % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "Is is not a multiple of 64");
+    if ((int64_t)T * (int64_t)k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "T * k >= 2^31");
+    return Check{};
+}
+
+Check check_aligned(const void* p, const char* name, size_t align) {
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+        return fail(MOE_ERR_MISALIGNED, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+    return Check{};
+}
+
+int router_splits(int T, int H) {
+    const int64_t tblocks = (T + kRouterBT - 1) / kRouterBT;
+    const int chunks = H / 64;
+    int64_t s = (512 + tblocks - 1) / std::max<int64_t>(tblocks, 1); // aim at >= 512 workgroups
+    s = std::max<int64_t>(1, std::min<int64_t>(s, chunks));
+    return (int)s;
+}
+
+GemmPath gemm_path(int T, int E, int k) {
+    return (int64_t)T * k <= (int64_t)kSkinnyBM * E ? GemmPath::Skinny : GemmPath::Wide;
+}
+
+int64_t max_tiles(int T, int E, int k, int BM) {
+    const int64_t slots = (int64_t)T * k;
+    return (slots + BM - 1) / BM + std::min<int64_t>(E, slots);
+}
+
+Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return at;
+    };
+    const size_t Tk = (size_t)T * (size_t)k;
+    const int BM = gemm_path(T, E, k) == GemmPath::Wide ? kWideBM : kSkinnyBM;
+    const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
+    L.ids = take(Tk * 4);
+    L.gates = take(Tk * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take(((size_t)E + 1) * 4);
+    L.row_token = take(Tk * 4);
+    L.slot_row = take(Tk * 4);
+    L.chunk_base = take(chunks * (size_t)E * 4);
+    L.tiles = take((size_t)max_tiles(T, E, k, BM) * 8);
+    L.ntiles = take(4);
+    L.partial = take((size_t)router_splits(T, H) * (size_t)T * (size_t)E * 4);
+    L.h_perm = take(Tk * (size_t)I * 2);
+    L.y_perm = take(Tk * (size_t)H * 2);
+    L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
+    L.y_sh = Is > 0 ? take((size_t)T * (size_t)H * 4) : size_t(-1);
+    L.total = off;
+    return L;
+}
+
+size_t permute_scratch_bytes(int T, int E) {
+    const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
+    return align_up(std::max<size_t>(chunks * (size_t)E * 4, 1), 256);
+}
+
+} // namespace moe

@@ -1,0 +1,49 @@
+// Host-side argument checks, launch planning and workspace layout of the MoE layer.
+// Pure C++: no HIP types or calls, so every rule here runs (and is tested) without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "moe.h"
+
+namespace moe {
+
+// Tile shapes the kernels are built for (the kernels static_assert against these).
+constexpr int kWideBM = 128;    // tokens per tile of the LDS-tiled grouped GEMM
+constexpr int kSkinnyBM = 16;   // tokens per tile of the weight-streaming grouped GEMM
+constexpr int kRouterBT = 32;   // tokens per router workgroup
+constexpr int kPermChunk = 256; // tokens per permutation chunk
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 32;
+
+enum class GemmPath { Wide, Skinny };
+
+struct Check {
+    moe_status status = MOE_OK;
+    std::string message;
+    bool ok() const { return status == MOE_OK; }
+};
+
+// Size rules shared by every entry point. I and Is are ignored when negative-one (router/permute).
+Check check_sizes(int T, int H, int E, int k, int I, int Is, bool need_I);
+Check check_aligned(const void* p, const char* name, size_t align = 16);
+
+// K-split of the router's logit GEMM: the number of K ranges (each a whole number of 64-wide chunks).
+int router_splits(int T, int H);
+// Weight-streaming kernel when experts average at most 16 rows, else the LDS-tiled one.
+GemmPath gemm_path(int T, int E, int k);
+// Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
+int64_t max_tiles(int T, int E, int k, int BM);
+
+struct Layout {
+    // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
+    size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,
+        y_perm, h_sh, y_sh;
+    size_t total;
+};
+Layout forward_layout(int T, int H, int E, int k, int I, int Is);
+size_t permute_scratch_bytes(int T, int E);
+
+} // namespace moe

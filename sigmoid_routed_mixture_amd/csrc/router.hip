@@ -1,0 +1,249 @@
+// Router of the sigmoid-routed MoE layer on gfx950: logits z = x W_r (bf16 MFMA, fp32 accumulation),
+// s = sigmoid(z), c = s + b, top-k of c per token (ties to the lower expert index) and the gates
+// G = scale * s / sum of the chosen s.
+// Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (z = x W_r, s = sigma(z),
+// E_sel = [i in top_8(s + b)], G_i = 2.5 s_i E_sel_i / sum_j s_j E_sel_j); nnterp encyclopedia glm_moe_dsa,
+// "The mixture" (the bias is added to the sigmoids only to choose; gates renormalised, times the scale).
+#include "common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBT = kRouterBT; // tokens per workgroup: two 16-token MFMA column blocks
+static_assert(kBT == 32, "router tiling assumes 32 tokens per workgroup");
+
+// Accumulates z for tokens [t0, t0 + 32) and experts [64 w, 64 w + 64) of wave w over the 64-wide
+// K chunks [c0, c1). acc[b][j]: expert block b (16 experts), token block j (16 tokens); lane l holds
+// experts 16 b + 4 (l / 16) + r and token 16 j + l % 16 in element r.
+// Each lane reads 32 contiguous bytes per row per chunk (k-group l / 16 covers k 16 g .. 16 g + 15) and
+// feeds the first 8 values to one MFMA and the next 8 to a second; x and W_r use the same k mapping, so
+// the pair of MFMAs sums all 64 products of the chunk.
+__device__ __forceinline__ void router_accumulate(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                  int T, int H, int E, int t0, int c0, int c1, f32x4 (&acc)[4][2]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rl = lane & 15;
+    const int kg = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int e_base = wave * 64;
+    if (e_base >= E) return;
+    int nb = (E - e_base + 15) / 16;
+    nb = nb > 4 ? 4 : nb;
+    const uint16_t* wrow[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        int e = e_base + b * 16 + rl;
+        e = e < E ? e : E - 1;
+        wrow[b] = wr + (size_t)e * H + kg * 16;
+    }
+    const uint16_t* xrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int t = t0 + j * 16 + rl;
+        t = t < T ? t : T - 1;
+        xrow[j] = x + (size_t)t * H + kg * 16;
+    }
+    for (int c = c0; c < c1; ++c) {
+        const int k = c * 64;
+        Pack16 xa[2], xb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            xa[j] = load16(xrow[j] + k);
+            xb[j] = load16(xrow[j] + k + 8);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b < nb) {
+                const Pack16 wa = load16(wrow[b] + k);
+                const Pack16 wb = load16(wrow[b] + k + 8);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[b][j] = mfma16x16x32(wa, xa[j], acc[b][j]);
+                    acc[b][j] = mfma16x16x32(wb, xb[j], acc[b][j]);
+                }
+            }
+        }
+    }
+}
+
+// Orderable key of a biased score: larger c first, then the lower expert index. 0 = no candidate.
+__device__ __forceinline__ uint64_t score_key(float c, int e) {
+    uint32_t u = __float_as_uint(c);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// One wave routes one token. z4[q] is the logit of expert lane + 64 q (ignored when that is >= E).
+__device__ __forceinline__ void topk_token(const float (&z4)[4], int t, int E, int k, float scale,
+                                           const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                           float* __restrict__ gates, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    float s4[4];
+    uint64_t key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        if (e < E) {
+            const float s = 1.0f / (1.0f + expf(-z4[q]));
+            s4[q] = s;
+            key[q] = score_key(s + bias[e], e);
+            if (logits) logits[(size_t)t * E + e] = z4[q];
+        } else {
+            s4[q] = 0.f;
+            key[q] = 0;
+        }
+    }
+    int my_id = 0;
+    float my_s = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xFFFFu - (uint32_t)(best & 0xFFFFu));
+        const int owner = e & 63;
+        const int qw = e >> 6;
+        float sq = s4[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) sq = qw == q ? s4[q] : sq;
+        const float s_w = __shfl(sq, owner, 64);
+        if (lane == owner) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q == qw) key[q] = 0;
+        }
+        if (lane == j) {
+            my_id = e;
+            my_s = s_w;
+        }
+    }
+    const float den = wave_sum(lane < k ? my_s : 0.f);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_id;
+        gates[(size_t)t * k + lane] = den > 0.f ? scale * my_s / den : 0.f;
+    }
+}
+
+// Whole router in one workgroup per 32 tokens: full-K logits into LDS, then 8 tokens per wave.
+__global__ __launch_bounds__(256) void router_fused_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, int T, int H, int E,
+                                                           int k, float scale, int32_t* __restrict__ ids,
+                                                           float* __restrict__ gates, float* __restrict__ logits) {
+    __shared__ float zs[kBT][kMaxE + 4];
+    const int t0 = blockIdx.x * kBT;
+    f32x4 acc[4][2];
+    router_accumulate(x, wr, T, H, E, t0, 0, H / 64, acc);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = wave * 64 + b * 16 + 4 * (lane >> 4) + r;
+                const int tl = j * 16 + (lane & 15);
+                if (e < E) zs[tl][e] = acc[b][j][r];
+            }
+    __syncthreads();
+    for (int tl = wave; tl < kBT; tl += 4) {
+        const int t = t0 + tl;
+        if (t >= T) break;
+        float z4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            z4[q] = e < E ? zs[tl][e] : 0.f;
+        }
+        topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
+    }
+}
+
+// K-split logits for small T: split s of S covers 64-wide chunks [s C / S, (s + 1) C / S).
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wr, int T, int H, int E,
+                                                             int S, float* __restrict__ partial) {
+    const int t0 = blockIdx.x * kBT;
+    const int s = blockIdx.y;
+    const int C = H / 64;
+    const int c0 = (int)((int64_t)s * C / S), c1 = (int)((int64_t)(s + 1) * C / S);
+    f32x4 acc[4][2];
+    router_accumulate(x, wr, T, H, E, t0, c0, c1, acc);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float* dst = partial + (size_t)s * T * E;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + j * 16 + (lane & 15);
+            if (t >= T) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = wave * 64 + b * 16 + 4 * (lane >> 4) + r;
+                if (e < E) dst[(size_t)t * E + e] = acc[b][j][r];
+            }
+        }
+}
+
+// Sums the S partial logits of each token in split order, then routes it (one wave per token).
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int S,
+                                                          const float* __restrict__ bias, int T, int E, int k,
+                                                          float scale, int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates, float* __restrict__ logits) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    float z4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        float z = 0.f;
+        if (e < E)
+            for (int s = 0; s < S; ++s) z += partial[((size_t)s * T + t) * E + e];
+        z4[q] = z;
+    }
+    topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
+}
+
+} // namespace
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
+                         float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
+                         hipStream_t stream) {
+    const int tblocks = (T + kBT - 1) / kBT;
+    if (S <= 1 || partial == nullptr) {
+        router_fused_kernel<<<tblocks, 256, 0, stream>>>(x, wr, bias, T, H, E, k, scale, ids, gates, logits);
+        return hipGetLastError();
+    }
+    router_partial_kernel<<<dim3(tblocks, S), 256, 0, stream>>>(x, wr, T, H, E, S, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    router_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(partial, S, bias, T, E, k, scale, ids, gates, logits);
+    return hipGetLastError();
+}
+
+} // namespace moe

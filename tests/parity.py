@@ -1,0 +1,114 @@
+"""Helpers of the GPU parity tests: host inputs -> device tensors, the oracle on host threads, and the
+comparison rules.
+
+Rules (from the layer's acceptance bar):
+* expert selection is compared as id sets per token, bit-exact, except tokens whose oracle k-th and
+  (k+1)-th biased scores differ by less than NEAR_TIE (counted and reported);
+* per-expert counts are bit-exact wherever no near-tie token changed its set;
+* outputs: max |gpu - oracle| <= OUT_TOL * RMS(oracle output) over every token whose id set matches.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+NEAR_TIE = 1e-5
+OUT_TOL = 2e-2
+GATE_RTOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_device(host: dict, device="cuda") -> dict:
+    out = {}
+    for key, v in host.items():
+        if v is None:
+            out[key] = None
+        elif v.dtype == np.uint16:
+            out[key] = dev_bf16(v, device)
+        else:
+            out[key] = dev(v, device)
+    return out
+
+
+def oracle_route_all(h: dict, k: int, scale: float):
+    T = h["x"].shape[0]
+    return oracle.run_sharded(lambda rows: oracle.route(h["x"], h["wr"], h["b"], k, scale, rows=rows), np.arange(T))
+
+
+def oracle_forward_rows(h: dict, k: int, scale: float, rows):
+    return oracle.run_sharded(lambda rows: oracle.forward(h, k, scale, rows=rows), np.asarray(rows))
+
+
+def compare_routing(ids_gpu, gates_gpu, ref, label=""):
+    """Returns (mask of tokens whose sets agree, number of near-tie tokens, number of those that differ)."""
+    ids_gpu = np.asarray(ids_gpu)
+    gates_gpu = np.asarray(gates_gpu)
+    near = ref["gap"] < NEAR_TIE
+    sg = np.sort(ids_gpu, axis=1)
+    so = np.sort(ref["ids"], axis=1)
+    same = np.all(sg == so, axis=1)
+    bad = ~same & ~near
+    assert not bad.any(), "%s: %d tokens chose other experts outside the near-tie band (first %s)" % (
+        label, bad.sum(), np.nonzero(bad)[0][:8])
+    # every gpu id is a valid, distinct expert
+    assert ids_gpu.min() >= 0
+    assert np.all(np.diff(sg, axis=1) > 0), "%s: repeated expert within a token" % label
+    # gates per expert id, on agreeing tokens
+    og = np.argsort(ids_gpu, axis=1)
+    oo = np.argsort(ref["ids"], axis=1)
+    gg = np.take_along_axis(gates_gpu, og, axis=1)[same]
+    go = np.take_along_axis(ref["gates"], oo, axis=1)[same]
+    assert np.allclose(gg, go, rtol=GATE_RTOL, atol=1e-7), "%s: gates differ (max %g)" % (
+        label, np.abs(gg - go).max())
+    return same, int(near.sum()), int((near & ~same).sum())
+
+
+def compare_out(out_gpu, out_ref, label=""):
+    out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    out_ref = np.asarray(out_ref, dtype=np.float64)
+    assert np.all(np.isfinite(out_gpu)), "%s: non-finite output" % label
+    rms = float(np.sqrt(np.mean(out_ref ** 2)))
+    err = float(np.max(np.abs(out_gpu - out_ref))) if out_ref.size else 0.0
+    ratio = err / rms if rms > 0 else err
+    say("  %s: max|err| = %.3e, RMS = %.3e, ratio = %.4f (limit %.3f)" % (label, err, rms, ratio, OUT_TOL))
+    assert ratio <= OUT_TOL, "%s: max|err|/RMS = %.4f > %.3f" % (label, ratio, OUT_TOL)
+    return ratio
+
+
+def sample_rows(ids_ref, n_random: int, seed: int = 0):
+    """A seeded sample of tokens plus, for every expert that got any token, the first token routed to it."""
+    T = ids_ref.shape[0]
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    flat = ids_ref.ravel()
+    seen = {}
+    for i, e in enumerate(flat):
+        if e not in seen:
+            seen[int(e)] = i // ids_ref.shape[1]
+    pick |= set(seen.values())
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+def config_host(cfg: wl.MoEConfig, weights: dict | None = None) -> dict:
+    h = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
+    if weights is None:
+        weights = {n: wl.weight(cfg, n) for n in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
+    h.update(weights)
+    return h

@@ -54,8 +54,7 @@ def lib():
     global _lib
     with _lib_lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build()
+            build()  # no-op unless the source is newer than the built library
             L = ctypes.CDLL(_LIB_PATH)
             u64, u32, i32, dbl = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_double
             p = ctypes.c_void_p
@@ -88,10 +87,17 @@ class MoEConfig:
     Is: int
     scale: float
     skewed: bool = False
+    weights_of: int = -1  # index of the workload whose expert weights this one shares (-1: its own)
 
     @property
     def seed(self) -> int:
+        """Seed of the tokens, router weight and bias."""
         return 0x5EED0000 + self.index
+
+    @property
+    def weight_seed(self) -> int:
+        """Seed of the routed and shared expert weights."""
+        return 0x5EED0000 + (self.index if self.weights_of < 0 else self.weights_of)
 
     def with_(self, **kw) -> "MoEConfig":
         d = dict(self.__dict__)
@@ -107,9 +113,12 @@ CONFIGS = [
     MoEConfig(0, "tiny", T=64, H=256, E=16, k=4, I=128, Is=128, scale=2.5),
     MoEConfig(1, "mid", T=4096, H=2048, E=64, k=4, I=1536, Is=1536, scale=1.0),
     MoEConfig(2, "glm5_decode", T=16, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5),
-    MoEConfig(3, "glm5_prefill", T=8192, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5),
-    MoEConfig(4, "glm5_skewed", T=32768, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5, skewed=True),
+    MoEConfig(3, "glm5_prefill", T=8192, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5, weights_of=2),
+    MoEConfig(4, "glm5_skewed", T=32768, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5, skewed=True,
+              weights_of=2),
 ]
+# The three GLM-5 workloads are one layer (one set of expert weights, 19.3 GB of routed experts) run on
+# three token batches; each has its own tokens, router weight and bias.
 BY_NAME = {c.name: c for c in CONFIGS}
 
 
@@ -170,7 +179,7 @@ def weight_shapes(cfg: MoEConfig) -> dict:
 
 
 def weight(cfg: MoEConfig, name: str, seed: int | None = None) -> np.ndarray:
-    seed = cfg.seed if seed is None else seed
+    seed = cfg.weight_seed if seed is None else seed
     tid, shape = weight_shapes(cfg)[name]
     n = int(np.prod(shape))
     return normal_bf16(seed, tid, SIGMA_W, 0, n).reshape(shape)
@@ -181,7 +190,7 @@ def host_inputs(cfg: MoEConfig, seed: int | None = None, with_weights: bool = Tr
     d = {"x": tokens(cfg, seed), "wr": router_weight(cfg, seed), "b": selection_bias(cfg, seed)}
     if with_weights:
         for name in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
-            d[name] = weight(cfg, name, seed)
+            d[name] = weight(cfg, name, None if seed is None else seed)
     return d
 
 
@@ -193,6 +202,7 @@ def device_inputs(cfg: MoEConfig, device, seed: int | None = None, chunk_elems: 
     """
     import torch
 
+    wseed = cfg.weight_seed if seed is None else seed
     seed = cfg.seed if seed is None else seed
     out = {}
     small = {"x": tokens(cfg, seed) if cfg.T * cfg.H <= chunk_elems else None,
@@ -203,12 +213,12 @@ def device_inputs(cfg: MoEConfig, device, seed: int | None = None, chunk_elems: 
     stage = torch.empty(chunk_elems, dtype=torch.int16, pin_memory=True)
     stage_np = stage.numpy().view(np.uint16)
 
-    def fill(tid, sigma, shape):
+    def fill(tid, sigma, shape, fseed=seed):
         n = int(np.prod(shape))
         dst = torch.empty(n, dtype=torch.bfloat16, device=device)
         for s in range(0, n, chunk_elems):
             c = min(chunk_elems, n - s)
-            normal_bf16(seed, tid, sigma, s, c, out=stage_np[:c])
+            normal_bf16(fseed, tid, sigma, s, c, out=stage_np[:c])
             dst[s:s + c].copy_(stage[:c].view(torch.bfloat16), non_blocking=True)
             torch.cuda.current_stream(device).synchronize()
         return dst.view(shape)
@@ -218,7 +228,7 @@ def device_inputs(cfg: MoEConfig, device, seed: int | None = None, chunk_elems: 
     else:
         out["x"] = fill(T_X, 1.0, (cfg.T, cfg.H))
     for name, (tid, shape) in weight_shapes(cfg).items():
-        out[name] = fill(tid, SIGMA_W, shape)
+        out[name] = fill(tid, SIGMA_W, shape, wseed)
     torch.cuda.synchronize(device)
     return out
 

@@ -113,9 +113,26 @@ typedef struct {
 static void* run_job(void* p) {
     job_t* j = (job_t*)p;
     if (j->kind == 0) {
+        /* bf16(sigma * q[u]) for all 65536 u, then one lookup per element */
+        uint16_t* lut = (uint16_t*)malloc(65536 * sizeof(uint16_t));
         uint16_t* o = (uint16_t*)j->out;
-        for (uint64_t i = 0; i < j->count; ++i)
-            o[i] = gen_bf16_from_double(j->a * normal_at(j->key, j->start + i));
+        if (lut) {
+            for (int u = 0; u < 65536; ++u) lut[u] = gen_bf16_from_double(j->a * g_quantile[u]);
+            uint64_t i = 0;
+            for (; i < j->count && ((j->start + i) & 3); ++i) o[i] = gen_bf16_from_double(j->a * normal_at(j->key, j->start + i));
+            for (; i + 4 <= j->count; i += 4) {
+                uint64_t w = word_of(j->key, (j->start + i) >> 2);
+                o[i] = lut[w & 0xFFFF];
+                o[i + 1] = lut[(w >> 16) & 0xFFFF];
+                o[i + 2] = lut[(w >> 32) & 0xFFFF];
+                o[i + 3] = lut[w >> 48];
+            }
+            for (; i < j->count; ++i) o[i] = gen_bf16_from_double(j->a * normal_at(j->key, j->start + i));
+            free(lut);
+        } else {
+            for (uint64_t i = 0; i < j->count; ++i)
+                o[i] = gen_bf16_from_double(j->a * normal_at(j->key, j->start + i));
+        }
     } else {
         float* o = (float*)j->out;
         for (uint64_t i = 0; i < j->count; ++i) {
