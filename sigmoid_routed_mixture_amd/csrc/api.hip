@@ -192,6 +192,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     r1.offsets = offsets;
     r1.tiles = tiles;
     r1.ntiles = ntiles;
+    r1.groups = E;
     r1.N = I;
     r1.K = H;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, r1, grid_tiles, s0), "routed gate/up GEMM");
@@ -204,6 +205,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     r2.offsets = offsets;
     r2.tiles = tiles;
     r2.ntiles = ntiles;
+    r2.groups = E;
     r2.N = H;
     r2.K = I;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::Down, wide, r2, grid_tiles, s0), "routed down GEMM");

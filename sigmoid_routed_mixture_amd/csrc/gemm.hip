@@ -42,6 +42,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
     }
     if (mtile >= a.ntiles[0]) return false;
     const int2 t = a.tiles[mtile];
+    if (t.x < 0 || t.x >= a.groups || t.y < 0) return false;
     ti.g = t.x;
     ti.m0 = t.y;
     ti.off = a.offsets[t.x];

@@ -35,6 +35,7 @@ struct GemmArgs {
     const int2* tiles;         // {group, first row in group} per tile
     const int32_t* ntiles;     // number of valid tiles
     int dense_rows;            // rows of the dense group
+    int groups;                // number of groups (routed experts); tiles naming another group are skipped
     int N, K;                  // output width (gate/up: I, h columns), reduction length
 };
 enum class GemmKind { GateUp, Down, DownF32 };

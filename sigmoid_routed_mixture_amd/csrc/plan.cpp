@@ -59,7 +59,6 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
         return at;
     };
     const size_t Tk = (size_t)T * (size_t)k;
-    const int BM = gemm_path(T, E, k) == GemmPath::Wide ? kWideBM : kSkinnyBM;
     const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
     L.ids = take(Tk * 4);
     L.gates = take(Tk * 4);
@@ -68,7 +67,8 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
     L.row_token = take(Tk * 4);
     L.slot_row = take(Tk * 4);
     L.chunk_base = take(chunks * (size_t)E * 4);
-    L.tiles = take((size_t)max_tiles(T, E, k, BM) * 8);
+    // room for the longest tile list either grouped-GEMM kernel can ask for (the smallest BM)
+    L.tiles = take((size_t)max_tiles(T, E, k, std::min(kWideBM, kSkinnyBM)) * 8);
     L.ntiles = take(4);
     L.partial = take((size_t)router_splits(T, H) * (size_t)T * (size_t)E * 4);
     L.h_perm = take(Tk * (size_t)I * 2);
