@@ -28,7 +28,8 @@
  *  - The caller owns every buffer and stream. The library never allocates or frees device memory and
  *    never copies to the host. Its only state is one pair of HIP events per device, made on first use.
  *  - Arguments are checked before anything is enqueued: a call that returns an error has no effect.
- *    T == 0 returns MOE_OK and enqueues nothing. Non-finite inputs are outside the contract.
+ *    T == 0 returns MOE_OK once the sizes pass their checks, without looking at any pointer, and
+ *    enqueues nothing. Non-finite inputs are outside the contract.
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H, I and Is multiples of 64, T * k < 2^31.
  *  - Calls on one stream run in order; overlapping calls that share output or workspace buffers race.
  */
@@ -111,8 +112,8 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
  *                                routed experts; it waits for work already on `stream` and `stream` waits
  *                                for it before the combine. NULL runs the shared expert on `stream`.
  * Expert GEMMs take bf16 operands with fp32 accumulation; the SwiGLU activation h is stored as bf16
- * between the two GEMMs; per-slot expert outputs are stored as bf16; the combine sums the k gated slots
- * in slot order plus the shared expert in fp32.
+ * between the two GEMMs (it is the down GEMM's bf16 MFMA operand); per-slot expert outputs are fp32;
+ * the combine sums the k gated slots in slot order plus the shared expert in fp32.
  * Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (g = x W1, u = x W3,
  * a = g sigma(g), h = a * u, E_i = h W2, y_routed = sum G_i E_i, the shared expert, delta_ffn =
  * y_routed + y_shared); nnterp glm_moe_dsa "The mixture" (routed + shared == mlp_output).

@@ -94,6 +94,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
                         size_t workspace_bytes, void* stream, void* stream_shared, void* const* events) {
     g_last_error.clear();
     MOE_TRY(from_check(moe::check_sizes(T, H, E, k, I, Is, true)));
+    if (T == 0) return MOE_OK;
     MOE_TRY(need(x, "x"));
     MOE_TRY(need(w_router, "w_router"));
     MOE_TRY(need(bias, "bias"));
@@ -126,7 +127,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     int2* tiles = static_cast<int2*>(at(L.tiles));
     int32_t* ntiles = static_cast<int32_t*>(at(L.ntiles));
     uint16_t* h_perm = static_cast<uint16_t*>(at(L.h_perm));
-    uint16_t* y_perm = static_cast<uint16_t*>(at(L.y_perm));
+    float* y_perm = static_cast<float*>(at(L.y_perm));
     uint16_t* h_sh = Is > 0 ? static_cast<uint16_t*>(at(L.h_sh)) : nullptr;
     float* y_sh = Is > 0 ? static_cast<float*>(at(L.y_sh)) : nullptr;
 
@@ -208,7 +209,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     r2.groups = E;
     r2.N = H;
     r2.K = I;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::Down, wide, r2, grid_tiles, s0), "routed down GEMM");
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
@@ -249,6 +250,7 @@ moe_status moe_route(const moe_bf16* x, const moe_bf16* w_router, const float* b
                      float scale, int32_t* topk_ids, float* topk_gates, float* logits, void* stream) {
     g_last_error.clear();
     MOE_TRY(from_check(moe::check_sizes(T, H, E, k, 0, 0, false)));
+    if (T == 0) return MOE_OK;
     MOE_TRY(need(x, "x"));
     MOE_TRY(need(w_router, "w_router"));
     MOE_TRY(need(bias, "bias"));
@@ -267,6 +269,7 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
                        size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     MOE_TRY(from_check(moe::check_sizes(T, H, E, k, 0, 0, false)));
+    if (T == 0) return MOE_OK;
     MOE_TRY(need(topk_ids, "topk_ids"));
     MOE_TRY(need(counts, "counts"));
     MOE_TRY(need(offsets, "offsets"));

@@ -1,6 +1,6 @@
 // Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t], in fp32 with
-// the k slots added in slot order, then the shared expert. One workgroup per token; each thread owns
-// 8-column chunks (16-byte bf16 loads, two 16-byte fp32 stores).
+// the k slots added in slot order, then the shared expert. The per-slot expert outputs y are fp32 rows.
+// One workgroup per token; each thread owns 8-column chunks (16-byte loads and stores).
 // Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (y_routed = sum_i G_i E_i,
 // delta_ffn = y_routed + y_shared); nnterp encyclopedia glm_moe_dsa, "The mixture" (routed + shared == out).
 #include "common.h"
@@ -10,7 +10,7 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ gates,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ y_shared, int T, int H, int k,
                                                       float* __restrict__ out) {
@@ -30,13 +30,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         for (int j = 0; j < k; ++j) {
             const int r = rr[j];
             if (r < 0) continue;
-            const Pack16 v = load16(y + (size_t)r * H + c * 8);
+            const float4 v0 = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8);
+            const float4 v1 = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8 + 4);
             const float gj = g[j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += gj * __uint_as_float(v.w[i] << 16);
-                acc[2 * i + 1] += gj * __uint_as_float(v.w[i] & 0xFFFF0000u);
-            }
+            acc[0] += gj * v0.x; acc[1] += gj * v0.y; acc[2] += gj * v0.z; acc[3] += gj * v0.w;
+            acc[4] += gj * v1.x; acc[5] += gj * v1.y; acc[6] += gj * v1.z; acc[7] += gj * v1.w;
         }
         float* o = out + (size_t)t * H + c * 8;
         if (y_shared) {
@@ -52,7 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 } // namespace
 
-hipError_t launch_combine(const uint16_t* y, const float* gates, const int32_t* slot_row, const float* y_shared,
+hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
                           int T, int H, int k, float* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     combine_kernel<<<T, 256, 0, stream>>>(y, gates, slot_row, y_shared, T, H, k, out);

@@ -42,7 +42,7 @@ enum class GemmKind { GateUp, Down, DownF32 };
 hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]), fp32, slot order.
-hipError_t launch_combine(const uint16_t* y, const float* gates, const int32_t* slot_row, const float* y_shared,
+hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
                           int T, int H, int k, float* out, hipStream_t stream);
 
 // Fills n ints with v.

@@ -72,7 +72,7 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
     L.ntiles = take(4);
     L.partial = take((size_t)router_splits(T, H) * (size_t)T * (size_t)E * 4);
     L.h_perm = take(Tk * (size_t)I * 2);
-    L.y_perm = take(Tk * (size_t)H * 2);
+    L.y_perm = take(Tk * (size_t)H * 4);
     L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
     L.y_sh = Is > 0 ? take((size_t)T * (size_t)H * 4) : size_t(-1);
     L.total = off;

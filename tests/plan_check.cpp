@@ -46,7 +46,7 @@ int main() {
                                 {L.slot_row, Tk * 4, "slot_row"}, {L.chunk_base, chunks * E * 4, "chunk_base"},
                                 {L.tiles, tiles_need, "tiles"}, {L.ntiles, 4, "ntiles"},
                                 {L.partial, (size_t)moe::router_splits(T, H) * T * E * 4, "partial"},
-                                {L.h_perm, Tk * I * 2, "h_perm"}, {L.y_perm, Tk * H * 2, "y_perm"}};
+                                {L.h_perm, Tk * I * 2, "h_perm"}, {L.y_perm, Tk * H * 4, "y_perm"}};
                             if (Is > 0) {
                                 rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
                                 rs.push_back({L.y_sh, (size_t)T * H * 4, "y_sh"});
