@@ -61,11 +61,12 @@ class Runner:
     def step(self, events=None):
         w = self.w
         args = (self.x, self.wr, self.b, w["w1"], w["w3"], w["w2"], w["ws1"], w["ws3"], w["ws2"], self.cfg.k,
-                self.cfg.scale, self.out, self.ws, self.ids, self.gates, self.counts)
+                self.cfg.scale, self.out, self.ws)
+        kw = dict(topk_ids=self.ids, topk_gates=self.gates, expert_counts=self.counts, stream_shared=self.s1)
         if events is None:
-            self.m.moe_forward(*args, stream_shared=self.s1)
+            self.m.moe_forward(*args, **kw)
         else:
-            self.m.moe_forward_profiled(*args, events=events, stream_shared=self.s1)
+            self.m.moe_forward_profiled(*args, events, **kw)
 
     def time(self, steps, warmup):
         import torch
