@@ -28,7 +28,7 @@ METRIC = "MoE-layer tokens/s at GLM-5 shape (prefill & decode); % peak MFMA / HB
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 WEIGHT_NAMES = ("w1", "w3", "w2", "ws1", "ws3", "ws2")
-STAGES = ("shared", "router", "permute", "gate_up", "down", "combine")
+STAGES = ("router", "permute", "shared", "gate_up", "down", "combine")
 
 
 def log(*a):
@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--single-stream", action="store_true", help="run the shared expert on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--profile-only", choices=["prefill", "decode"], default=None,
+                    help="run only this workload's timed steps and print its timings (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer's hot path has no multi-GPU mode (see the sharding "
@@ -159,7 +161,10 @@ def main():
     two = not args.single_stream
 
     results = {}
-    for cfg, steps in ((cfg_p, args.steps), (cfg_d, args.decode_steps)):
+    plan = ((cfg_p, args.steps), (cfg_d, args.decode_steps))
+    if args.profile_only:
+        plan = tuple(p for p in plan if p[0].name.endswith(args.profile_only))
+    for cfg, steps in plan:
         host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
         r = Runner(m, cfg, dev_w, host_t, device, two)
         ms, stages = r.time(steps, args.warmup)
@@ -169,6 +174,8 @@ def main():
         del r
         torch.cuda.empty_cache()
 
+    if args.profile_only:
+        return
     ms_p, st_p, act_p, host_tp = results[cfg_p.name]
     ms_d, st_d, act_d, _ = results[cfg_d.name]
     gu_ms = st_p["gate_up"]

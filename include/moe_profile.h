@@ -2,14 +2,15 @@
  * moe_profile.h -- instrumented variant of moe_forward for benchmarks.
  *
  * Computes exactly what moe_forward (include/moe.h) computes, with the same arguments and rules, and in
- * addition records six caller-created HIP events (hipEvent_t, created with timing enabled) on `stream`
- * at the stage boundaries of the routed path:
- *   events[0] before the router          events[3] after the routed gate/up (SwiGLU) grouped GEMM
- *   events[1] after the router           events[4] after the routed down grouped GEMM
- *   events[2] after the permutation      events[5] after the combine (the end of the layer)
+ * addition records seven caller-created HIP events (hipEvent_t, created with timing enabled) on `stream`
+ * at the stage boundaries:
+ *   events[0] start of the layer              events[4] after the routed gate/up (SwiGLU) grouped GEMM
+ *   events[1] after the router                events[5] after the routed down grouped GEMM
+ *   events[2] after the permutation           events[6] after the combine (the end of the layer)
+ *   events[3] after the shared expert (when it runs on `stream`)
  * hipEventElapsedTime between consecutive events gives each stage's device time. The events stay owned
- * by the caller. With stream_shared non-null the shared expert runs concurrently on that stream and is
- * not bracketed by these events (its time overlaps the routed stages).
+ * by the caller. With stream_shared non-null the shared expert runs on that stream, forked after the
+ * permutation: events[2] to events[3] is then empty and its time overlaps the routed GEMMs.
  * Pages: as moe_forward (open-model-atlas GLM-5 "MoE transformer block", "All 43 steps").
  */
 #ifndef SIGMOID_ROUTED_MIXTURE_MOE_PROFILE_H

@@ -135,10 +135,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     hipStream_t s1 = static_cast<hipStream_t>(stream_shared);
     const bool two_streams = Is > 0 && s1 != nullptr && s1 != s0;
     DeviceEvents* ev = nullptr;
-    if (two_streams) {
-        MOE_TRY(device_events(&ev));
-        MOE_TRY(order_after(s1, s0, ev->fork));
-    }
+    if (two_streams) MOE_TRY(device_events(&ev));
 
     const moe::GemmPath path = pick_path(T, E, k);
     const bool wide = path == moe::GemmPath::Wide;
@@ -149,7 +146,18 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
         return from_hip(hipEventRecord(static_cast<hipEvent_t>(events[i]), s0), "hipEventRecord (profile)");
     };
     MOE_TRY(mark(0));
-    // shared expert first on its own stream, so it overlaps routing and the routed experts
+    const int S = moe::router_splits(T, H);
+    MOE_HIP(moe::launch_router(x, w_router, bias, T, H, E, k, scale, ids, gates, nullptr,
+                               static_cast<float*>(at(L.partial)), S, s0),
+            "router");
+    MOE_TRY(mark(1));
+    MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
+                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, s0),
+            "permute");
+    MOE_TRY(mark(2));
+    // The shared expert needs no routing: with a second stream it forks here, after the router and the
+    // permutation (so it cannot delay them), and overlaps the routed experts.
+    if (two_streams) MOE_TRY(order_after(s1, s0, ev->fork));
     if (Is > 0) {
         hipStream_t ss = two_streams ? s1 : s0;
         moe::GemmArgs g1{};
@@ -171,17 +179,8 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
         g2.K = Is;
         MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, g2, dense_tiles, ss), "shared down GEMM");
     }
-
-    MOE_TRY(mark(1));
-    const int S = moe::router_splits(T, H);
-    MOE_HIP(moe::launch_router(x, w_router, bias, T, H, E, k, scale, ids, gates, nullptr,
-                               static_cast<float*>(at(L.partial)), S, s0),
-            "router");
-    MOE_TRY(mark(2));
-    MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, s0),
-            "permute");
     MOE_TRY(mark(3));
+
     const int64_t grid_tiles = moe::max_tiles(T, E, k, BM);
     moe::GemmArgs r1{};
     r1.act = x;

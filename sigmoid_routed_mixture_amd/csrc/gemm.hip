@@ -10,9 +10,9 @@
 // four accumulator elements are four consecutive output features of one token row: 8-byte bf16 stores.
 //
 // Two kernels:
-//  * wide   : 128 tokens x 128 weight rows per workgroup, K in steps of 64 staged through LDS (double
-//             buffered, 16-byte chunks XOR-swizzled by row so MFMA fragment reads are conflict-free);
-//             4 waves in a 2 x 2 grid, each 64 weight rows x 64 tokens (16 MFMA tiles).
+//  * wide   : 128 tokens x 256 weight rows per 8-wave workgroup. Each wave streams its own 32 weight
+//             rows from HBM into MFMA registers; the token tile goes through double-buffered LDS. It
+//             also computes the router logits (dense, K split across workgroups).
 //  * skinny : 16 tokens per tile for experts with few rows (decode). No LDS: each wave streams its own
 //             weight rows straight from HBM with 32-byte loads per lane, several 64-wide K chunks in
 //             flight, so the kernel runs at the weight-streaming bound.
@@ -63,116 +63,140 @@ __device__ __forceinline__ const uint16_t* act_row(const GemmArgs& a, const Tile
 // ------------------------------------------------------------------------------------------------
 // wide kernel
 
-constexpr int kWBM = kWideBM;   // tokens per tile
-constexpr int kWBN = 128;       // weight rows per tile
+constexpr int kWBM = kWideBM;        // tokens per tile: 8 MFMA column blocks of 16
+constexpr int kWaves = 8;            // waves per workgroup (two per SIMD)
+constexpr int kWaveRows = 32;        // weight rows per wave: 2 MFMA row blocks of 16
+constexpr int kWBN = kWaves * kWaveRows;  // weight rows per workgroup
+constexpr int kWThreads = 64 * kWaves;
 static_assert(kWBM == 128, "wide tiling assumes 128 tokens");
 
-// LDS tile: [128 rows][64 k] bf16; chunk c (8 bf16) of row r lives at chunk c ^ (r & 7).
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// LDS token tile: [128 rows][64 k] bf16 (128 B per row); 16-byte chunk c of row r lives at chunk
+// c ^ (r & 7) ^ ((r >> 3) & 1). An MFMA fragment read is 16 lanes on rows r..r+15 (r a multiple of 16) at
+// one chunk: the permutation gives every 8 consecutive rows distinct chunks, and even rows (and odd
+// rows) distinct chunks, so the 16 lanes cover all 64 four-byte banks and each 8-lane half all 32 of a
+// 128-byte line: no bank conflicts whether the LDS serves 8 or 16 lanes of a b128 read per cycle.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+    return row * kBK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
+}
 
-template <GemmKind KIND, bool DENSE>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a, int ntn) {
-    const int64_t bid = blockIdx.x;
-    const int ntile = (int)(bid % ntn);
-    TileInfo ti;
-    if (!tile_info<DENSE, kWBM>(a, bid / ntn, ti)) return;
-
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kWBN * kBK];
-
+// One 128-token x 256-weight-row tile. Each of the 8 waves streams its own 32 weight rows from HBM
+// straight into MFMA A-operand registers (a weight row is used by one wave only, so it never touches
+// LDS); the 128 token rows, shared by all waves, are staged through double-buffered LDS. Per 64-wide K
+// step a lane loads 32 contiguous bytes of each of its 2 weight rows (k-group g = lane / 16 covers
+// k 16 g .. 16 g + 15); MFMA h in {0, 1} takes the h-th 8 of them and token chunk 2 g + h from LDS.
+// With 8 waves the register budget allows two waves per SIMD, so one wave's memory waits are covered by
+// the other's MFMAs.
+// Pipeline: step s computes on weights W(s) (register set s % 3) and tokens X(s) (LDS buffer s % 2). It
+// first issues the token loads of X(s + 2) (register set s % 2, free since X(s) went to LDS) and the
+// weight loads of W(s + 2); at its end it stores X(s + 1) (loaded during step s - 1) into LDS buffer
+// (s + 1) % 2, whose last reader was step s - 1, and a barrier publishes it. Loads past the end re-read
+// the last chunk (in bounds, unused); the scheduling barrier keeps each step's loads ahead of its MFMAs.
+// Only NB of the 8 token blocks (the ones holding valid rows, rounded to 1, 2, 4 or 8) are computed.
+template <GemmKind KIND, bool DENSE, int NB>
+__device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti, int split, int col0,
+                                          const uint16_t* const (&wsrc)[2], const uint16_t* const (&xsrc)[2],
+                                          int kbeg, int kend, uint16_t* xs0, uint16_t* xs1) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
     const int rl = lane & 15, kg = lane >> 4;
-    const int K = a.K, N = a.N;
-
-    // global -> LDS assignment: chunk c of rows r_i = (tid >> 3) + 32 i
     const int lc = tid & 7;
-    const uint16_t* wsrc[4];
-    const uint16_t* xsrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        if (KIND == GemmKind::GateUp) {
-            const int slab = r >> 6, q = r & 63;
-            const int n = ntile * 64 + slab * 32 + (q & 31);
-            const uint16_t* base = q < 32 ? a.w_a : a.w_b;
-            wsrc[i] = base + ((size_t)ti.g * N + n) * K + lc * 8;
-        } else {
-            int n = ntile * kWBN + r;
-            n = n < N ? n : N - 1;
-            wsrc[i] = a.w_a + ((size_t)ti.g * N + n) * K + lc * 8;
-        }
-        xsrc[i] = act_row<KIND, DENSE>(a, ti, r) + lc * 8;
-    }
+    const int N = a.N;
 
-    f32x4 acc[4][4];
+    f32x4 acc[2][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Pack16 wv[4], xv[4];
-    auto gload = [&](int kk) {
+    typedef Pack16 WSet[2][2];
+    typedef Pack16 XSet[2];
+    WSet w0, w1, w2;
+    XSet x0, x1;
+    auto wload = [&](WSet& w, int kk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wv[i] = load16(wsrc[i] + kk);
-            xv[i] = load16(xsrc[i] + kk);
+        for (int i = 0; i < 2; ++i) {
+            w[i][0] = load16(wsrc[i] + kk);
+            w[i][1] = load16(wsrc[i] + kk + 8);
         }
     };
-    auto lstore = [&](int buf) {
+    auto xload = [&](XSet& x, int kk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            store16(&lds[buf][0][lds_off(r, lc)], wv[i]);
-            store16(&lds[buf][1][lds_off(r, lc)], xv[i]);
+        for (int i = 0; i < 2; ++i) x[i] = load16(xsrc[i] + kk);
+    };
+    auto xstore = [&](const XSet& x, uint16_t* buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) store16(&buf[lds_off((tid >> 3) + 64 * i, lc)], x[i]);
+    };
+    // Token fragments: all of the first half are read up front; each second-half fragment is read into
+    // the register its first-half twin frees, right after that twin's MFMAs issue.
+    auto compute = [&](const WSet& w, const uint16_t* xb) {
+        Pack16 bfr[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bfr[j] = load16(&xb[lds_off(j * 16 + rl, 2 * kg)]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(w[i][0], bfr[j], acc[i][j]);
+            bfr[j] = load16(&xb[lds_off(j * 16 + rl, 2 * kg + 1)]);
         }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(w[i][1], bfr[j], acc[i][j]);
     };
 
-    const int nk = K / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int chunk = ks * 4 + kg;
-            Pack16 af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = load16(&lds[cur][0][lds_off(wn * 64 + i * 16 + rl, chunk)]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = load16(&lds[cur][1][lds_off(wm * 64 + j * 16 + rl, chunk)]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) lstore(cur ^ 1);
+    const int nk = (kend - kbeg) / kBK;
+    const int klast = kend - kBK;
+    auto kat = [&](int st) { const int k = kbeg + st * kBK; return k < klast ? k : klast; };
+    auto step = [&](const WSet& wcur, WSet& wfut, XSet& xfut, const XSet& xnext, const uint16_t* bcur,
+                    uint16_t* bnext, int st) {
+        xload(xfut, kat(st + 2));
+        wload(wfut, kat(st + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wcur, bcur);
+        xstore(xnext, bnext);
         __syncthreads();
+    };
+    xload(x0, kat(0));
+    wload(w0, kat(0));
+    xload(x1, kat(1));
+    wload(w1, kat(1));
+    xstore(x0, xs0);
+    __syncthreads();
+    // six steps per iteration: the token registers cycle with period 2, the weights with period 3
+    int s = 0;
+    for (; s + 6 <= nk; s += 6) {
+        step(w0, w2, x0, x1, xs0, xs1, s);
+        step(w1, w0, x1, x0, xs1, xs0, s + 1);
+        step(w2, w1, x0, x1, xs0, xs1, s + 2);
+        step(w0, w2, x1, x0, xs1, xs0, s + 3);
+        step(w1, w0, x0, x1, xs0, xs1, s + 4);
+        step(w2, w1, x1, x0, xs1, xs0, s + 5);
     }
+    if (s < nk) step(w0, w2, x0, x1, xs0, xs1, s);
+    if (s + 1 < nk) step(w1, w0, x1, x0, xs1, xs0, s + 1);
+    if (s + 2 < nk) step(w2, w1, x0, x1, xs0, xs1, s + 2);
+    if (s + 3 < nk) step(w0, w2, x1, x0, xs1, xs0, s + 3);
+    if (s + 4 < nk) step(w1, w0, x0, x1, xs0, xs1, s + 4);
+    if (col0 >= N) return; // a wave past the last output column computed on clamped rows: nothing to store
 
     // epilogue: lane holds features 4 kg + r of weight block i and token rl of token block j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int m = wm * 64 + j * 16 + rl;
+    for (int j = 0; j < NB; ++j) {
+        const int m = j * 16 + rl;
         if (m >= ti.rows) continue;
         const size_t row = (size_t)ti.off + ti.m0 + m;
         if (KIND == GemmKind::GateUp) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int col = ntile * 64 + wn * 32 + i * 16 + 4 * kg;
-                const f32x4 g = acc[i][j], u = acc[i + 2][j];
-                uint2 v;
-                v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
-                v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
-            }
+            const int col = col0 + 4 * kg;
+            const f32x4 g = acc[0][j], u = acc[1][j];
+            uint2 v;
+            v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+            v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = ntile * kWBN + wn * 64 + i * 16 + 4 * kg;
+            for (int i = 0; i < 2; ++i) {
+                const int col = col0 + i * 16 + 4 * kg;
                 if (col >= N) continue;
                 const f32x4 y = acc[i][j];
                 if (KIND == GemmKind::Down) {
@@ -181,12 +205,81 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a, int ntn) {
                     v.y = pack_bf16x2(y[2], y[3]);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
                 } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * N + col) =
-                        make_float4(y[0], y[1], y[2], y[3]);
+                    float* o = static_cast<float*>(a.out) + (size_t)split * a.dense_rows * N + row * N + col;
+                    if (col + 3 < N) {
+                        *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (col + r < N) o[r] = y[r];
+                    }
                 }
             }
         }
     }
+}
+
+template <GemmKind KIND, bool DENSE>
+__global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int ntn, int64_t tiles_per_split) {
+    int64_t bid = blockIdx.x;
+    int split = 0;
+    if (KIND == GemmKind::Logits) {
+        split = (int)(bid / (tiles_per_split * ntn));
+        bid -= (int64_t)split * tiles_per_split * ntn;
+    }
+    const int ntile = (int)(bid % ntn);
+    TileInfo ti;
+    if (!tile_info<DENSE, kWBM>(a, bid / ntn, ti)) return;
+
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[kWBM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[kWBM * kBK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int rl = lane & 15, kg = lane >> 4;
+    const int K = a.K, N = a.N;
+
+    int kbeg = 0, kend = K;
+    if (KIND == GemmKind::Logits) {
+        const int C = K / kBK;
+        kbeg = (int)((int64_t)split * C / a.ksplit) * kBK;
+        kend = (int)((int64_t)(split + 1) * C / a.ksplit) * kBK;
+    }
+
+    // this wave's two weight row blocks, clamped to the last row (a wave past N computes on them and
+    // stores nothing). Gate/up: W1 and W3 rows of the same 16 output columns.
+    int col0;
+    const uint16_t* wsrc[2];
+    if (KIND == GemmKind::GateUp) {
+        col0 = ntile * (kWBN / 2) + wave * 16;
+        int n = col0 + rl;
+        n = n < N ? n : N - 1;
+        wsrc[0] = a.w_a + ((size_t)ti.g * N + n) * K + kg * 16;
+        wsrc[1] = a.w_b + ((size_t)ti.g * N + n) * K + kg * 16;
+    } else {
+        col0 = ntile * kWBN + wave * kWaveRows;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int n = col0 + i * 16 + rl;
+            n = n < N ? n : N - 1;
+            wsrc[i] = a.w_a + ((size_t)ti.g * N + n) * K + kg * 16;
+        }
+    }
+    const int lc = tid & 7;
+    const uint16_t* xsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xsrc[i] = act_row<KIND, DENSE>(a, ti, (tid >> 3) + 64 * i) + lc * 8;
+
+    const int nbj = (ti.rows + 15) >> 4;
+    if (nbj > 4)
+        wide_tile<KIND, DENSE, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    else if (nbj > 2)
+        wide_tile<KIND, DENSE, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    else if (nbj > 1)
+        wide_tile<KIND, DENSE, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    else
+        wide_tile<KIND, DENSE, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -288,14 +381,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
 
 template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
-    const int ntn = KIND == GemmKind::GateUp ? a.N / 64 : (a.N + 127) / 128;
-    const int64_t blocks = grid_tiles * ntn;
+    int ntn;
+    if (wide)
+        ntn = KIND == GemmKind::GateUp ? (a.N + kWBN / 2 - 1) / (kWBN / 2) : (a.N + kWBN - 1) / kWBN;
+    else
+        ntn = KIND == GemmKind::GateUp ? a.N / 64 : (a.N + 127) / 128;
+    const int splits = KIND == GemmKind::Logits ? a.ksplit : 1;
+    const int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     if (wide)
-        gemm_wide_kernel<KIND, DENSE><<<dim3((unsigned)blocks), 256, 0, stream>>>(a, ntn);
-    else
+        gemm_wide_kernel<KIND, DENSE><<<dim3((unsigned)blocks), kWThreads, 0, stream>>>(a, ntn, grid_tiles);
+    else if (KIND != GemmKind::Logits)
         gemm_skinny_kernel<KIND, DENSE><<<dim3((unsigned)blocks), 256, 0, stream>>>(a, ntn);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -313,6 +413,8 @@ hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid
     case GemmKind::DownF32:
         return dense ? launch_one<GemmKind::DownF32, true>(wide, a, grid_tiles, stream)
                      : launch_one<GemmKind::DownF32, false>(wide, a, grid_tiles, stream);
+    case GemmKind::Logits:
+        return dense ? launch_one<GemmKind::Logits, true>(true, a, grid_tiles, stream) : hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }

@@ -6,8 +6,9 @@
 
 namespace moe {
 
-// Router: logits, sigmoid, biased top-k, gates. S > 1 with `partial` [S, T, E] fp32 splits the logit
-// GEMM over K (for few tokens); otherwise one fused kernel does everything.
+// Router: logits, sigmoid, biased top-k, gates. With `partial` ([S, T, E] fp32 scratch) the logits run
+// as a K-split dense GEMM on the grouped-GEMM kernel and a top-k kernel sums the S partials in order;
+// without it one fused kernel (32 tokens per workgroup) does everything.
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
                          float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
                          hipStream_t stream);
@@ -34,11 +35,12 @@ struct GemmArgs {
     const int32_t* offsets;    // first row of each group
     const int2* tiles;         // {group, first row in group} per tile
     const int32_t* ntiles;     // number of valid tiles
-    int dense_rows;            // rows of the dense group
+    int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped
     int N, K;                  // output width (gate/up: I, h columns), reduction length
+    int ksplit;                // logits only: K ranges, each writing its own [dense_rows, N] fp32 partial
 };
-enum class GemmKind { GateUp, Down, DownF32 };
+enum class GemmKind { GateUp, Down, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]), fp32, slot order.

@@ -34,10 +34,11 @@ Check check_aligned(const void* p, const char* name, size_t align) {
 }
 
 int router_splits(int T, int H) {
-    const int64_t tblocks = (T + kRouterBT - 1) / kRouterBT;
-    const int chunks = H / 64;
-    int64_t s = (512 + tblocks - 1) / std::max<int64_t>(tblocks, 1); // aim at >= 512 workgroups
-    s = std::max<int64_t>(1, std::min<int64_t>(s, chunks));
+    // enough K ranges that the logits GEMM has >= 256 workgroups of 128 tokens, at most 32 and at most one
+    // per 64-wide K chunk
+    const int64_t tiles = ((int64_t)T + kWideBM - 1) / kWideBM;
+    int64_t s = (256 + tiles - 1) / std::max<int64_t>(tiles, 1);
+    s = std::max<int64_t>(1, std::min<int64_t>(s, std::min(32, H / 64)));
     return (int)s;
 }
 

@@ -182,33 +182,6 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const uint16_t* __res
     }
 }
 
-// K-split logits for small T: split s of S covers 64-wide chunks [s C / S, (s + 1) C / S).
-__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ wr, int T, int H, int E,
-                                                             int S, float* __restrict__ partial) {
-    const int t0 = blockIdx.x * kBT;
-    const int s = blockIdx.y;
-    const int C = H / 64;
-    const int c0 = (int)((int64_t)s * C / S), c1 = (int)((int64_t)(s + 1) * C / S);
-    f32x4 acc[4][2];
-    router_accumulate(x, wr, T, H, E, t0, c0, c1, acc);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    float* dst = partial + (size_t)s * T * E;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + j * 16 + (lane & 15);
-            if (t >= T) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = wave * 64 + b * 16 + 4 * (lane >> 4) + r;
-                if (e < E) dst[(size_t)t * E + e] = acc[b][j][r];
-            }
-        }
-}
-
 // Sums the S partial logits of each token in split order, then routes it (one wave per token).
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int S,
                                                           const float* __restrict__ bias, int T, int E, int k,
@@ -218,12 +191,24 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     float z4[4];
+    const size_t stride = (size_t)T * E;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
         float z = 0.f;
-        if (e < E)
-            for (int s = 0; s < S; ++s) z += partial[((size_t)s * T + t) * E + e];
+        if (e < E) {
+            const float* p = partial + (size_t)t * E + e;
+            int s = 0;
+            for (; s + 4 <= S; s += 4) { // four independent loads in flight, added in split order
+                const float p0 = p[(size_t)s * stride], p1 = p[(size_t)(s + 1) * stride];
+                const float p2 = p[(size_t)(s + 2) * stride], p3 = p[(size_t)(s + 3) * stride];
+                z += p0;
+                z += p1;
+                z += p2;
+                z += p3;
+            }
+            for (; s < S; ++s) z += p[(size_t)s * stride];
+        }
         z4[q] = z;
     }
     topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
@@ -234,15 +219,24 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
                          float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
                          hipStream_t stream) {
-    const int tblocks = (T + kBT - 1) / kBT;
-    if (S <= 1 || partial == nullptr) {
+    if (partial == nullptr) {
+        const int tblocks = (T + kBT - 1) / kBT;
         router_fused_kernel<<<tblocks, 256, 0, stream>>>(x, wr, bias, T, H, E, k, scale, ids, gates, logits);
         return hipGetLastError();
     }
-    router_partial_kernel<<<dim3(tblocks, S), 256, 0, stream>>>(x, wr, T, H, E, S, partial);
-    hipError_t e = hipGetLastError();
+    // logits as a dense GEMM (W_r rows x token tiles), K split S ways into fp32 partials, then the top-k
+    GemmArgs g{};
+    g.act = x;
+    g.w_a = wr;
+    g.out = partial;
+    g.dense_rows = T;
+    g.N = E;
+    g.K = H;
+    g.ksplit = S < 1 ? 1 : S;
+    hipError_t e = launch_gemm(GemmKind::Logits, true, g, ((int64_t)T + kWideBM - 1) / kWideBM, stream);
     if (e != hipSuccess) return e;
-    router_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(partial, S, bias, T, E, k, scale, ids, gates, logits);
+    router_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(partial, g.ksplit, bias, T, E, k, scale, ids, gates,
+                                                         logits);
     return hipGetLastError();
 }
 
