@@ -50,6 +50,23 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
     return ti.rows > 0;
 }
 
+// Workgroup -> (token tile, output-column tile) of the grouped wide GEMM. The live blocks go in
+// expert-major order and each XCD takes one contiguous eighth of it: the token tiles that share a slice
+// of an expert's weights run side by side on one XCD, and so do the column tiles that share a token
+// tile, so both come from HBM about once instead of once per XCD.
+template <int BM>
+__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
+                                              int& ntile) {
+    const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
+    if (L < 0) return false;
+    const int2 entry = a.tiles[L / ntn];
+    if (entry.x < 0 || entry.x >= a.groups || entry.y < 0) return false;
+    const int m = (a.counts[entry.x] + BM - 1) / BM;
+    if (m <= 0) return false;
+    mtile = expert_major_tile(L, ntn, entry.y / BM, m, ntile);
+    return true;
+}
+
 // Activation row for tile row m (clamped to the tile's last valid row: padded columns of the MFMA tile
 // read a real row and are never stored).
 template <GemmKind KIND, bool DENSE>
@@ -227,9 +244,16 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
         split = (int)(bid / (tiles_per_split * ntn));
         bid -= (int64_t)split * tiles_per_split * ntn;
     }
-    const int ntile = (int)(bid % ntn);
+    int ntile;
+    int64_t mtile;
+    if (DENSE) {
+        ntile = (int)(bid % ntn);
+        mtile = bid / ntn;
+    } else if (!grouped_block<kWBM>(a, ntn, bid, mtile, ntile)) {
+        return;
+    }
     TileInfo ti;
-    if (!tile_info<DENSE, kWBM>(a, bid / ntn, ti)) return;
+    if (!tile_info<DENSE, kWBM>(a, mtile, ti)) return;
 
     __shared__ __attribute__((aligned(16))) uint16_t xs0[kWBM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t xs1[kWBM * kBK];
@@ -387,8 +411,9 @@ hipError_t launch_one(bool wide, const GemmArgs& a, int64_t grid_tiles, hipStrea
     else
         ntn = KIND == GemmKind::GateUp ? a.N / 64 : (a.N + 127) / 128;
     const int splits = KIND == GemmKind::Logits ? a.ksplit : 1;
-    const int64_t blocks = grid_tiles * ntn * splits;
+    int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
+    if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     if (wide)
         gemm_wide_kernel<KIND, DENSE><<<dim3((unsigned)blocks), kWThreads, 0, stream>>>(a, ntn, grid_tiles);

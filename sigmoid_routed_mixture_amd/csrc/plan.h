@@ -37,6 +37,27 @@ GemmPath gemm_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);
 
+// Workgroup order of the LDS-tiled grouped GEMM (pure arithmetic, also used by the kernel).
+// The hardware hands workgroup b to XCD b % kXcds and each XCD has its own L2, so the `live` blocks are
+// put in one order and XCD x takes the x-th contiguous chunk of it. Returns the block's position L in
+// that order, or -1 when workgroup `bid` has no block (the grid is padded to a multiple of kXcds).
+constexpr int kXcds = 8;
+constexpr int64_t xcd_block_order(int64_t bid, int64_t live) {
+    const int64_t chunk = (live + kXcds - 1) / kXcds;
+    const int64_t local = bid / kXcds;
+    const int64_t L = (bid % kXcds) * chunk + local;
+    return (local < chunk && L < live) ? L : -1;
+}
+// Expert-major order: position L lies in the range of an expert whose tiles are [first, first + m) of
+// the tile list (L / ntn is tile i of the expert); inside the range, output-column tile 0 of every token
+// tile comes first, then column tile 1, and so on. Returns the tile-list index, sets the column tile.
+constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile) {
+    const int64_t first = L / ntn - i;
+    const int64_t r = L - first * ntn;
+    ntile = (int)(r / m);
+    return first + r % m;
+}
+
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
     size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,

@@ -2,6 +2,8 @@
 // write into it (either grouped-GEMM kernel, any router split), and regions do not overlap.
 // Built and run by tests/test_plan.py with g++ against the library's planner source.
 #include <cstdio>
+#include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 #include <vector>
 
@@ -61,6 +63,57 @@ int main() {
                             CHECK(S >= 1 && S <= H / 64, "splits %d for H=%d", S, H);
                         }
                 }
+    // Workgroup order of the LDS-tiled grouped GEMM: with the grid padded to a multiple of kXcds, every
+    // (tile, column tile) pair of the live tile list is taken by exactly one workgroup, each XCD's
+    // workgroups cover a contiguous range of the order, and an expert's pairs are contiguous in it.
+    uint64_t rng = 0x9E3779B97F4A7C15ull;
+    auto next = [&]() {
+        rng ^= rng << 13;
+        rng ^= rng >> 7;
+        rng ^= rng << 17;
+        return rng;
+    };
+    int orders = 0;
+    for (int trial = 0; trial < 300; ++trial) {
+        const int E = 1 + (int)(next() % 64);
+        const int k = 1 + (int)(next() % std::min(E, 8));
+        const int T = (int)(next() % 2000);
+        const int ntn = 1 + (int)(next() % 40);
+        const int BM = moe::kWideBM;
+        std::vector<int> counts(E, 0);
+        const bool skew = trial % 3 == 0;
+        for (int t = 0; t < T * k; ++t) counts[skew ? (int)(next() % 4) % E : (int)(next() % E)]++;
+        std::vector<std::pair<int, int>> tiles; // {expert, first row}
+        for (int e = 0; e < E; ++e)
+            for (int r = 0; r < counts[e]; r += BM) tiles.push_back({e, r});
+        const int64_t live = (int64_t)tiles.size() * ntn;
+        int64_t grid = moe::max_tiles(T, E, k, BM) * ntn;
+        CHECK(grid >= live, "grid %lld < live %lld", (long long)grid, (long long)live);
+        grid = (grid + moe::kXcds - 1) / moe::kXcds * moe::kXcds;
+        std::vector<int> seen(live, 0);
+        std::vector<int64_t> lo(moe::kXcds, INT64_MAX), hi(moe::kXcds, -1), cnt(moe::kXcds, 0);
+        for (int64_t b = 0; b < grid; ++b) {
+            const int64_t L = moe::xcd_block_order(b, live);
+            if (L < 0) continue;
+            const int x = (int)(b % moe::kXcds);
+            lo[x] = std::min(lo[x], L);
+            hi[x] = std::max(hi[x], L);
+            ++cnt[x];
+            const auto entry = tiles[L / ntn];
+            const int m = (counts[entry.first] + BM - 1) / BM;
+            int nt = -1;
+            const int64_t mt = moe::expert_major_tile(L, ntn, entry.second / BM, m, nt);
+            CHECK(mt >= 0 && mt < (int64_t)tiles.size() && tiles[mt].first == entry.first,
+                  "block %lld: tile %lld outside expert %d", (long long)b, (long long)mt, entry.first);
+            CHECK(nt >= 0 && nt < ntn, "block %lld: column tile %d of %d", (long long)b, nt, ntn);
+            if (mt >= 0 && mt < (int64_t)tiles.size() && nt >= 0 && nt < ntn) seen[mt * ntn + nt]++;
+        }
+        for (int64_t i = 0; i < live; ++i) CHECK(seen[i] == 1, "pair %lld taken %d times", (long long)i, seen[i]);
+        for (int x = 0; x < moe::kXcds; ++x)
+            CHECK(cnt[x] == 0 || hi[x] - lo[x] + 1 == cnt[x], "XCD %d range not contiguous", x);
+        ++orders;
+    }
+    std::printf("%d block orders checked\n", orders);
     std::printf("%d layouts checked, %d failures\n", n, fails);
     return fails ? 1 : 0;
 }
