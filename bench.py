@@ -91,6 +91,45 @@ class Runner:
         return ms, stages
 
 
+# Sources that fix the routed gate/up kernel's memory traffic at a given workload: the kernel, its tile list
+# and block order, and the seeded workload generator. Counter figures stored under profiles/ carry this
+# digest; bench.py reports them as `traffic` only while it still matches the tree.
+TRAFFIC_SOURCES = ("sigmoid_routed_mixture_amd/csrc/gemm.hip", "sigmoid_routed_mixture_amd/csrc/common.h",
+                   "sigmoid_routed_mixture_amd/csrc/kernels.h", "sigmoid_routed_mixture_amd/csrc/plan.h",
+                   "sigmoid_routed_mixture_amd/csrc/permute.hip", "workloads/gen.c")
+TRAFFIC_PROFILE = "profiles/gate_up_glm5_prefill_traffic.txt"
+
+
+def kernel_sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per routed gate/up launch from the stored counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by the plain-copy calibration), or None when the summary is missing or the kernel changed since."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def gate_up_flops(cfg):
     return 4 * cfg.T * cfg.k * cfg.H * cfg.I
 
@@ -136,6 +175,9 @@ def main():
     ap.add_argument("--single-stream", action="store_true", help="run the shared expert on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibration", type=float, default=None, metavar="GIB",
+                    help="time a plain device-to-device copy of this many GiB (HBM ceiling, and the known-size "
+                         "reference for profiler byte counters) and exit")
     ap.add_argument("--profile-only", choices=["prefill", "decode"], default=None,
                     help="run only this workload's timed steps and print its timings (for profiler runs)")
     args = ap.parse_args()
@@ -145,6 +187,25 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = int(args.copy_calibration * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        s0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        print(json.dumps({"copy_bytes_each_way": n, "ms": ms, "read_plus_write_GBs": 2 * n / ms / 1e6}), flush=True)
+        return
 
     import sigmoid_routed_mixture_amd as m
     import workloads as wl
@@ -201,7 +262,8 @@ def main():
                    "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none"},
         "roofline": {"bound": "mfma", "kernel": "routed gate/up SwiGLU grouped GEMM", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "launch_ms": gu_ms},
+                     "traffic": measured_traffic(), "launch_ms": gu_ms,
+                     "algorithmic_bytes": gate_up_bytes(cfg_p, act_p)},
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_BF16_TFLOPS,
                   "gbs": layer_bytes(cfg_p, act_p) / (ms_p * 1e-3) / 1e9, "active_experts": act_p,
                   "stages_ms": st_p},
