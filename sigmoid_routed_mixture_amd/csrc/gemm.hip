@@ -14,8 +14,8 @@
 //             rows from HBM into MFMA registers; the token tile goes through double-buffered LDS. It
 //             also computes the router logits (dense, K split across workgroups).
 //  * skinny : 16 tokens per tile for experts with few rows (decode). No LDS: each wave streams its own
-//             weight rows straight from HBM with 32-byte loads per lane, several 64-wide K chunks in
-//             flight, so the kernel runs at the weight-streaming bound.
+//             weight rows straight from HBM with 32-byte loads per lane, two 64-wide K chunks in flight
+//             ahead of its MFMAs, so the kernel runs at the weight-streaming bound.
 // Both take their (expert, first row) tiles from the device-side list the permutation builds; the grid is
 // an upper bound and workgroups past the list's length exit at once.
 #include "common.h"
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
 
 constexpr int kSBM = kSkinnyBM; // tokens per tile
 static_assert(kSBM == 16, "skinny tiling assumes one 16-token MFMA column block");
-constexpr int kUnroll = 4;      // 64-wide K chunks in flight per lane
+constexpr int kSU = 1;          // 64-wide K chunks per pipeline stage (K is a multiple of 64)
 
 template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
@@ -325,8 +325,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
     const int rl = lane & 15, kg = lane >> 4;
     const int K = a.K, N = a.N;
 
-    // two 16-row weight blocks per wave: gate/up -> W1 and W3 rows of the same 16 h columns;
-    // down -> 32 consecutive W2 rows
     const uint16_t* wsrc[2];
     int col0;
     if (KIND == GemmKind::GateUp) {
@@ -345,36 +343,48 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
     }
     const uint16_t* xsrc = act_row<KIND, DENSE>(a, ti, rl) + kg * 16;
 
+    // Two register stages: the loads of K chunk st + 2 are issued right after chunk st's MFMAs, so every
+    // wave keeps two chunks of weights in flight while it computes (loads past the end re-read the last
+    // chunk: in bounds, unused).
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const int kfull = K / (64 * kUnroll) * (64 * kUnroll);
-    for (int kk = 0; kk < kfull; kk += 64 * kUnroll) {
-        Pack16 w[kUnroll][2][2], xr[kUnroll][2];
+    struct Stage {
+        Pack16 w[kSU][2][2], x[kSU][2];
+    };
+    const int nst = K / (64 * kSU);
+    auto load = [&](Stage& s, int st) {
+        st = st < nst ? st : nst - 1;
+        const int kk = st * 64 * kSU;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                w[u][b][0] = load16(wsrc[b] + kk + u * 64);
-                w[u][b][1] = load16(wsrc[b] + kk + u * 64 + 8);
-            }
-            xr[u][0] = load16(xsrc + kk + u * 64);
-            xr[u][1] = load16(xsrc + kk + u * 64 + 8);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kSU; ++u) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                acc[b] = mfma16x16x32(w[u][b][0], xr[u][0], acc[b]);
-                acc[b] = mfma16x16x32(w[u][b][1], xr[u][1], acc[b]);
+                s.w[u][b][0] = load16(wsrc[b] + kk + u * 64);
+                s.w[u][b][1] = load16(wsrc[b] + kk + u * 64 + 8);
             }
-    }
-    for (int kk = kfull; kk < K; kk += 64) {
-        const Pack16 x0 = load16(xsrc + kk), x1 = load16(xsrc + kk + 8);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            acc[b] = mfma16x16x32(load16(wsrc[b] + kk), x0, acc[b]);
-            acc[b] = mfma16x16x32(load16(wsrc[b] + kk + 8), x1, acc[b]);
+            s.x[u][0] = load16(xsrc + kk + u * 64);
+            s.x[u][1] = load16(xsrc + kk + u * 64 + 8);
         }
+    };
+    auto compute = [&](const Stage& s) {
+#pragma unroll
+        for (int u = 0; u < kSU; ++u)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                acc[b] = mfma16x16x32(s.w[u][b][0], s.x[u][0], acc[b]);
+                acc[b] = mfma16x16x32(s.w[u][b][1], s.x[u][1], acc[b]);
+            }
+    };
+    Stage s0, s1;
+    load(s0, 0);
+    load(s1, 1);
+    int st = 0;
+    for (; st + 2 <= nst; st += 2) {
+        compute(s0);
+        load(s0, st + 2);
+        compute(s1);
+        load(s1, st + 3);
     }
+    if (st < nst) compute(s0);
 
     if (rl >= ti.rows) return;
     const size_t row = (size_t)ti.off + ti.m0 + rl;
