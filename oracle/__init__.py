@@ -55,6 +55,15 @@ def lib():
             L.oracle_permute.restype = i32
             L.oracle_param_count.argtypes = [ctypes.c_uint64] * 4
             L.oracle_param_count.restype = ctypes.c_uint64
+            dbl = ctypes.c_double
+            L.oracle_round_bf16.argtypes = [dbl]
+            L.oracle_round_bf16.restype = ctypes.c_uint16
+            L.oracle_rmsnorm.argtypes = [i32, dbl, p, p, p, i32, p]
+            L.oracle_rmsnorm.restype = i32
+            L.oracle_block_forward.argtypes = [i32, i32, i32, i32, i32, f32, dbl] + [p] * 11 + [i32] + [p] * 5
+            L.oracle_block_forward.restype = i32
+            L.oracle_dense_mlp.argtypes = [i32, i32, p, p, p, p, p, i32, p]
+            L.oracle_dense_mlp.restype = i32
             _lib = L
     return _lib
 
@@ -161,6 +170,64 @@ def forward_routed(inp, ids, gates, rows=None):
                                      _p(ws1), _p(ws3), _p(ws2), _p(rows), n, _p(out))
     if rc != 0:
         raise ValueError("oracle_forward_routed rejected its arguments")
+    return out
+
+
+def round_bf16(v: float) -> int:
+    """bf16 bits of the double v, rounded to nearest, ties to even, in one step."""
+    return lib().oracle_round_bf16(v)
+
+
+def rmsnorm(x, gamma, eps, rows=None):
+    """RMSNorm of the listed rows: bf16 bits [n, H] of (x * rstd) * gamma, rstd = 1 / sqrt(mean x^2 + eps)."""
+    x, gamma = _bf16(x), _bf16(gamma)
+    H = x.shape[1]
+    rows, n = _rows_arg(rows, x.shape[0])
+    out = np.empty((n, H), np.uint16)
+    if lib().oracle_rmsnorm(H, eps, _p(x), _p(gamma), _p(rows), n, _p(out)) != 0:
+        raise ValueError("oracle_rmsnorm rejected its arguments")
+    return out
+
+
+def _shared(inp):
+    ws1 = inp.get("ws1")
+    Is = 0 if ws1 is None or ws1.size == 0 else ws1.shape[0]
+    if not Is:
+        return 0, None, None, None
+    return Is, _bf16(ws1), _bf16(inp["ws3"]), _bf16(inp["ws2"])
+
+
+def block_forward(inp, gamma, eps, k, scale, rows=None):
+    """The mixture half of a block on the residual stream inp["x"]: out = x' + mixture(RMSNorm(x')).
+    Returns dict out, x_norm, ids, gates, gap for the listed tokens."""
+    x, wr = _bf16(inp["x"]), _bf16(inp["wr"])
+    gamma = _bf16(gamma)
+    b = np.ascontiguousarray(inp["b"], dtype=np.float32)
+    w1, w3, w2 = _bf16(inp["w1"]), _bf16(inp["w3"]), _bf16(inp["w2"])
+    H, E, I = x.shape[1], wr.shape[0], w1.shape[1]
+    Is, ws1, ws3, ws2 = _shared(inp)
+    rows, n = _rows_arg(rows, x.shape[0])
+    out = np.empty((n, H), np.float32)
+    xn = np.empty((n, H), np.uint16)
+    ids = np.empty((n, k), np.int32)
+    gates = np.empty((n, k), np.float32)
+    gap = np.empty(n, np.float64)
+    rc = lib().oracle_block_forward(H, E, k, I, Is, scale, eps, _p(x), _p(gamma), _p(wr), _p(b), _p(w1), _p(w3),
+                                    _p(w2), _p(ws1), _p(ws3), _p(ws2), _p(rows), n, _p(out), _p(xn), _p(ids),
+                                    _p(gates), _p(gap))
+    if rc != 0:
+        raise ValueError("oracle_block_forward rejected its arguments")
+    return {"out": out, "x_norm": xn, "ids": ids, "gates": gates, "gap": gap}
+
+
+def dense_mlp(x, w1, w3, w2, rows=None):
+    """Dense SwiGLU MLP of the listed rows: fp32 [n, H] of (silu(x W1) * (x W3)) W2, W1/W3 [Id, H], W2 [H, Id]."""
+    x, w1, w3, w2 = _bf16(x), _bf16(w1), _bf16(w3), _bf16(w2)
+    H, Id = x.shape[1], w1.shape[0]
+    rows, n = _rows_arg(rows, x.shape[0])
+    out = np.empty((n, H), np.float32)
+    if lib().oracle_dense_mlp(H, Id, _p(x), _p(w1), _p(w3), _p(w2), _p(rows), n, _p(out)) != 0:
+        raise ValueError("oracle_dense_mlp rejected its arguments")
     return out
 
 

@@ -17,6 +17,14 @@
  *   y_shared = (silu(x Ws1) * (x Ws3)) Ws2
  *   out = y_routed + y_shared
  *
+ * and the steps on either side of the mixture in a GLM-5 block, plus the dense MLP of the dense-first
+ * blocks (same pages: "All 43 steps" x_ffn = RMSNorm(x'_n) and x_{n+1} = x'_n + delta_ffn; the nnterp
+ * module trees' post_attention_layernorm with eps 1e-5 and the dense gate/up/down MLP):
+ *
+ *   x_ffn = RMSNorm(x') = gamma * x' / sqrt(mean(x'^2) + eps)   rounded once to bf16
+ *   x_next = x' + out(x_ffn)
+ *   y_dense = (silu(x W1) * (x W3)) W2
+ *
  * Weights are stored [out, in] like nn.Linear, so "x W1" is sum_h x[h] W1[n, h]. W1 is the gate (it gets
  * the sigmoid-weighted linear unit), W3 the up projection, W2 the down projection.
  *
@@ -25,12 +33,17 @@
  *  - z, s and c = s + b are fp32 values; z is the fp32 rounding of the exact (double) dot product;
  *  - b is fp32;
  *  - a zero gate denominator (never reached by these workloads) gives zero gates;
- *  - no intermediate of the expert MLPs is rounded; the output is fp32.
+ *  - no intermediate of the expert MLPs is rounded; the output is fp32;
+ *  - RMSNorm is the textbook definition (the pages name the module and its eps, not its formula), in
+ *    double with the product taken as (x * rstd) * gamma, and its output is rounded once to bf16, the
+ *    dtype the mixture takes.
  *
  * Parity status: every function here is pinned by a CPU test (brute-force top-k, crafted ties, the
  * sigmoid's closed forms, gate sums, the bias-only-moves-the-choice property, k = E dense mixture,
  * E = 1 dense SwiGLU MLP, linearity, token independence, the stable-sort permutation, the skewed
- * workload's closed forms and the pages' GLM-5 parameter count).
+ * workload's closed forms and the pages' GLM-5 parameter count; the bf16 rounding against fp32 rounding
+ * and crafted ties, RMSNorm's scale invariance and one-hot / constant rows, the block's residual wiring,
+ * and the dense MLP against numpy matrix products).
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,6 +60,46 @@ double oracle_bf16_to_double(uint16_t v) {
 
 /* s = sigma(z) = 1 / (1 + e^-z), evaluated in double and rounded once to fp32. */
 float oracle_sigmoid(float z) { return (float)(1.0 / (1.0 + exp(-(double)z))); }
+
+/* double -> bf16 storage, round to nearest, ties to even, straight from the double (no detour through
+ * fp32, which could round twice). |v| = m 2^e with m in [0.5, 1); a normal bf16 keeps 8 significant bits,
+ * so q = m 2^8 is split into its integer part (the kept bits) and the exact remainder. Below 2^-126 the
+ * quantum is the subnormal step 2^-133. */
+uint16_t oracle_round_bf16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7FC0u;
+    if (isinf(a)) return sign | 0x7F80u;
+    if (a == 0.0) return sign;
+    int e;
+    double m = frexp(a, &e); /* a = m 2^e */
+    int biased = e - 1 + 127;
+    double q = biased >= 1 ? ldexp(m, 8) : ldexp(a, 133);
+    double whole = floor(q);
+    double rem = q - whole;
+    uint32_t n = (uint32_t)whole;
+    if (rem > 0.5 || (rem == 0.5 && (n & 1u))) n++;
+    if (biased < 1) return sign | (uint16_t)n; /* n == 128 is the smallest normal, which the same bits encode */
+    if (n == 256u) {
+        n = 128u;
+        biased++;
+    }
+    if (biased >= 255) return sign | 0x7F80u;
+    return sign | (uint16_t)((uint32_t)biased << 7) | (uint16_t)(n - 128u);
+}
+
+/* RMSNorm of one row: rstd = 1 / sqrt(sum_h x[h]^2 / H + eps) in double (h ascending), then
+ * out[h] = bf16((x[h] * rstd) * gamma[h]). */
+static void rmsnorm_row(int H, double eps, const uint16_t* xrow, const uint16_t* gamma, uint16_t* out) {
+    double ss = 0.0;
+    for (int h = 0; h < H; ++h) {
+        double xv = oracle_bf16_to_double(xrow[h]);
+        ss += xv * xv;
+    }
+    double rstd = 1.0 / sqrt(ss / (double)H + eps);
+    for (int h = 0; h < H; ++h)
+        out[h] = oracle_round_bf16(oracle_bf16_to_double(xrow[h]) * rstd * oracle_bf16_to_double(gamma[h]));
+}
 
 /* One token's router logits: z[e] = fp32(sum_h x[h] W_r[e, h]), h ascending. */
 static void token_logits(int H, int E, const uint16_t* xrow, const uint16_t* wr, float* z) {
@@ -149,48 +202,150 @@ int oracle_route(int H, int E, int k, float scale, const uint16_t* x, const uint
  * optional ids/gates [nrows, k], gap [nrows], routed/shared [nrows, H] (each rounded to fp32 on its own).
  * Returns 0, or -1 on bad arguments or allocation failure.
  */
+/* Per-call scratch of the mixture on one token. */
+typedef struct {
+    float *z, *s, *c;
+    char* taken;
+    double *gd, *y, *routed, *shared, *hbuf;
+    int32_t* sel;
+} MixScratch;
+
+static void mix_free(MixScratch* m) {
+    free(m->z); free(m->taken); free(m->gd); free(m->sel); free(m->y); free(m->routed); free(m->shared);
+    free(m->hbuf);
+}
+
+static int mix_alloc(MixScratch* m, int H, int E, int k, int wmax) {
+    m->z = (float*)malloc(sizeof(float) * (size_t)E * 3);
+    m->taken = (char*)malloc((size_t)E);
+    m->gd = (double*)malloc(sizeof(double) * (size_t)k);
+    m->sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    m->y = (double*)malloc(sizeof(double) * (size_t)H);
+    m->routed = (double*)malloc(sizeof(double) * (size_t)H);
+    m->shared = (double*)malloc(sizeof(double) * (size_t)H);
+    m->hbuf = (double*)malloc(sizeof(double) * (size_t)wmax);
+    if (!m->z || !m->taken || !m->gd || !m->sel || !m->y || !m->routed || !m->shared || !m->hbuf) {
+        mix_free(m);
+        return -1;
+    }
+    m->s = m->z + E;
+    m->c = m->z + 2 * E;
+    return 0;
+}
+
+/* The mixture on one token x (a bf16 row): routing into m->sel / m->gd, the gated routed sum into
+ * m->routed and the shared expert into m->shared (both double, unrounded). Returns the selection gap. */
+static double token_mixture(int H, int E, int k, int I, int Is, float scale, const uint16_t* xrow,
+                            const uint16_t* wr, const float* b, const uint16_t* w1, const uint16_t* w3,
+                            const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                            MixScratch* m) {
+    const size_t expert_in = (size_t)I * (size_t)H;
+    token_logits(H, E, xrow, wr, m->z);
+    double g = token_route(E, k, scale, m->z, b, m->s, m->c, m->taken, m->sel, m->gd);
+    for (int i = 0; i < H; ++i) m->routed[i] = 0.0;
+    for (int j = 0; j < k; ++j) {
+        size_t e = (size_t)m->sel[j];
+        swiglu_mlp(H, I, xrow, w1 + e * expert_in, w3 + e * expert_in, w2 + e * expert_in, m->y, m->hbuf);
+        for (int i = 0; i < H; ++i) m->routed[i] += m->gd[j] * m->y[i];
+    }
+    if (Is > 0) swiglu_mlp(H, Is, xrow, ws1, ws3, ws2, m->shared, m->hbuf);
+    else for (int i = 0; i < H; ++i) m->shared[i] = 0.0;
+    return g;
+}
+
+static void store_routing(const MixScratch* m, int k, int r, double g, int32_t* ids, float* gates, double* gap) {
+    if (ids) memcpy(ids + (size_t)r * k, m->sel, sizeof(int32_t) * (size_t)k);
+    if (gates) for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = (float)m->gd[j];
+    if (gap) gap[r] = g;
+}
+
 int oracle_forward(int H, int E, int k, int I, int Is, float scale, const uint16_t* x, const uint16_t* wr,
                    const float* b, const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
                    const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2, const int32_t* rows, int nrows,
                    float* out, int32_t* ids, float* gates, double* gap, float* routed_out, float* shared_out) {
     if (H <= 0 || E <= 0 || k < 1 || k > E || I <= 0 || Is < 0 || nrows < 0) return -1;
-    int wmax = I > Is ? I : Is;
-    float* z = (float*)malloc(sizeof(float) * (size_t)E * 3);
-    char* taken = (char*)malloc((size_t)E);
-    double* gd = (double*)malloc(sizeof(double) * (size_t)k);
-    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-    double* y = (double*)malloc(sizeof(double) * (size_t)H);
-    double* routed = (double*)malloc(sizeof(double) * (size_t)H);
-    double* shared = (double*)malloc(sizeof(double) * (size_t)H);
-    double* hbuf = (double*)malloc(sizeof(double) * (size_t)wmax);
-    if (!z || !taken || !gd || !sel || !y || !routed || !shared || !hbuf) {
-        free(z); free(taken); free(gd); free(sel); free(y); free(routed); free(shared); free(hbuf);
-        return -1;
-    }
-    float* s = z + E;
-    float* c = z + 2 * E;
-    const size_t expert_in = (size_t)I * (size_t)H;
+    MixScratch m;
+    if (mix_alloc(&m, H, E, k, I > Is ? I : Is) != 0) return -1;
     for (int r = 0; r < nrows; ++r) {
         size_t t = rows ? (size_t)rows[r] : (size_t)r;
-        const uint16_t* xrow = x + t * (size_t)H;
-        token_logits(H, E, xrow, wr, z);
-        double g = token_route(E, k, scale, z, b, s, c, taken, sel, gd);
-        for (int m = 0; m < H; ++m) routed[m] = 0.0;
-        for (int j = 0; j < k; ++j) {
-            size_t e = (size_t)sel[j];
-            swiglu_mlp(H, I, xrow, w1 + e * expert_in, w3 + e * expert_in, w2 + e * expert_in, y, hbuf);
-            for (int m = 0; m < H; ++m) routed[m] += gd[j] * y[m];
-        }
-        if (Is > 0) swiglu_mlp(H, Is, xrow, ws1, ws3, ws2, shared, hbuf);
-        else for (int m = 0; m < H; ++m) shared[m] = 0.0;
-        for (int m = 0; m < H; ++m) out[(size_t)r * H + m] = (float)(routed[m] + shared[m]);
-        if (routed_out) for (int m = 0; m < H; ++m) routed_out[(size_t)r * H + m] = (float)routed[m];
-        if (shared_out) for (int m = 0; m < H; ++m) shared_out[(size_t)r * H + m] = (float)shared[m];
-        if (ids) memcpy(ids + (size_t)r * k, sel, sizeof(int32_t) * (size_t)k);
-        if (gates) for (int j = 0; j < k; ++j) gates[(size_t)r * k + j] = (float)gd[j];
-        if (gap) gap[r] = g;
+        double g = token_mixture(H, E, k, I, Is, scale, x + t * (size_t)H, wr, b, w1, w3, w2, ws1, ws3, ws2, &m);
+        for (int i = 0; i < H; ++i) out[(size_t)r * H + i] = (float)(m.routed[i] + m.shared[i]);
+        if (routed_out) for (int i = 0; i < H; ++i) routed_out[(size_t)r * H + i] = (float)m.routed[i];
+        if (shared_out) for (int i = 0; i < H; ++i) shared_out[(size_t)r * H + i] = (float)m.shared[i];
+        store_routing(&m, k, r, g, ids, gates, gap);
     }
-    free(z); free(taken); free(gd); free(sel); free(y); free(routed); free(shared); free(hbuf);
+    mix_free(&m);
+    return 0;
+}
+
+/*
+ * RMSNorm of the listed rows of x [*, H] with weight gamma [H]: out [nrows, H] bf16 by list position.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_rmsnorm(int H, double eps, const uint16_t* x, const uint16_t* gamma, const int32_t* rows, int nrows,
+                   uint16_t* out) {
+    if (H <= 0 || nrows < 0 || !(eps >= 0.0)) return -1;
+    for (int r = 0; r < nrows; ++r) {
+        size_t t = rows ? (size_t)rows[r] : (size_t)r;
+        rmsnorm_row(H, eps, x + t * (size_t)H, gamma, out + (size_t)r * H);
+    }
+    return 0;
+}
+
+/*
+ * The mixture half of a GLM-5 block on the residual stream x' [*, H]: x_ffn = RMSNorm(x') (bf16), the
+ * mixture on x_ffn, and the residual add out = fp32(x' + routed + shared). Outputs by list position:
+ * out [nrows, H]; optional x_norm [nrows, H] bf16, ids/gates [nrows, k], gap [nrows].
+ */
+int oracle_block_forward(int H, int E, int k, int I, int Is, float scale, double eps, const uint16_t* resid,
+                         const uint16_t* gamma, const uint16_t* wr, const float* b, const uint16_t* w1,
+                         const uint16_t* w3, const uint16_t* w2, const uint16_t* ws1, const uint16_t* ws3,
+                         const uint16_t* ws2, const int32_t* rows, int nrows, float* out, uint16_t* x_norm,
+                         int32_t* ids, float* gates, double* gap) {
+    if (H <= 0 || E <= 0 || k < 1 || k > E || I <= 0 || Is < 0 || nrows < 0 || !(eps >= 0.0)) return -1;
+    MixScratch m;
+    if (mix_alloc(&m, H, E, k, I > Is ? I : Is) != 0) return -1;
+    uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+    if (!xn) {
+        mix_free(&m);
+        return -1;
+    }
+    for (int r = 0; r < nrows; ++r) {
+        size_t t = rows ? (size_t)rows[r] : (size_t)r;
+        const uint16_t* xr = resid + t * (size_t)H;
+        rmsnorm_row(H, eps, xr, gamma, xn);
+        double g = token_mixture(H, E, k, I, Is, scale, xn, wr, b, w1, w3, w2, ws1, ws3, ws2, &m);
+        for (int i = 0; i < H; ++i)
+            out[(size_t)r * H + i] = (float)(oracle_bf16_to_double(xr[i]) + m.routed[i] + m.shared[i]);
+        if (x_norm) memcpy(x_norm + (size_t)r * H, xn, sizeof(uint16_t) * (size_t)H);
+        store_routing(&m, k, r, g, ids, gates, gap);
+    }
+    free(xn);
+    mix_free(&m);
+    return 0;
+}
+
+/*
+ * Dense SwiGLU MLP of the listed rows of x [*, H]: out [nrows, H] = fp32((silu(x W1) * (x W3)) W2), with
+ * W1, W3 [Id, H] and W2 [H, Id]. Returns 0, or -1 on bad arguments or allocation failure.
+ */
+int oracle_dense_mlp(int H, int Id, const uint16_t* x, const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                     const int32_t* rows, int nrows, float* out) {
+    if (H <= 0 || Id <= 0 || nrows < 0) return -1;
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* hbuf = (double*)malloc(sizeof(double) * (size_t)Id);
+    if (!y || !hbuf) {
+        free(y);
+        free(hbuf);
+        return -1;
+    }
+    for (int r = 0; r < nrows; ++r) {
+        size_t t = rows ? (size_t)rows[r] : (size_t)r;
+        swiglu_mlp(H, Id, x + t * (size_t)H, w1, w3, w2, y, hbuf);
+        for (int i = 0; i < H; ++i) out[(size_t)r * H + i] = (float)y[i];
+    }
+    free(y);
+    free(hbuf);
     return 0;
 }
 

@@ -125,7 +125,8 @@ def test_permute_parity(moe, name):
         (ref["counts"] > 0).sum(), ref["counts"].max(), (ref["counts"] == 0).sum()))
 
 
-SAMPLE = {"tiny": None, "mid": 512, "glm5_decode": None, "glm5_prefill": 96, "glm5_skewed": 64}
+SAMPLE = {"tiny": None, "mid": 512, "glm5_decode": None, "glm5_prefill": 96, "glm5_skewed": 64,
+          "glm47_decode": None, "glm47_prefill": 256}
 
 
 @pytest.mark.parametrize("name", ALL)

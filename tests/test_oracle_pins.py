@@ -83,6 +83,17 @@ def test_workload_shapes_follow_pages():
     c = wl.BY_NAME["mid"]
     assert (c.H, c.E, c.k, c.I) == (f["hidden_size"], f["n_routed_experts"], f["num_experts_per_tok"],
                                     f["moe_intermediate_size"])
+    for name in ("glm47_decode", "glm47_prefill"):
+        c = wl.BY_NAME[name]
+        assert (c.H, c.E, c.k, c.I, c.Is, c.scale) == (
+            f["hidden_size"], f["n_routed_experts"], f["num_experts_per_tok"], f["moe_intermediate_size"],
+            f["n_shared_experts"] * f["moe_intermediate_size"], f["routed_scaling_factor"])
+    dn = load("dense_mlp_and_norm_shapes.json")
+    for name, model in (("glm5_dense_decode", "glm5"), ("glm5_dense_prefill", "glm5"),
+                        ("glm47_dense_prefill", "glm47_flash")):
+        c = wl.DENSE_BY_NAME[name]
+        assert (c.H, c.Id) == (dn[model]["hidden_size"], dn[model]["intermediate_size"])
+    assert wl.NORM_EPS == dn["glm5"]["rms_norm_eps"] == dn["glm47_flash"]["rms_norm_eps"]
 
 
 # ---------------------------------------------------------------------------------------------------
@@ -334,3 +345,108 @@ def test_skewed_routing_closed_forms():
     # experts 0..7 outrank every i >= 59: b_j - b_i >= 0.5 ln(60 / 8) > 1 >= s_i - s_j
     assert np.all(counts[59:] == 0)
     assert counts.sum() == cfg.T * cfg.k
+
+
+# ---------------------------------------------------------------------------------------------------
+# bf16 rounding, RMSNorm, the block's residual wiring and the dense MLP
+
+def f32_to_bf16_rne(f):
+    """Textbook fp32 -> bf16 round-to-nearest-even with integer operations (finite inputs)."""
+    b = np.asarray(f, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_round_bf16_against_fp32_rounding_and_ties():
+    rng = np.random.default_rng(5)
+    f = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    got = np.array([oracle.round_bf16(float(v)) for v in f], np.uint16)
+    assert np.array_equal(got, f32_to_bf16_rne(f))
+    # halfway cases go to the even neighbour; a bit below fp32's precision breaks the tie upward (a detour
+    # through fp32 would lose it and round down)
+    assert oracle.round_bf16(1 + 2 ** -8) == 0x3F80
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 0x3F82
+    assert oracle.round_bf16(1 + 2 ** -8 + 2 ** -40) == 0x3F81
+    assert oracle.round_bf16(-(1 + 2 ** -8 + 2 ** -40)) == 0xBF81
+    # subnormals step by 2^-133; the largest finite bf16 is 0x7F7F
+    assert oracle.round_bf16(2.0 ** -133) == 0x0001
+    assert oracle.round_bf16(1.5 * 2.0 ** -133) == 0x0002
+    assert oracle.round_bf16(2.0 ** -126) == 0x0080
+    assert oracle.round_bf16(0.0) == 0x0000 and oracle.round_bf16(-0.0) == 0x8000
+    assert oracle.round_bf16(3.3895313892515355e38) == 0x7F7F
+    assert oracle.round_bf16(3.4e38) == 0x7F80
+
+
+def test_rmsnorm_scale_invariance_and_closed_forms():
+    H = 256
+    gamma = wl.norm_weight(H, 11)
+    x = wl.normal_bf16(3, 0, 1.0, 0, 8 * H).reshape(8, H)
+    assert np.all((x & 0x7F80) > 0x0080) and np.all((x & 0x7F80) < 0x7E00)  # normal, room to double
+    # eps = 0: doubling x (exponent + 1, exact) leaves x / rms unchanged bit for bit
+    x2 = (x + 0x0080).astype(np.uint16)
+    assert np.array_equal(dec(x2), 2 * dec(x))
+    assert np.array_equal(oracle.rmsnorm(x2, gamma, 0.0), oracle.rmsnorm(x, gamma, 0.0))
+    # a constant row c: x / rms = sign(c), so the row is gamma or -gamma exactly
+    xc = np.stack([np.full(H, enc_exact([0.75])[0]), np.full(H, enc_exact([-3.0])[0])])
+    out = oracle.rmsnorm(xc, gamma, 0.0)
+    assert np.array_equal(out[0], gamma) and np.array_equal(out[1], gamma ^ 0x8000)
+    # eps = 3 c^2 halves it: x / sqrt(c^2 + 3 c^2) = sign(c) / 2
+    for c in (2.0, -0.5):
+        row = np.full((1, H), enc_exact([c])[0])
+        half = oracle.rmsnorm(row, gamma, 3 * c * c)[0]
+        assert np.array_equal(dec(half), np.sign(c) * dec(gamma) / 2)
+    # a one-hot row a e_j (H = 256): rms = |a| / 16, so position j holds 16 sign(a) gamma_j, the rest 0
+    for a, j in ((4.0, 5), (-0.25, 200)):
+        row = np.zeros((1, H), np.uint16)
+        row[0, j] = enc_exact([a])[0]
+        out = oracle.rmsnorm(row, gamma, 0.0)[0]
+        want = np.zeros(H)
+        want[j] = 16 * np.sign(a) * dec(gamma[j])
+        assert np.array_equal(dec(out), want)
+    # a zero row stays zero with eps > 0; mean((out / gamma)^2) = m / (m + eps) for mean square m
+    assert np.all(dec(oracle.rmsnorm(np.zeros((1, H), np.uint16), gamma, 1e-5)) == 0)
+    out = dec(oracle.rmsnorm(x, gamma, 0.5))
+    m = np.mean(dec(x) ** 2, axis=1)
+    assert np.allclose(np.mean((out / dec(gamma)) ** 2, axis=1), m / (m + 0.5), rtol=1e-2)
+    # rows are independent and the listed-rows form picks the same bytes
+    assert np.array_equal(oracle.rmsnorm(x, gamma, 1e-5, rows=[6, 1]), oracle.rmsnorm(x, gamma, 1e-5)[[6, 1]])
+
+
+def test_block_forward_wires_norm_and_residual():
+    d = small_inputs(T=6, H=128, E=8, I=64, Is=64, seed=21)
+    gamma = wl.norm_weight(128, 21)
+    k, scale, eps = 2, 2.5, 1e-5
+    blk = oracle.block_forward(d, gamma, eps, k, scale)
+    xn = oracle.rmsnorm(d["x"], gamma, eps)
+    assert np.array_equal(blk["x_norm"], xn)
+    dn = dict(d)
+    dn["x"] = xn
+    f = oracle.forward(dn, k, scale, parts=True)
+    assert np.array_equal(blk["ids"], f["ids"]) and np.array_equal(blk["gates"], f["gates"])
+    # out = x' + routed + shared, rounded once: within an ulp of the sum of the separately rounded parts
+    want = dec(d["x"]) + f["routed"].astype(np.float64) + f["shared"].astype(np.float64)
+    assert np.allclose(blk["out"], want, rtol=0, atol=2 * np.spacing(np.float32(np.abs(want).max())))
+    # with eps = 0 the norm ignores the stream's scale, so doubling x' doubles only the residual term
+    d2 = dict(d)
+    d2["x"] = (d["x"] + 0x0080).astype(np.uint16)
+    b1 = oracle.block_forward(d, gamma, 0.0, k, scale)
+    b2 = oracle.block_forward(d2, gamma, 0.0, k, scale)
+    assert np.array_equal(b1["x_norm"], b2["x_norm"])
+    delta1 = b1["out"].astype(np.float64) - dec(d["x"])
+    delta2 = b2["out"].astype(np.float64) - dec(d2["x"])
+    assert np.allclose(delta1, delta2, rtol=0, atol=4 * np.spacing(np.float32(np.abs(dec(d2["x"])).max())))
+
+
+def test_dense_mlp_against_numpy_matmuls():
+    H, Id, T = 96, 160, 5
+    x = wl.normal_bf16(31, 0, 1.0, 0, T * H).reshape(T, H)
+    w1 = wl.normal_bf16(31, 10, 0.02, 0, Id * H).reshape(Id, H)
+    w3 = wl.normal_bf16(31, 11, 0.02, 0, Id * H).reshape(Id, H)
+    w2 = wl.normal_bf16(31, 12, 0.02, 0, H * Id).reshape(H, Id)
+    got = oracle.dense_mlp(x, w1, w3, w2)
+    ref = np_swiglu(dec(x), dec(w1), dec(w3), dec(w2))
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-12)
+    assert np.array_equal(oracle.dense_mlp(x, w1, w3, w2, rows=[4, 0]), got[[4, 0]])
+    # the mixture with one expert, k = 1, scale 1 and no shared expert is exactly this MLP
+    d = {"x": x, "wr": wl.normal_bf16(31, 1, 0.02, 0, H).reshape(1, H), "b": np.zeros(1, np.float32),
+         "w1": w1[None], "w3": w3[None], "w2": w2[None], "ws1": None, "ws3": None, "ws2": None}
+    assert np.array_equal(oracle.forward(d, 1, 1.0)["out"], got)

@@ -8,8 +8,13 @@ Shapes follow the pages:
 * GLM-5 (GlmMoeDsa) MoE block: hidden 6144, 256 routed experts, top-8, expert width 2048, one shared
   expert of the same width, routed scaling factor 2.5 (nnterp encyclopedia "glm_moe_dsa", Config table;
   atlas.klimoza.dev GLM-5 "Vocabulary projection", config.json).
-* GLM-4.7-Flash (Glm4MoeLite): hidden 2048, 64 experts, top-4, width 1536 (nnterp encyclopedia
-  "glm4_moe_lite", Config table); the mid workload keeps those shapes at scale 1.0.
+* GLM-4.7-Flash (Glm4MoeLite): hidden 2048, 64 experts, top-4, width 1536, one shared expert, routed
+  scaling factor 1.8 (nnterp encyclopedia "glm4_moe_lite", Config table); the mid workload keeps those
+  shapes at scale 1.0, the glm47 workloads use the model's own scale.
+* Dense-first blocks: the dense SwiGLU MLP of GLM-5 (intermediate 12288) and GLM-4.7-Flash (10240)
+  (the module trees' GlmMoeDsaMLP / Glm4MoeLiteMLP gate_proj, up_proj, down_proj).
+* The RMSNorm before the mixture has eps 1e-5 on both models (post_attention_layernorm in the module
+  trees); its weight gamma ~ 1 + N(0, 0.1) stands in for a trained one.
 
 Value distributions: x ~ N(0, 1) stands in for the RMS-normalised stream that enters the mixture (the
 GLM-5 block's equations on open-model-atlas apply RMSNorm before the router); weights ~ N(0, 0.02), the
@@ -33,11 +38,13 @@ _lib = None
 _lib_lock = threading.Lock()
 
 # Tensor ids of the counter-based generator.
-T_X, T_WR, T_B, T_W1, T_W3, T_W2, T_WS1, T_WS3, T_WS2 = range(9)
+T_X, T_WR, T_B, T_W1, T_W3, T_W2, T_WS1, T_WS3, T_WS2, T_GAMMA, T_WD1, T_WD3, T_WD2 = range(13)
 
 SIGMA_W = 0.02
 BIAS_LO, BIAS_HI = -0.1, 0.1
 SKEW_ALPHA, SKEW_POWER, SKEW_BIAS_COEF = 0.02, 1.2, 0.5
+NORM_EPS = 1e-5
+GAMMA_SIGMA = 0.1
 
 
 def build(force: bool = False) -> str:
@@ -116,10 +123,44 @@ CONFIGS = [
     MoEConfig(3, "glm5_prefill", T=8192, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5, weights_of=2),
     MoEConfig(4, "glm5_skewed", T=32768, H=6144, E=256, k=8, I=2048, Is=2048, scale=2.5, skewed=True,
               weights_of=2),
+    MoEConfig(5, "glm47_decode", T=16, H=2048, E=64, k=4, I=1536, Is=1536, scale=1.8),
+    MoEConfig(6, "glm47_prefill", T=8192, H=2048, E=64, k=4, I=1536, Is=1536, scale=1.8, weights_of=5),
 ]
 # The three GLM-5 workloads are one layer (one set of expert weights, 19.3 GB of routed experts) run on
-# three token batches; each has its own tokens, router weight and bias.
+# three token batches; each has its own tokens, router weight and bias. The two GLM-4.7-Flash workloads
+# likewise share one layer.
 BY_NAME = {c.name: c for c in CONFIGS}
+
+
+@dataclass(frozen=True)
+class DenseConfig:
+    """The dense SwiGLU MLP of a dense-first block: x [T, H] -> (silu(x W1) * (x W3)) W2, width Id."""
+    index: int
+    name: str
+    T: int
+    H: int
+    Id: int
+    weights_of: int = -1
+
+    @property
+    def seed(self) -> int:
+        return 0x5EED0000 + self.index
+
+    @property
+    def weight_seed(self) -> int:
+        return 0x5EED0000 + (self.index if self.weights_of < 0 else self.weights_of)
+
+    def flops(self) -> int:
+        return 6 * self.T * self.H * self.Id
+
+
+DENSE_CONFIGS = [
+    DenseConfig(7, "dense_tiny", T=64, H=256, Id=384),
+    DenseConfig(8, "glm5_dense_decode", T=16, H=6144, Id=12288),
+    DenseConfig(9, "glm5_dense_prefill", T=8192, H=6144, Id=12288, weights_of=8),
+    DenseConfig(10, "glm47_dense_prefill", T=8192, H=2048, Id=10240),
+]
+DENSE_BY_NAME = {c.name: c for c in DENSE_CONFIGS}
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -183,6 +224,23 @@ def weight(cfg: MoEConfig, name: str, seed: int | None = None) -> np.ndarray:
     tid, shape = weight_shapes(cfg)[name]
     n = int(np.prod(shape))
     return normal_bf16(seed, tid, SIGMA_W, 0, n).reshape(shape)
+
+
+def norm_weight(H: int, seed: int) -> np.ndarray:
+    """RMSNorm weight gamma [H] as bf16 bits: bf16(1 + bf16(0.1 N))."""
+    dev = normal_bf16(seed, T_GAMMA, GAMMA_SIGMA, 0, H)
+    vals = (dev.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.array([lib().gen_bf16_from_double(1.0 + v) for v in vals], dtype=np.uint16)
+
+
+def dense_tokens(cfg: DenseConfig) -> np.ndarray:
+    return normal_bf16(cfg.seed, T_X, 1.0, 0, cfg.T * cfg.H).reshape(cfg.T, cfg.H)
+
+
+def dense_weight(cfg: DenseConfig, name: str) -> np.ndarray:
+    tid, shape = {"w1": (T_WD1, (cfg.Id, cfg.H)), "w3": (T_WD3, (cfg.Id, cfg.H)),
+                  "w2": (T_WD2, (cfg.H, cfg.Id))}[name]
+    return normal_bf16(cfg.weight_seed, tid, SIGMA_W, 0, int(np.prod(shape))).reshape(shape)
 
 
 def host_inputs(cfg: MoEConfig, seed: int | None = None, with_weights: bool = True) -> dict:
