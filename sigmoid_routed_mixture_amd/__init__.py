@@ -10,6 +10,17 @@ include/moe.h. PyTorch supplies device memory and streams. The functions keep th
     moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids=None,
                 topk_gates=None, expert_counts=None, stream=None, stream_shared=None)
 
+and those of include/moe_block.h:
+
+    moe_forward_routed(x, topk_ids, topk_gates, w1, w3, w2, ws1, ws3, ws2, out, workspace, expert_counts=None,
+                       stream=None, stream_shared=None)
+    moe_block_workspace_bytes(T, H, E, k, I, Is)
+    moe_block_forward(resid, gamma, eps, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace,
+                      x_norm=None, topk_ids=None, topk_gates=None, expert_counts=None, stream=None,
+                      stream_shared=None)
+    moe_dense_mlp_workspace_bytes(T, H, I)
+    moe_dense_mlp(x, w1, w3, w2, out, workspace, stream=None)
+
 bf16 tensors are torch.bfloat16; ids and counts int32; gates, bias, logits and out float32. All tensors
 must be contiguous and on the same HIP device. A non-OK status raises MoEError with the library's text.
 If libmoe.so is missing this module raises at import: there is no fallback.
@@ -42,6 +53,17 @@ _lib.moe_forward.argtypes = [_p] * 9 + [_i] * 6 + [_f] + [_p] * 5 + [_sz, _p, _p
 _lib.moe_forward.restype = _i
 _lib.moe_forward_profiled.argtypes = [_p] * 9 + [_i] * 6 + [_f] + [_p] * 5 + [_sz, _p, _p, _p]
 _lib.moe_forward_profiled.restype = _i
+_d = ctypes.c_double
+_lib.moe_forward_routed.argtypes = [_p] * 9 + [_i] * 6 + [_p, _p, _p, _sz, _p, _p]
+_lib.moe_forward_routed.restype = _i
+_lib.moe_block_workspace_bytes.argtypes = [_i] * 6
+_lib.moe_block_workspace_bytes.restype = _sz
+_lib.moe_block_forward.argtypes = [_p, _p, _d] + [_p] * 8 + [_i] * 6 + [_f] + [_p] * 6 + [_sz, _p, _p]
+_lib.moe_block_forward.restype = _i
+_lib.moe_dense_mlp_workspace_bytes.argtypes = [_i] * 3
+_lib.moe_dense_mlp_workspace_bytes.restype = _sz
+_lib.moe_dense_mlp.argtypes = [_p] * 4 + [_i] * 3 + [_p, _p, _sz, _p]
+_lib.moe_dense_mlp.restype = _i
 _lib.moe_status_string.argtypes = [_i]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = []
@@ -49,7 +71,9 @@ _lib.moe_last_error.restype = ctypes.c_char_p
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_route", "moe_permute",
-                    "moe_forward", "moe_forward_profiled", "moe_status_string", "moe_last_error")
+                    "moe_forward", "moe_forward_profiled", "moe_status_string", "moe_last_error",
+                    "moe_forward_routed", "moe_block_workspace_bytes", "moe_block_forward",
+                    "moe_dense_mlp_workspace_bytes", "moe_dense_mlp")
 
 
 class MoEError(RuntimeError):
@@ -149,6 +173,60 @@ def moe_forward_profiled(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale,
     handles = (ctypes.c_void_p * 7)(*[e.cuda_event for e in events])
     _forward(_lib.moe_forward_profiled, (handles,), x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out,
              workspace, topk_ids, topk_gates, expert_counts, stream, stream_shared)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def moe_forward_routed(x, topk_ids, topk_gates, w1, w3, w2, ws1, ws3, ws2, out, workspace, expert_counts=None,
+                       stream=None, stream_shared=None):
+    T, H = x.shape
+    E, I, _ = w1.shape
+    k = topk_ids.shape[1]
+    Is = 0 if ws1 is None else ws1.shape[0]
+    bf = torch.bfloat16
+    s1 = None if stream_shared is None else _stream(stream_shared, x.device)
+    _check(_lib.moe_forward_routed(
+        _ptr(x, bf, "x"), _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_gates, torch.float32, "topk_gates"),
+        _ptr(w1, bf, "w1"), _ptr(w3, bf, "w3"), _ptr(w2, bf, "w2"), _ptr(ws1, bf, "ws1"), _ptr(ws3, bf, "ws3"),
+        _ptr(ws2, bf, "ws2"), T, H, E, k, I, Is, _ptr(out, torch.float32, "out"),
+        _ptr(expert_counts, torch.int32, "expert_counts"), _ptr(workspace, None, "workspace"), _nbytes(workspace),
+        _stream(stream, x.device), s1))
+
+
+def moe_block_workspace_bytes(T: int, H: int, E: int, k: int, I: int, Is: int) -> int:
+    return _lib.moe_block_workspace_bytes(T, H, E, k, I, Is)
+
+
+def moe_block_forward(resid, gamma, eps, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace,
+                      x_norm=None, topk_ids=None, topk_gates=None, expert_counts=None, stream=None,
+                      stream_shared=None):
+    T, H = resid.shape
+    E, I, _ = w1.shape
+    Is = 0 if ws1 is None else ws1.shape[0]
+    bf = torch.bfloat16
+    s1 = None if stream_shared is None else _stream(stream_shared, resid.device)
+    _check(_lib.moe_block_forward(
+        _ptr(resid, bf, "resid"), _ptr(gamma, bf, "gamma"), float(eps), _ptr(w_router, bf, "w_router"),
+        _ptr(bias, torch.float32, "bias"), _ptr(w1, bf, "w1"), _ptr(w3, bf, "w3"), _ptr(w2, bf, "w2"),
+        _ptr(ws1, bf, "ws1"), _ptr(ws3, bf, "ws3"), _ptr(ws2, bf, "ws2"), T, H, E, k, I, Is, float(scale),
+        _ptr(out, torch.float32, "out"), _ptr(x_norm, bf, "x_norm"), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_gates, torch.float32, "topk_gates"), _ptr(expert_counts, torch.int32, "expert_counts"),
+        _ptr(workspace, None, "workspace"), _nbytes(workspace), _stream(stream, resid.device), s1))
+
+
+def moe_dense_mlp_workspace_bytes(T: int, H: int, I: int) -> int:
+    return _lib.moe_dense_mlp_workspace_bytes(T, H, I)
+
+
+def moe_dense_mlp(x, w1, w3, w2, out, workspace, stream=None):
+    T, H = x.shape
+    I = w1.shape[0]
+    bf = torch.bfloat16
+    _check(_lib.moe_dense_mlp(_ptr(x, bf, "x"), _ptr(w1, bf, "w1"), _ptr(w3, bf, "w3"), _ptr(w2, bf, "w2"), T, H, I,
+                              _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+                              _nbytes(workspace), _stream(stream, x.device)))
 
 
 class MoELayer:

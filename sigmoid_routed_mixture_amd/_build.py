@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 OBJDIR = os.path.join(ROOT, "_build", "moe")
 
-HIP_SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "api.hip"]
+HIP_SOURCES = ["router.hip", "permute.hip", "gemm.hip", "combine.hip", "norm.hip", "api.hip"]
 CXX_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

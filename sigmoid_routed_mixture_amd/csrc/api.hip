@@ -6,6 +6,7 @@
 
 #include "kernels.h"
 #include "moe.h"
+#include "moe_block.h"
 #include "moe_profile.h"
 #include "plan.h"
 
@@ -87,40 +88,90 @@ moe::GemmPath pick_path(int T, int E, int k) {
 
 namespace {
 
-moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float* bias, const moe_bf16* w1,
-                        const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1, const moe_bf16* ws3,
-                        const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is, float scale, float* out,
-                        int32_t* topk_ids, float* topk_gates, int32_t* expert_counts, void* workspace,
-                        size_t workspace_bytes, void* stream, void* stream_shared, void* const* events) {
-    g_last_error.clear();
-    MOE_TRY(from_check(moe::check_sizes(T, H, E, k, I, Is, true)));
-    if (T == 0) return MOE_OK;
-    MOE_TRY(need(x, "x"));
-    MOE_TRY(need(w_router, "w_router"));
-    MOE_TRY(need(bias, "bias"));
-    MOE_TRY(need(w1, "w1"));
-    MOE_TRY(need(w3, "w3"));
-    MOE_TRY(need(w2, "w2"));
-    if (Is > 0) {
-        MOE_TRY(need(ws1, "ws1"));
-        MOE_TRY(need(ws3, "ws3"));
-        MOE_TRY(need(ws2, "ws2"));
-    }
-    MOE_TRY(need(out, "out"));
-    MOE_TRY(optional(topk_ids, "topk_ids"));
-    MOE_TRY(optional(topk_gates, "topk_gates"));
-    MOE_TRY(optional(expert_counts, "expert_counts"));
-    if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is null");
-    MOE_TRY(from_check(moe::check_aligned(workspace, "workspace", 256)));
-    const moe::Layout L = moe::forward_layout(T, H, E, k, I, Is);
-    if (workspace_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_bytes");
-    if (T == 0) return MOE_OK;
+// One mixture pass. The input is either x (the normalised stream) or resid + gamma (the block entry
+// point normalises first and adds resid back in the combine); the routing is either computed (w_router,
+// bias, scale) or given (ids_in, gates_in).
+struct Request {
+    const moe_bf16* x = nullptr;
+    const moe_bf16* resid = nullptr;
+    const moe_bf16* gamma = nullptr;
+    double eps = 0.0;
+    moe_bf16* x_norm = nullptr;
+    const moe_bf16* w_router = nullptr;
+    const float* bias = nullptr;
+    float scale = 1.0f;
+    const int32_t* ids_in = nullptr;
+    const float* gates_in = nullptr;
+    const moe_bf16 *w1 = nullptr, *w3 = nullptr, *w2 = nullptr, *ws1 = nullptr, *ws3 = nullptr, *ws2 = nullptr;
+    int T = 0, H = 0, E = 0, k = 0, I = 0, Is = 0;
+    float* out = nullptr;
+    int32_t* topk_ids = nullptr;
+    float* topk_gates = nullptr;
+    int32_t* expert_counts = nullptr;
+    void* workspace = nullptr;
+    size_t workspace_bytes = 0;
+    void* stream = nullptr;
+    void* stream_shared = nullptr;
+    void* const* events = nullptr;
+};
 
-    char* ws = static_cast<char*>(workspace);
+moe_status forward_impl(const Request& q) {
+    g_last_error.clear();
+    const int T = q.T, H = q.H, E = q.E, k = q.k, I = q.I, Is = q.Is;
+    const bool block = q.resid != nullptr || q.gamma != nullptr;
+    const bool given = q.ids_in != nullptr || q.gates_in != nullptr;
+    MOE_TRY(from_check(moe::check_sizes(T, H, E, k, I, Is, true)));
+    if (block && !(q.eps >= 0.0 && q.eps <= 1e300)) return fail(MOE_ERR_INVALID_ARG, "eps is negative or not finite");
+    if (T == 0) return MOE_OK;
+    if (block) {
+        MOE_TRY(need(q.resid, "resid"));
+        MOE_TRY(need(q.gamma, "gamma"));
+        MOE_TRY(optional(q.x_norm, "x_norm"));
+    } else {
+        MOE_TRY(need(q.x, "x"));
+    }
+    if (given) {
+        MOE_TRY(need(q.ids_in, "topk_ids"));
+        MOE_TRY(need(q.gates_in, "topk_gates"));
+    } else {
+        MOE_TRY(need(q.w_router, "w_router"));
+        MOE_TRY(need(q.bias, "bias"));
+        MOE_TRY(optional(q.topk_ids, "topk_ids"));
+        MOE_TRY(optional(q.topk_gates, "topk_gates"));
+    }
+    MOE_TRY(need(q.w1, "w1"));
+    MOE_TRY(need(q.w3, "w3"));
+    MOE_TRY(need(q.w2, "w2"));
+    if (Is > 0) {
+        MOE_TRY(need(q.ws1, "ws1"));
+        MOE_TRY(need(q.ws3, "ws3"));
+        MOE_TRY(need(q.ws2, "ws2"));
+    }
+    MOE_TRY(need(q.out, "out"));
+    MOE_TRY(optional(q.expert_counts, "expert_counts"));
+    if (q.workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is null");
+    MOE_TRY(from_check(moe::check_aligned(q.workspace, "workspace", 256)));
+    const moe::Layout L = moe::forward_layout(T, H, E, k, I, Is, block);
+    if (q.workspace_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, block ? "workspace smaller than moe_block_workspace_bytes"
+                                             : "workspace smaller than moe_workspace_bytes");
+
+    char* ws = static_cast<char*>(q.workspace);
     auto at = [ws](size_t off) { return static_cast<void*>(ws + off); };
-    int32_t* ids = topk_ids ? topk_ids : static_cast<int32_t*>(at(L.ids));
-    float* gates = topk_gates ? topk_gates : static_cast<float*>(at(L.gates));
-    int32_t* counts = expert_counts ? expert_counts : static_cast<int32_t*>(at(L.counts));
+    const int32_t* ids;
+    const float* gates;
+    int32_t* ids_out = nullptr;
+    float* gates_out = nullptr;
+    if (given) {
+        ids = q.ids_in;
+        gates = q.gates_in;
+    } else {
+        ids_out = q.topk_ids ? q.topk_ids : static_cast<int32_t*>(at(L.ids));
+        gates_out = q.topk_gates ? q.topk_gates : static_cast<float*>(at(L.gates));
+        ids = ids_out;
+        gates = gates_out;
+    }
+    int32_t* counts = q.expert_counts ? q.expert_counts : static_cast<int32_t*>(at(L.counts));
     int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
     int32_t* row_token = static_cast<int32_t*>(at(L.row_token));
     int32_t* slot_row = static_cast<int32_t*>(at(L.slot_row));
@@ -131,8 +182,8 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     uint16_t* h_sh = Is > 0 ? static_cast<uint16_t*>(at(L.h_sh)) : nullptr;
     float* y_sh = Is > 0 ? static_cast<float*>(at(L.y_sh)) : nullptr;
 
-    hipStream_t s0 = static_cast<hipStream_t>(stream);
-    hipStream_t s1 = static_cast<hipStream_t>(stream_shared);
+    hipStream_t s0 = static_cast<hipStream_t>(q.stream);
+    hipStream_t s1 = static_cast<hipStream_t>(q.stream_shared);
     const bool two_streams = Is > 0 && s1 != nullptr && s1 != s0;
     DeviceEvents* ev = nullptr;
     if (two_streams) MOE_TRY(device_events(&ev));
@@ -142,14 +193,23 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     const int BM = wide ? moe::kWideBM : moe::kSkinnyBM;
 
     auto mark = [&](int i) -> moe_status {
-        if (events == nullptr) return MOE_OK;
-        return from_hip(hipEventRecord(static_cast<hipEvent_t>(events[i]), s0), "hipEventRecord (profile)");
+        if (q.events == nullptr) return MOE_OK;
+        return from_hip(hipEventRecord(static_cast<hipEvent_t>(q.events[i]), s0), "hipEventRecord (profile)");
     };
     MOE_TRY(mark(0));
-    const int S = moe::router_splits(T, H);
-    MOE_HIP(moe::launch_router(x, w_router, bias, T, H, E, k, scale, ids, gates, nullptr,
-                               static_cast<float*>(at(L.partial)), S, s0),
-            "router");
+    // the mixture's input: x, or RMSNorm(resid) written to the caller's x_norm or the workspace
+    const uint16_t* xin = q.x;
+    if (block) {
+        uint16_t* xn = q.x_norm ? q.x_norm : static_cast<uint16_t*>(at(L.x_norm));
+        MOE_HIP(moe::launch_rmsnorm(q.resid, q.gamma, q.eps, T, H, xn, s0), "rmsnorm");
+        xin = xn;
+    }
+    if (!given) {
+        const int S = moe::router_splits(T, H);
+        MOE_HIP(moe::launch_router(xin, q.w_router, q.bias, T, H, E, k, q.scale, ids_out, gates_out, nullptr,
+                                   static_cast<float*>(at(L.partial)), S, s0),
+                "router");
+    }
     MOE_TRY(mark(1));
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
                                 static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, s0),
@@ -161,9 +221,9 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     if (Is > 0) {
         hipStream_t ss = two_streams ? s1 : s0;
         moe::GemmArgs g1{};
-        g1.act = x;
-        g1.w_a = ws1;
-        g1.w_b = ws3;
+        g1.act = xin;
+        g1.w_a = q.ws1;
+        g1.w_b = q.ws3;
         g1.out = h_sh;
         g1.dense_rows = T;
         g1.N = Is;
@@ -172,7 +232,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
         MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, g1, dense_tiles, ss), "shared gate/up GEMM");
         moe::GemmArgs g2{};
         g2.act = h_sh;
-        g2.w_a = ws2;
+        g2.w_a = q.ws2;
         g2.out = y_sh;
         g2.dense_rows = T;
         g2.N = H;
@@ -183,10 +243,10 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
 
     const int64_t grid_tiles = moe::max_tiles(T, E, k, BM);
     moe::GemmArgs r1{};
-    r1.act = x;
+    r1.act = xin;
     r1.row_token = row_token;
-    r1.w_a = w1;
-    r1.w_b = w3;
+    r1.w_a = q.w1;
+    r1.w_b = q.w3;
     r1.out = h_perm;
     r1.counts = counts;
     r1.offsets = offsets;
@@ -199,7 +259,7 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
     r2.act = h_perm;
-    r2.w_a = w2;
+    r2.w_a = q.w2;
     r2.out = y_perm;
     r2.counts = counts;
     r2.offsets = offsets;
@@ -212,9 +272,43 @@ moe_status forward_impl(const moe_bf16* x, const moe_bf16* w_router, const float
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
-    MOE_HIP(moe::launch_combine(y_perm, gates, slot_row, y_sh, T, H, k, out, s0), "combine");
+    MOE_HIP(moe::launch_combine(y_perm, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out, s0),
+            "combine");
     MOE_TRY(mark(6));
     return MOE_OK;
+}
+
+Request plain_request(const moe_bf16* x, const moe_bf16* w_router, const float* bias, const moe_bf16* w1,
+                      const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1, const moe_bf16* ws3,
+                      const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is, float scale, float* out,
+                      int32_t* topk_ids, float* topk_gates, int32_t* expert_counts, void* workspace,
+                      size_t workspace_bytes, void* stream, void* stream_shared) {
+    Request q;
+    q.x = x;
+    q.w_router = w_router;
+    q.bias = bias;
+    q.w1 = w1;
+    q.w3 = w3;
+    q.w2 = w2;
+    q.ws1 = ws1;
+    q.ws3 = ws3;
+    q.ws2 = ws2;
+    q.T = T;
+    q.H = H;
+    q.E = E;
+    q.k = k;
+    q.I = I;
+    q.Is = Is;
+    q.scale = scale;
+    q.out = out;
+    q.topk_ids = topk_ids;
+    q.topk_gates = topk_gates;
+    q.expert_counts = expert_counts;
+    q.workspace = workspace;
+    q.workspace_bytes = workspace_bytes;
+    q.stream = stream;
+    q.stream_shared = stream_shared;
+    return q;
 }
 
 } // namespace
@@ -294,8 +388,92 @@ moe_status moe_forward(const moe_bf16* x, const moe_bf16* w_router, const float*
                        const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is, float scale, float* out,
                        int32_t* topk_ids, float* topk_gates, int32_t* expert_counts, void* workspace,
                        size_t workspace_bytes, void* stream, void* stream_shared) {
-    return forward_impl(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out, topk_ids,
-                        topk_gates, expert_counts, workspace, workspace_bytes, stream, stream_shared, nullptr);
+    return forward_impl(plain_request(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out,
+                                      topk_ids, topk_gates, expert_counts, workspace, workspace_bytes, stream,
+                                      stream_shared));
+}
+
+moe_status moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_gates,
+                              const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1,
+                              const moe_bf16* ws3, const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is,
+                              float* out, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                              void* stream, void* stream_shared) {
+    Request q = plain_request(x, nullptr, nullptr, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, 1.0f, out,
+                              nullptr, nullptr, expert_counts, workspace, workspace_bytes, stream, stream_shared);
+    q.ids_in = topk_ids;
+    q.gates_in = topk_gates;
+    if (T > 0 && (topk_ids == nullptr || topk_gates == nullptr)) {
+        g_last_error.clear();
+        return fail(MOE_ERR_INVALID_ARG, topk_ids == nullptr ? "topk_ids is null" : "topk_gates is null");
+    }
+    return forward_impl(q);
+}
+
+size_t moe_block_workspace_bytes(int T, int H, int E, int k, int I, int Is) {
+    if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) return 0;
+    return moe::forward_layout(T, H, E, k, I, Is, true).total;
+}
+
+moe_status moe_block_forward(const moe_bf16* resid, const moe_bf16* gamma, double eps, const moe_bf16* w_router,
+                             const float* bias, const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2,
+                             const moe_bf16* ws1, const moe_bf16* ws3, const moe_bf16* ws2, int T, int H, int E,
+                             int k, int I, int Is, float scale, float* out, moe_bf16* x_norm, int32_t* topk_ids,
+                             float* topk_gates, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                             void* stream, void* stream_shared) {
+    Request q = plain_request(nullptr, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out,
+                              topk_ids, topk_gates, expert_counts, workspace, workspace_bytes, stream, stream_shared);
+    q.resid = resid;
+    q.gamma = gamma;
+    q.eps = eps;
+    q.x_norm = x_norm;
+    if (T > 0 && (resid == nullptr || gamma == nullptr)) {
+        g_last_error.clear();
+        return fail(MOE_ERR_INVALID_ARG, resid == nullptr ? "resid is null" : "gamma is null");
+    }
+    return forward_impl(q);
+}
+
+size_t moe_dense_mlp_workspace_bytes(int T, int H, int I) {
+    if (!moe::check_dense_sizes(T, H, I).ok()) return 0;
+    return moe::dense_workspace_bytes(T, I);
+}
+
+moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2, int T,
+                         int H, int I, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    MOE_TRY(from_check(moe::check_dense_sizes(T, H, I)));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(need(x, "x"));
+    MOE_TRY(need(w1, "w1"));
+    MOE_TRY(need(w3, "w3"));
+    MOE_TRY(need(w2, "w2"));
+    MOE_TRY(need(out, "out"));
+    if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is null");
+    MOE_TRY(from_check(moe::check_aligned(workspace, "workspace", 256)));
+    if (workspace_bytes < moe::dense_workspace_bytes(T, I))
+        return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dense_mlp_workspace_bytes");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool wide = pick_path(T, 1, 1) == moe::GemmPath::Wide;
+    const int BM = wide ? moe::kWideBM : moe::kSkinnyBM;
+    const int64_t tiles = ((int64_t)T + BM - 1) / BM;
+    moe::GemmArgs g1{};
+    g1.act = x;
+    g1.w_a = w1;
+    g1.w_b = w3;
+    g1.out = workspace;
+    g1.dense_rows = T;
+    g1.N = I;
+    g1.K = H;
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, g1, tiles, s), "dense gate/up GEMM");
+    moe::GemmArgs g2{};
+    g2.act = static_cast<const uint16_t*>(workspace);
+    g2.w_a = w2;
+    g2.out = out;
+    g2.dense_rows = T;
+    g2.N = H;
+    g2.K = I;
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, g2, tiles, s), "dense down GEMM");
+    return MOE_OK;
 }
 
 moe_status moe_forward_profiled(const moe_bf16* x, const moe_bf16* w_router, const float* bias,
@@ -307,8 +485,10 @@ moe_status moe_forward_profiled(const moe_bf16* x, const moe_bf16* w_router, con
     if (events == nullptr) return fail(MOE_ERR_INVALID_ARG, "events is null");
     for (int i = 0; i < 7; ++i)
         if (events[i] == nullptr) return fail(MOE_ERR_INVALID_ARG, "an event is null");
-    return forward_impl(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out, topk_ids,
-                        topk_gates, expert_counts, workspace, workspace_bytes, stream, stream_shared, events);
+    Request q = plain_request(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out, topk_ids,
+                              topk_gates, expert_counts, workspace, workspace_bytes, stream, stream_shared);
+    q.events = events;
+    return forward_impl(q);
 }
 
 } // extern "C"

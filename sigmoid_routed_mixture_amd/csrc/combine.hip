@@ -1,8 +1,10 @@
-// Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t], in fp32 with
-// the k slots added in slot order, then the shared expert. The per-slot expert outputs y are fp32 rows.
+// Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t] (+ x'[t]), in
+// fp32 with the k slots added in slot order, then the shared expert, then (block entry point) the residual
+// stream. The per-slot expert outputs y are fp32 rows.
 // One workgroup per token; each thread owns 8-column chunks (16-byte loads and stores).
 // Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (y_routed = sum_i G_i E_i,
-// delta_ffn = y_routed + y_shared); nnterp encyclopedia glm_moe_dsa, "The mixture" (routed + shared == out).
+// delta_ffn = y_routed + y_shared, x_{n+1} = x'_n + delta_ffn); nnterp encyclopedia glm_moe_dsa, "The
+// mixture" (routed + shared == out).
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -12,7 +14,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_row,
-                                                      const float* __restrict__ y_shared, int T, int H, int k,
+                                                      const float* __restrict__ y_shared,
+                                                      const uint16_t* __restrict__ resid, int T, int H, int k,
                                                       float* __restrict__ out) {
     __shared__ float g[kMaxK];
     __shared__ int rr[kMaxK];
@@ -43,6 +46,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             acc[0] += s0.x; acc[1] += s0.y; acc[2] += s0.z; acc[3] += s0.w;
             acc[4] += s1.x; acc[5] += s1.y; acc[6] += s1.z; acc[7] += s1.w;
         }
+        if (resid) {
+            const Pack16 r = load16(resid + (size_t)t * H + c * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += bf16_to_f32((uint16_t)(r.w[i] & 0xFFFFu));
+                acc[2 * i + 1] += bf16_to_f32((uint16_t)(r.w[i] >> 16));
+            }
+        }
         *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
@@ -51,9 +62,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 } // namespace
 
 hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          int T, int H, int k, float* out, hipStream_t stream) {
+                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    combine_kernel<<<T, 256, 0, stream>>>(y, gates, slot_row, y_shared, T, H, k, out);
+    combine_kernel<<<T, 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out);
     return hipGetLastError();
 }
 

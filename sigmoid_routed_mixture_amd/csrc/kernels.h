@@ -43,9 +43,14 @@ struct GemmArgs {
 enum class GemmKind { GateUp, Down, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
 
-// out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]), fp32, slot order.
+// out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
+// residual (bf16) added last.
 hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          int T, int H, int k, float* out, hipStream_t stream);
+                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream);
+
+// out[t] = bf16(gamma * x[t] / sqrt(mean(x[t]^2) + eps)), computed in fp64.
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps, int T, int H, uint16_t* out,
+                          hipStream_t stream);
 
 // Fills n ints with v.
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);

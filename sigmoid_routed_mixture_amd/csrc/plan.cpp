@@ -51,7 +51,7 @@ int64_t max_tiles(int T, int E, int k, int BM) {
     return (slots + BM - 1) / BM + std::min<int64_t>(E, slots);
 }
 
-Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
+Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm) {
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -76,9 +76,22 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is) {
     L.y_perm = take(Tk * (size_t)H * 4);
     L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
     L.y_sh = Is > 0 ? take((size_t)T * (size_t)H * 4) : size_t(-1);
+    L.x_norm = with_norm ? take((size_t)T * (size_t)H * 2) : size_t(-1);
     L.total = off;
     return L;
 }
+
+Check check_dense_sizes(int T, int H, int Id) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (H <= 0) return fail(MOE_ERR_INVALID_ARG, "H <= 0");
+    if (Id <= 0) return fail(MOE_ERR_INVALID_ARG, "I <= 0");
+    if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "H is not a multiple of 64");
+    if (Id % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I is not a multiple of 64");
+    if ((int64_t)T >= (int64_t(1) << 31) / 16) return fail(MOE_ERR_UNSUPPORTED, "T >= 2^27");
+    return Check{};
+}
+
+size_t dense_workspace_bytes(int T, int Id) { return align_up(std::max<size_t>((size_t)T * (size_t)Id * 2, 1), 256); }
 
 size_t permute_scratch_bytes(int T, int E) {
     const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;

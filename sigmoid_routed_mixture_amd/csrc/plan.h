@@ -61,10 +61,15 @@ constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
     size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,
-        y_perm, h_sh, y_sh;
+        y_perm, h_sh, y_sh, x_norm;
     size_t total;
 };
-Layout forward_layout(int T, int H, int E, int k, int I, int Is);
+// with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.
+Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm = false);
 size_t permute_scratch_bytes(int T, int E);
+
+// Dense SwiGLU MLP: T >= 0, H and Id positive multiples of 64. Its workspace is h [T, Id] bf16.
+Check check_dense_sizes(int T, int H, int Id);
+size_t dense_workspace_bytes(int T, int Id);
 
 } // namespace moe

@@ -112,3 +112,60 @@ def config_host(cfg: wl.MoEConfig, weights: dict | None = None) -> dict:
         weights = {n: wl.weight(cfg, n) for n in ("w1", "w3", "w2", "ws1", "ws3", "ws2")}
     h.update(weights)
     return h
+
+
+# ---------------------------------------------------------------------------------------------------
+# workload cache shared by the GPU test modules (one host and one device copy of each layer's weights)
+
+WEIGHT_NAMES = ("w1", "w3", "w2", "ws1", "ws3", "ws2")
+_CACHE = {}
+
+
+def layer_weights(cfg: wl.MoEConfig):
+    key = ("weights", cfg.weight_seed, cfg.E, cfg.H, cfg.I, cfg.Is)
+    if key not in _CACHE:
+        gb = (3 * cfg.E * cfg.H * cfg.I + 3 * cfg.H * cfg.Is) * 2 / 1e9
+        say("generating the expert weights of %s (%.1f GB) on host and device" % (cfg.name, gb))
+        host = {n: wl.weight(cfg, n) for n in WEIGHT_NAMES}
+        _CACHE[key] = (host, to_device(host))
+    return _CACHE[key]
+
+
+def case(name):
+    """(cfg, host inputs, device inputs) of a mixture workload."""
+    if name not in _CACHE:
+        cfg = wl.BY_NAME[name]
+        wh, wd = layer_weights(cfg)
+        h = config_host(cfg, wh)
+        d = to_device({"x": h["x"], "wr": h["wr"], "b": h["b"]})
+        d.update(wd)
+        _CACHE[name] = (cfg, h, d)
+    return _CACHE[name]
+
+
+def route_ref(name):
+    key = ("route", name)
+    if key not in _CACHE:
+        cfg, h, _ = case(name)
+        say("oracle routing of %s (T=%d) on host threads" % (name, cfg.T))
+        _CACHE[key] = oracle_route_all(h, cfg.k, cfg.scale)
+    return _CACHE[key]
+
+
+def dense_case(name):
+    """(cfg, host inputs, device inputs) of a dense-MLP workload."""
+    key = ("dense", name)
+    if key not in _CACHE:
+        cfg = wl.DENSE_BY_NAME[name]
+        wkey = ("dense_weights", cfg.weight_seed, cfg.H, cfg.Id)
+        if wkey not in _CACHE:
+            say("generating the dense MLP weights of %s (%.2f GB)" % (name, 3 * cfg.H * cfg.Id * 2 / 1e9))
+            host = {n: wl.dense_weight(cfg, n) for n in ("w1", "w3", "w2")}
+            _CACHE[wkey] = (host, to_device(host))
+        wh, wd = _CACHE[wkey]
+        h = dict(wh)
+        h["x"] = wl.dense_tokens(cfg)
+        d = dict(wd)
+        d["x"] = dev_bf16(h["x"])
+        _CACHE[key] = (cfg, h, d)
+    return _CACHE[key]

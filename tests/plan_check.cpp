@@ -36,7 +36,10 @@ int main() {
                         for (int Is : {0, I}) {
                             if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) continue;
                             ++n;
-                            const moe::Layout L = moe::forward_layout(T, H, E, k, I, Is);
+                            const moe::Layout L = moe::forward_layout(T, H, E, k, I, Is, true);
+                            const moe::Layout L0 = moe::forward_layout(T, H, E, k, I, Is);
+                            CHECK(L0.y_perm == L.y_perm && L0.x_norm == size_t(-1) && L0.total <= L.x_norm,
+                                  "the norm region must only extend the plain layout");
                             const size_t Tk = (size_t)T * k;
                             const size_t chunks = ((size_t)T + moe::kPermChunk - 1) / moe::kPermChunk;
                             const size_t tiles_need = (size_t)std::max(moe::max_tiles(T, E, k, moe::kSkinnyBM),
@@ -53,6 +56,7 @@ int main() {
                                 rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
                                 rs.push_back({L.y_sh, (size_t)T * H * 4, "y_sh"});
                             }
+                            rs.push_back({L.x_norm, (size_t)T * H * 2, "x_norm"});
                             for (size_t i = 0; i < rs.size(); ++i) {
                                 const size_t end = i + 1 < rs.size() ? rs[i + 1].off : L.total;
                                 CHECK(rs[i].off % 256 == 0, "%s offset %zu", rs[i].name, rs[i].off);

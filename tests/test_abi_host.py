@@ -57,6 +57,14 @@ def lib():
     L.moe_forward.argtypes = [p] * 9 + [i] * 6 + [f] + [p] * 5 + [sz, p, p]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.restype = ctypes.c_char_p
+    d = ctypes.c_double
+    L.moe_forward_routed.argtypes = [p] * 9 + [i] * 6 + [p, p, p, sz, p, p]
+    L.moe_block_workspace_bytes.argtypes = [i] * 6
+    L.moe_block_workspace_bytes.restype = sz
+    L.moe_block_forward.argtypes = [p, p, d] + [p] * 8 + [i] * 6 + [f] + [p] * 6 + [sz, p, p]
+    L.moe_dense_mlp_workspace_bytes.argtypes = [i] * 3
+    L.moe_dense_mlp_workspace_bytes.restype = sz
+    L.moe_dense_mlp.argtypes = [p] * 4 + [i] * 3 + [p, p, sz, p]
     return L
 
 
@@ -128,3 +136,67 @@ def test_permute_argument_checks(lib):
     assert L.moe_permute(None, A, 64, 256, 16, 4, A, A, A, A, A, ws, nb, None) == INVALID  # x_perm needs x
     assert L.moe_permute(None, A, 64, 256, 16, 4, A, A, A, A, None, ws, 4, None) == WORKSPACE
     assert L.moe_permute(None, A, 64, 256, 16, 4, A, A, A, A, None, ws + 64, nb, None) == MISALIGNED
+
+
+def routed(L, T=64, H=256, E=16, k=4, I=128, Is=128, ws_bytes=None, **ptrs):
+    P = dict(x=A, ids=A, gates=A, w1=A, w3=A, w2=A, ws1=A, ws3=A, ws2=A, out=A, counts=None, ws=0x100000)
+    P.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = L.moe_workspace_bytes(max(T, 0), H, E, k, I, Is)
+    return L.moe_forward_routed(P["x"], P["ids"], P["gates"], P["w1"], P["w3"], P["w2"], P["ws1"], P["ws3"],
+                                P["ws2"], T, H, E, k, I, Is, P["out"], P["counts"], P["ws"], ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ids=None), INVALID), (dict(gates=None), INVALID), (dict(x=None), INVALID), (dict(w3=None), INVALID),
+    (dict(gates=A + 4), MISALIGNED), (dict(I=96), UNSUPPORTED), (dict(ws_bytes=4096), WORKSPACE),
+    (dict(T=0), OK), (dict(T=0, ids=None, gates=None), OK), (dict(k=17), INVALID),
+])
+def test_forward_routed_argument_checks(lib, kw, status):
+    assert routed(lib, **kw) == status
+
+
+def block(L, T=64, H=256, E=16, k=4, I=128, Is=128, eps=1e-5, ws_bytes=None, **ptrs):
+    P = dict(resid=A, gamma=A, wr=A, b=A, w1=A, w3=A, w2=A, ws1=A, ws3=A, ws2=A, out=A, xn=None, ids=None,
+             gates=None, counts=None, ws=0x100000)
+    P.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = L.moe_block_workspace_bytes(max(T, 0), H, E, k, I, Is)
+    return L.moe_block_forward(P["resid"], P["gamma"], eps, P["wr"], P["b"], P["w1"], P["w3"], P["w2"], P["ws1"],
+                               P["ws3"], P["ws2"], T, H, E, k, I, Is, 2.5, P["out"], P["xn"], P["ids"], P["gates"],
+                               P["counts"], P["ws"], ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(resid=None), INVALID), (dict(gamma=None), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID), (dict(xn=A + 2), MISALIGNED),
+    (dict(wr=None), INVALID), (dict(H=100), UNSUPPORTED), (dict(T=0), OK), (dict(T=0, eps=-1.0), INVALID),
+])
+def test_block_forward_argument_checks(lib, kw, status):
+    assert block(lib, **kw) == status
+
+
+def test_block_workspace_holds_the_normalised_stream(lib):
+    for T, H, E, k, I, Is in ((64, 256, 16, 4, 128, 128), (8192, 6144, 256, 8, 2048, 2048)):
+        plain = lib.moe_workspace_bytes(T, H, E, k, I, Is)
+        assert lib.moe_block_workspace_bytes(T, H, E, k, I, Is) >= plain + T * H * 2
+        # the plain workspace is too small for the block entry point
+        assert block(lib, T=T, H=H, E=E, k=k, I=I, Is=Is, ws_bytes=plain) == WORKSPACE
+
+
+def test_dense_mlp_argument_checks(lib):
+    L = lib
+    ws = 0x100000
+    nb = L.moe_dense_mlp_workspace_bytes(64, 256, 384)
+    assert nb >= 64 * 384 * 2
+    assert L.moe_dense_mlp_workspace_bytes(64, 250, 384) == 0
+    assert L.moe_dense_mlp_workspace_bytes(64, 256, 100) == 0
+    assert L.moe_dense_mlp(None, A, A, A, 64, 256, 384, A, ws, nb, None) == INVALID
+    assert L.moe_dense_mlp(A, A, None, A, 64, 256, 384, A, ws, nb, None) == INVALID
+    assert L.moe_dense_mlp(A, A, A, A, 64, 256, 384, None, ws, nb, None) == INVALID
+    assert L.moe_dense_mlp(A, A, A, A, 64, 256, 384, A, ws, 16, None) == WORKSPACE
+    assert L.moe_dense_mlp(A, A, A, A, 64, 256, 384, A, ws + 16, nb, None) == MISALIGNED
+    assert L.moe_dense_mlp(A + 2, A, A, A, 64, 256, 384, A, ws, nb, None) == MISALIGNED
+    assert L.moe_dense_mlp(A, A, A, A, -1, 256, 384, A, ws, nb, None) == INVALID
+    assert L.moe_dense_mlp(A, A, A, A, 64, 256, 96, A, ws, nb, None) == UNSUPPORTED
+    assert L.moe_dense_mlp(None, None, None, None, 0, 256, 384, None, None, 0, None) == OK

@@ -14,53 +14,16 @@ import torch
 
 import oracle
 import workloads as wl
-from parity import (NEAR_TIE, compare_out, compare_routing, config_host, dev, dev_bf16, oracle_forward_rows,
-                    oracle_route_all, sample_rows, say, to_device)
+from parity import (NEAR_TIE, case, compare_out, compare_routing, config_host, dev, dev_bf16,
+                    oracle_forward_rows, oracle_route_all, route_ref, sample_rows, say, to_device)
 
 pytestmark = pytest.mark.gpu
-
-WEIGHT_NAMES = ("w1", "w3", "w2", "ws1", "ws3", "ws2")
-_CACHE = {}
-
 
 @pytest.fixture(scope="module")
 def moe():
     import sigmoid_routed_mixture_amd as m
 
     return m
-
-
-def glm5_weights():
-    if "glm5" not in _CACHE:
-        cfg = wl.BY_NAME["glm5_decode"]
-        say("generating GLM-5 expert weights (19.3 GB of routed experts) on host and device")
-        host = {n: wl.weight(cfg, n) for n in WEIGHT_NAMES}
-        _CACHE["glm5"] = (host, to_device(host))
-    return _CACHE["glm5"]
-
-
-def case(name):
-    if name not in _CACHE:
-        cfg = wl.BY_NAME[name]
-        if cfg.H == 6144:
-            wh, wd = glm5_weights()
-            h = config_host(cfg, wh)
-            d = to_device({"x": h["x"], "wr": h["wr"], "b": h["b"]})
-            d.update(wd)
-        else:
-            h = config_host(cfg)
-            d = to_device(h)
-        _CACHE[name] = (cfg, h, d)
-    return _CACHE[name]
-
-
-def route_ref(name):
-    key = ("route", name)
-    if key not in _CACHE:
-        cfg, h, _ = case(name)
-        say("oracle routing of %s (T=%d) on host threads" % (name, cfg.T))
-        _CACHE[key] = oracle_route_all(h, cfg.k, cfg.scale)
-    return _CACHE[key]
 
 
 def run_forward(m, cfg, d, stream_shared=None, T=None):
