@@ -75,11 +75,12 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
     return MOE_OK;
 }
 
-// Test knob: MOE_GEMM_PATH=wide|skinny forces one grouped-GEMM kernel for every size (both are exact
+// Test knob: MOE_GEMM_PATH=wide|tall|skinny forces one grouped-GEMM kernel for every size (all are exact
 // implementations of the same GEMMs; the default picks by rows per expert).
 moe::GemmPath pick_path(int T, int E, int k) {
     const char* f = std::getenv("MOE_GEMM_PATH");
     if (f && std::strcmp(f, "wide") == 0) return moe::GemmPath::Wide;
+    if (f && std::strcmp(f, "tall") == 0) return moe::GemmPath::Tall;
     if (f && std::strcmp(f, "skinny") == 0) return moe::GemmPath::Skinny;
     return moe::gemm_path(T, E, k);
 }
@@ -189,8 +190,7 @@ moe_status forward_impl(const Request& q) {
     if (two_streams) MOE_TRY(device_events(&ev));
 
     const moe::GemmPath path = pick_path(T, E, k);
-    const bool wide = path == moe::GemmPath::Wide;
-    const int BM = wide ? moe::kWideBM : moe::kSkinnyBM;
+    const int BM = moe::path_bm(path);
 
     auto mark = [&](int i) -> moe_status {
         if (q.events == nullptr) return MOE_OK;
@@ -229,7 +229,7 @@ moe_status forward_impl(const Request& q) {
         g1.N = Is;
         g1.K = H;
         const int64_t dense_tiles = ((int64_t)T + BM - 1) / BM;
-        MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, g1, dense_tiles, ss), "shared gate/up GEMM");
+        MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, dense_tiles, ss), "shared gate/up GEMM");
         moe::GemmArgs g2{};
         g2.act = h_sh;
         g2.w_a = q.ws2;
@@ -237,7 +237,7 @@ moe_status forward_impl(const Request& q) {
         g2.dense_rows = T;
         g2.N = H;
         g2.K = Is;
-        MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, g2, dense_tiles, ss), "shared down GEMM");
+        MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, dense_tiles, ss), "shared down GEMM");
     }
     MOE_TRY(mark(3));
 
@@ -255,7 +255,7 @@ moe_status forward_impl(const Request& q) {
     r1.groups = E;
     r1.N = I;
     r1.K = H;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, r1, grid_tiles, s0), "routed gate/up GEMM");
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
     r2.act = h_perm;
@@ -268,7 +268,7 @@ moe_status forward_impl(const Request& q) {
     r2.groups = E;
     r2.N = H;
     r2.K = I;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, r2, grid_tiles, s0), "routed down GEMM");
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
@@ -453,8 +453,8 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     if (workspace_bytes < moe::dense_workspace_bytes(T, I))
         return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dense_mlp_workspace_bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool wide = pick_path(T, 1, 1) == moe::GemmPath::Wide;
-    const int BM = wide ? moe::kWideBM : moe::kSkinnyBM;
+    const moe::GemmPath path = pick_path(T, 1, 1);
+    const int BM = moe::path_bm(path);
     const int64_t tiles = ((int64_t)T + BM - 1) / BM;
     moe::GemmArgs g1{};
     g1.act = x;
@@ -464,7 +464,7 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     g1.dense_rows = T;
     g1.N = I;
     g1.K = H;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, wide, g1, tiles, s), "dense gate/up GEMM");
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), "dense gate/up GEMM");
     moe::GemmArgs g2{};
     g2.act = static_cast<const uint16_t*>(workspace);
     g2.w_a = w2;
@@ -472,7 +472,7 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     g2.dense_rows = T;
     g2.N = H;
     g2.K = I;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, wide, g2, tiles, s), "dense down GEMM");
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, tiles, s), "dense down GEMM");
     return MOE_OK;
 }
 

@@ -10,9 +10,9 @@
 // four accumulator elements are four consecutive output features of one token row: 8-byte bf16 stores.
 //
 // Two kernels:
-//  * wide   : 128 tokens x 256 weight rows per 8-wave workgroup. Each wave streams its own 32 weight
-//             rows from HBM into MFMA registers; the token tile goes through double-buffered LDS. It
-//             also computes the router logits (dense, K split across workgroups).
+//  * wide   : 128 or 256 tokens x 256 weight rows per 8-wave workgroup. Each wave streams its own 32
+//             weight rows from HBM into MFMA registers; the token tile goes through double-buffered LDS.
+//             The 128-token form also computes the router logits (dense, K split across workgroups).
 //  * skinny : 16 tokens per tile for experts with few rows (decode). No LDS: each wave streams its own
 //             weight rows straight from HBM with 32-byte loads per lane, two 64-wide K chunks in flight
 //             ahead of its MFMAs, so the kernel runs at the weight-streaming bound.
@@ -80,14 +80,24 @@ __device__ __forceinline__ const uint16_t* act_row(const GemmArgs& a, const Tile
 // ------------------------------------------------------------------------------------------------
 // wide kernel
 
-constexpr int kWBM = kWideBM;        // tokens per tile: 8 MFMA column blocks of 16
 constexpr int kWaves = 8;            // waves per workgroup (two per SIMD)
 constexpr int kWaveRows = 32;        // weight rows per wave: 2 MFMA row blocks of 16
 constexpr int kWBN = kWaves * kWaveRows;  // weight rows per workgroup
 constexpr int kWThreads = 64 * kWaves;
-static_assert(kWBM == 128, "wide tiling assumes 128 tokens");
 
-// LDS token tile: [128 rows][64 k] bf16 (128 B per row); 16-byte chunk c of row r lives at chunk
+// Tile heights: 128 tokens (8 MFMA column blocks) or 256 (16). The taller tile loads a third fewer bytes
+// per FLOP through the L1, which bounds this kernel (each CU keeps about 64 cache-line misses in flight
+// at ~450 cycles of L2 latency); it holds one K step of token loads in registers instead of two to stay
+// within 256 registers, and reads token fragments in groups of four blocks.
+template <int BM>
+struct WideShape {
+    static_assert(BM == kWideBM || BM == kTallBM, "wide tiling assumes 128 or 256 tokens");
+    static constexpr int XQ = BM / 64;               // token-row loads per thread per K step
+    static constexpr int XS = BM == kWideBM ? 2 : 1; // token register stages (loads XS steps ahead)
+    static constexpr int G = BM == kWideBM ? 8 : 4;  // token blocks per fragment group
+};
+
+// LDS token tile: [BM rows][64 k] bf16 (128 B per row); 16-byte chunk c of row r lives at chunk
 // c ^ (r & 7) ^ ((r >> 3) & 1). An MFMA fragment read is 16 lanes on rows r..r+15 (r a multiple of 16) at
 // one chunk: the permutation gives every 8 consecutive rows distinct chunks, and even rows (and odd
 // rows) distinct chunks, so the 16 lanes cover all 64 four-byte banks and each 8-lane half all 32 of a
@@ -96,23 +106,25 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kBK + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
 }
 
-// One 128-token x 256-weight-row tile. Each of the 8 waves streams its own 32 weight rows from HBM
+// One BM-token x 256-weight-row tile. Each of the 8 waves streams its own 32 weight rows from HBM
 // straight into MFMA A-operand registers (a weight row is used by one wave only, so it never touches
-// LDS); the 128 token rows, shared by all waves, are staged through double-buffered LDS. Per 64-wide K
+// LDS); the BM token rows, shared by all waves, are staged through double-buffered LDS. Per 64-wide K
 // step a lane loads 32 contiguous bytes of each of its 2 weight rows (k-group g = lane / 16 covers
 // k 16 g .. 16 g + 15); MFMA h in {0, 1} takes the h-th 8 of them and token chunk 2 g + h from LDS.
 // With 8 waves the register budget allows two waves per SIMD, so one wave's memory waits are covered by
 // the other's MFMAs.
 // Pipeline: step s computes on weights W(s) (register set s % 3) and tokens X(s) (LDS buffer s % 2). It
-// first issues the token loads of X(s + 2) (register set s % 2, free since X(s) went to LDS) and the
-// weight loads of W(s + 2); at its end it stores X(s + 1) (loaded during step s - 1) into LDS buffer
-// (s + 1) % 2, whose last reader was step s - 1, and a barrier publishes it. Loads past the end re-read
-// the last chunk (in bounds, unused); the scheduling barrier keeps each step's loads ahead of its MFMAs.
-// Only NB of the 8 token blocks (the ones holding valid rows, rounded to 1, 2, 4 or 8) are computed.
-template <GemmKind KIND, bool DENSE, int NB>
+// first issues the token loads of X(s + XS) and the weight loads of W(s + 2) (into registers whose last
+// use is over); at its end it stores X(s + 1) into LDS buffer (s + 1) % 2, whose last reader was step
+// s - 1, and a barrier publishes it. Loads past the end re-read the last chunk (in bounds, unused); the
+// scheduling barrier keeps each step's loads ahead of its MFMAs.
+// Only NB of the token blocks (the ones holding valid rows, rounded up to a compiled count) are computed.
+template <GemmKind KIND, bool DENSE, int BM, int NB>
 __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti, int split, int col0,
-                                          const uint16_t* const (&wsrc)[2], const uint16_t* const (&xsrc)[2],
-                                          int kbeg, int kend, uint16_t* xs0, uint16_t* xs1) {
+                                          const uint16_t* const (&wsrc)[2],
+                                          const uint16_t* const (&xsrc)[WideShape<BM>::XQ], int kbeg, int kend,
+                                          uint16_t* xs0, uint16_t* xs1) {
+    constexpr int XQ = WideShape<BM>::XQ, XS = WideShape<BM>::XS, G = WideShape<BM>::G;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int rl = lane & 15, kg = lane >> 4;
@@ -126,9 +138,11 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     typedef Pack16 WSet[2][2];
-    typedef Pack16 XSet[2];
+    typedef Pack16 XSet[XQ];
     WSet w0, w1, w2;
-    XSet x0, x1;
+    XSet xa, xb;
+    XSet& xA = xa;
+    XSet& xB = XS == 2 ? xb : xa; // with one stage the load and store sets are the same registers
     auto wload = [&](WSet& w, int kk) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -138,28 +152,38 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
     };
     auto xload = [&](XSet& x, int kk) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) x[i] = load16(xsrc[i] + kk);
+        for (int q = 0; q < XQ; ++q) x[q] = load16(xsrc[q] + kk);
     };
     auto xstore = [&](const XSet& x, uint16_t* buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) store16(&buf[lds_off((tid >> 3) + 64 * i, lc)], x[i]);
+        for (int q = 0; q < XQ; ++q) store16(&buf[lds_off((tid >> 3) + 64 * q, lc)], x[q]);
     };
-    // Token fragments: all of the first half are read up front; each second-half fragment is read into
-    // the register its first-half twin frees, right after that twin's MFMAs issue.
-    auto compute = [&](const WSet& w, const uint16_t* xb) {
-        Pack16 bfr[NB];
+    // Token fragments, G blocks at a time: the group's first-half fragments are read up front; each
+    // second-half fragment is read into the register its first-half twin frees, right after that twin's
+    // MFMAs issue.
+    auto compute = [&](const WSet& w, const uint16_t* xb_lds) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bfr[j] = load16(&xb[lds_off(j * 16 + rl, 2 * kg)]);
+        for (int c0 = 0; c0 < NB; c0 += G) {
+            Pack16 bfr[G];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+            for (int jj = 0; jj < G; ++jj)
+                if (c0 + jj < NB) bfr[jj] = load16(&xb_lds[lds_off((c0 + jj) * 16 + rl, 2 * kg)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(w[i][0], bfr[j], acc[i][j]);
-            bfr[j] = load16(&xb[lds_off(j * 16 + rl, 2 * kg + 1)]);
+            for (int jj = 0; jj < G; ++jj)
+                if (c0 + jj < NB) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][c0 + jj] = mfma16x16x32(w[i][0], bfr[jj], acc[i][c0 + jj]);
+                    bfr[jj] = load16(&xb_lds[lds_off((c0 + jj) * 16 + rl, 2 * kg + 1)]);
+                }
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj)
+                if (c0 + jj < NB) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][c0 + jj] = mfma16x16x32(w[i][1], bfr[jj], acc[i][c0 + jj]);
+                }
         }
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(w[i][1], bfr[j], acc[i][j]);
     };
 
     const int nk = (kend - kbeg) / kBK;
@@ -167,34 +191,35 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
     auto kat = [&](int st) { const int k = kbeg + st * kBK; return k < klast ? k : klast; };
     auto step = [&](const WSet& wcur, WSet& wfut, XSet& xfut, const XSet& xnext, const uint16_t* bcur,
                     uint16_t* bnext, int st) {
-        xload(xfut, kat(st + 2));
+        xload(xfut, kat(st + XS));
         wload(wfut, kat(st + 2));
         __builtin_amdgcn_sched_barrier(0);
         compute(wcur, bcur);
         xstore(xnext, bnext);
         __syncthreads();
     };
-    xload(x0, kat(0));
+    xload(xA, kat(0));
     wload(w0, kat(0));
-    xload(x1, kat(1));
+    if (XS == 2) xload(xB, kat(1));
     wload(w1, kat(1));
-    xstore(x0, xs0);
+    xstore(xA, xs0);
     __syncthreads();
-    // six steps per iteration: the token registers cycle with period 2, the weights with period 3
+    // six steps per iteration: the weight registers cycle with period 3, the token sets and LDS buffers
+    // with period 2
     int s = 0;
     for (; s + 6 <= nk; s += 6) {
-        step(w0, w2, x0, x1, xs0, xs1, s);
-        step(w1, w0, x1, x0, xs1, xs0, s + 1);
-        step(w2, w1, x0, x1, xs0, xs1, s + 2);
-        step(w0, w2, x1, x0, xs1, xs0, s + 3);
-        step(w1, w0, x0, x1, xs0, xs1, s + 4);
-        step(w2, w1, x1, x0, xs1, xs0, s + 5);
+        step(w0, w2, xA, xB, xs0, xs1, s);
+        step(w1, w0, xB, xA, xs1, xs0, s + 1);
+        step(w2, w1, xA, xB, xs0, xs1, s + 2);
+        step(w0, w2, xB, xA, xs1, xs0, s + 3);
+        step(w1, w0, xA, xB, xs0, xs1, s + 4);
+        step(w2, w1, xB, xA, xs1, xs0, s + 5);
     }
-    if (s < nk) step(w0, w2, x0, x1, xs0, xs1, s);
-    if (s + 1 < nk) step(w1, w0, x1, x0, xs1, xs0, s + 1);
-    if (s + 2 < nk) step(w2, w1, x0, x1, xs0, xs1, s + 2);
-    if (s + 3 < nk) step(w0, w2, x1, x0, xs1, xs0, s + 3);
-    if (s + 4 < nk) step(w1, w0, x0, x1, xs0, xs1, s + 4);
+    if (s < nk) step(w0, w2, xA, xB, xs0, xs1, s);
+    if (s + 1 < nk) step(w1, w0, xB, xA, xs1, xs0, s + 1);
+    if (s + 2 < nk) step(w2, w1, xA, xB, xs0, xs1, s + 2);
+    if (s + 3 < nk) step(w0, w2, xB, xA, xs1, xs0, s + 3);
+    if (s + 4 < nk) step(w1, w0, xA, xB, xs0, xs1, s + 4);
     if (col0 >= N) return; // a wave past the last output column computed on clamped rows: nothing to store
 
     // epilogue: lane holds features 4 kg + r of weight block i and token rl of token block j
@@ -236,8 +261,9 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
     }
 }
 
-template <GemmKind KIND, bool DENSE>
+template <GemmKind KIND, bool DENSE, int BM>
 __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int ntn, int64_t tiles_per_split) {
+    constexpr int XQ = WideShape<BM>::XQ;
     int64_t bid = blockIdx.x;
     int split = 0;
     if (KIND == GemmKind::Logits) {
@@ -249,14 +275,14 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
     if (DENSE) {
         ntile = (int)(bid % ntn);
         mtile = bid / ntn;
-    } else if (!grouped_block<kWBM>(a, ntn, bid, mtile, ntile)) {
+    } else if (!grouped_block<BM>(a, ntn, bid, mtile, ntile)) {
         return;
     }
     TileInfo ti;
-    if (!tile_info<DENSE, kWBM>(a, mtile, ti)) return;
+    if (!tile_info<DENSE, BM>(a, mtile, ti)) return;
 
-    __shared__ __attribute__((aligned(16))) uint16_t xs0[kWBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t xs1[kWBM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[BM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[BM * kBK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -291,19 +317,34 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
         }
     }
     const int lc = tid & 7;
-    const uint16_t* xsrc[2];
+    const uint16_t* xsrc[XQ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xsrc[i] = act_row<KIND, DENSE>(a, ti, (tid >> 3) + 64 * i) + lc * 8;
+    for (int q = 0; q < XQ; ++q) xsrc[q] = act_row<KIND, DENSE>(a, ti, (tid >> 3) + 64 * q) + lc * 8;
 
     const int nbj = (ti.rows + 15) >> 4;
-    if (nbj > 4)
-        wide_tile<KIND, DENSE, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-    else if (nbj > 2)
-        wide_tile<KIND, DENSE, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-    else if (nbj > 1)
-        wide_tile<KIND, DENSE, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-    else
-        wide_tile<KIND, DENSE, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    if constexpr (BM == kTallBM) {
+        if (nbj > 12)
+            wide_tile<KIND, DENSE, BM, 16>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 8)
+            wide_tile<KIND, DENSE, BM, 12>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 4)
+            wide_tile<KIND, DENSE, BM, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 2)
+            wide_tile<KIND, DENSE, BM, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 1)
+            wide_tile<KIND, DENSE, BM, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else
+            wide_tile<KIND, DENSE, BM, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    } else {
+        if (nbj > 4)
+            wide_tile<KIND, DENSE, BM, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 2)
+            wide_tile<KIND, DENSE, BM, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 1)
+            wide_tile<KIND, DENSE, BM, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else
+            wide_tile<KIND, DENSE, BM, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -414,7 +455,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
 }
 
 template <GemmKind KIND, bool DENSE>
-hipError_t launch_one(bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
+hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
+    const bool wide = path != GemmPath::Skinny;
     int ntn;
     if (wide)
         ntn = KIND == GemmKind::GateUp ? (a.N + kWBN / 2 - 1) / (kWBN / 2) : (a.N + kWBN - 1) / kWBN;
@@ -425,31 +467,37 @@ hipError_t launch_one(bool wide, const GemmArgs& a, int64_t grid_tiles, hipStrea
     if (blocks <= 0) return hipSuccess;
     if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (blocks > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
-    if (wide)
-        gemm_wide_kernel<KIND, DENSE><<<dim3((unsigned)blocks), kWThreads, 0, stream>>>(a, ntn, grid_tiles);
-    else if (KIND != GemmKind::Logits)
-        gemm_skinny_kernel<KIND, DENSE><<<dim3((unsigned)blocks), 256, 0, stream>>>(a, ntn);
-    else
-        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
+    if constexpr (KIND == GemmKind::Logits) {
+        if (path != GemmPath::Wide) return hipErrorInvalidValue;
+        gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
+    } else {
+        if (path == GemmPath::Wide)
+            gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
+        else if (path == GemmPath::Tall)
+            gemm_wide_kernel<KIND, DENSE, kTallBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
+        else
+            gemm_skinny_kernel<KIND, DENSE><<<grid, 256, 0, stream>>>(a, ntn);
+    }
     return hipGetLastError();
 }
 
 } // namespace
 
-hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
+hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     const bool dense = a.counts == nullptr;
     switch (kind) {
     case GemmKind::GateUp:
-        return dense ? launch_one<GemmKind::GateUp, true>(wide, a, grid_tiles, stream)
-                     : launch_one<GemmKind::GateUp, false>(wide, a, grid_tiles, stream);
+        return dense ? launch_one<GemmKind::GateUp, true>(path, a, grid_tiles, stream)
+                     : launch_one<GemmKind::GateUp, false>(path, a, grid_tiles, stream);
     case GemmKind::Down:
-        return dense ? launch_one<GemmKind::Down, true>(wide, a, grid_tiles, stream)
-                     : launch_one<GemmKind::Down, false>(wide, a, grid_tiles, stream);
+        return dense ? launch_one<GemmKind::Down, true>(path, a, grid_tiles, stream)
+                     : launch_one<GemmKind::Down, false>(path, a, grid_tiles, stream);
     case GemmKind::DownF32:
-        return dense ? launch_one<GemmKind::DownF32, true>(wide, a, grid_tiles, stream)
-                     : launch_one<GemmKind::DownF32, false>(wide, a, grid_tiles, stream);
+        return dense ? launch_one<GemmKind::DownF32, true>(path, a, grid_tiles, stream)
+                     : launch_one<GemmKind::DownF32, false>(path, a, grid_tiles, stream);
     case GemmKind::Logits:
-        return dense ? launch_one<GemmKind::Logits, true>(true, a, grid_tiles, stream) : hipErrorInvalidValue;
+        return dense ? launch_one<GemmKind::Logits, true>(path, a, grid_tiles, stream) : hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace moe {
 
 // Router: logits, sigmoid, biased top-k, gates. With `partial` ([S, T, E] fp32 scratch) the logits run
@@ -41,7 +43,7 @@ struct GemmArgs {
     int ksplit;                // logits only: K ranges, each writing its own [dense_rows, N] fp32 partial
 };
 enum class GemmKind { GateUp, Down, DownF32, Logits };
-hipError_t launch_gemm(GemmKind kind, bool wide, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
+hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
 // residual (bf16) added last.

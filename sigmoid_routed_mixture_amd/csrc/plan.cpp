@@ -43,7 +43,9 @@ int router_splits(int T, int H) {
 }
 
 GemmPath gemm_path(int T, int E, int k) {
-    return (int64_t)T * k <= (int64_t)kSkinnyBM * E ? GemmPath::Skinny : GemmPath::Wide;
+    const int64_t slots = (int64_t)T * k;
+    if (slots <= (int64_t)kSkinnyBM * E) return GemmPath::Skinny;
+    return slots < (int64_t)192 * E ? GemmPath::Wide : GemmPath::Tall;
 }
 
 int64_t max_tiles(int T, int E, int k, int BM) {
@@ -69,7 +71,7 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     L.slot_row = take(Tk * 4);
     L.chunk_base = take(chunks * (size_t)E * 4);
     // room for the longest tile list either grouped-GEMM kernel can ask for (the smallest BM)
-    L.tiles = take((size_t)max_tiles(T, E, k, std::min(kWideBM, kSkinnyBM)) * 8);
+    L.tiles = take((size_t)max_tiles(T, E, k, std::min(std::min(kWideBM, kTallBM), kSkinnyBM)) * 8);
     L.ntiles = take(4);
     L.partial = take((size_t)router_splits(T, H) * (size_t)T * (size_t)E * 4);
     L.h_perm = take(Tk * (size_t)I * 2);

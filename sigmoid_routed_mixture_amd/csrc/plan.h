@@ -12,13 +12,15 @@ namespace moe {
 
 // Tile shapes the kernels are built for (the kernels static_assert against these).
 constexpr int kWideBM = 128;    // tokens per tile of the LDS-tiled grouped GEMM
+constexpr int kTallBM = 256;    // tokens per tile of its tall variant (experts of >= 192 rows on average)
 constexpr int kSkinnyBM = 16;   // tokens per tile of the weight-streaming grouped GEMM
 constexpr int kRouterBT = 32;   // tokens per router workgroup
 constexpr int kPermChunk = 256; // tokens per permutation chunk
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
 
-enum class GemmPath { Wide, Skinny };
+enum class GemmPath { Wide, Tall, Skinny };
+constexpr int path_bm(GemmPath p) { return p == GemmPath::Tall ? kTallBM : p == GemmPath::Wide ? kWideBM : kSkinnyBM; }
 
 struct Check {
     moe_status status = MOE_OK;
@@ -32,7 +34,8 @@ Check check_aligned(const void* p, const char* name, size_t align = 16);
 
 // K-split of the router's logit GEMM: the number of K ranges (each a whole number of 64-wide chunks).
 int router_splits(int T, int H);
-// Weight-streaming kernel when experts average at most 16 rows, else the LDS-tiled one.
+// Weight-streaming kernel when experts average at most 16 rows, the LDS-tiled one with 128-token tiles
+// below 192 rows on average, and with 256-token tiles from there (it loads a third fewer bytes per FLOP).
 GemmPath gemm_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);

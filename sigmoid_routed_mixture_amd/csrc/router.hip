@@ -233,7 +233,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
     g.N = E;
     g.K = H;
     g.ksplit = S < 1 ? 1 : S;
-    hipError_t e = launch_gemm(GemmKind::Logits, true, g, ((int64_t)T + kWideBM - 1) / kWideBM, stream);
+    hipError_t e = launch_gemm(GemmKind::Logits, GemmPath::Wide, g, ((int64_t)T + kWideBM - 1) / kWideBM, stream);
     if (e != hipSuccess) return e;
     router_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(partial, g.ksplit, bias, T, E, k, scale, ids, gates,
                                                          logits);

@@ -43,7 +43,8 @@ int main() {
                             const size_t Tk = (size_t)T * k;
                             const size_t chunks = ((size_t)T + moe::kPermChunk - 1) / moe::kPermChunk;
                             const size_t tiles_need = (size_t)std::max(moe::max_tiles(T, E, k, moe::kSkinnyBM),
-                                                                       moe::max_tiles(T, E, k, moe::kWideBM)) * 8;
+                                                                       std::max(moe::max_tiles(T, E, k, moe::kWideBM),
+                                                                                moe::max_tiles(T, E, k, moe::kTallBM))) * 8;
                             struct R { size_t off, need; const char* name; };
                             std::vector<R> rs = {
                                 {L.ids, Tk * 4, "ids"}, {L.gates, Tk * 4, "gates"}, {L.counts, (size_t)E * 4, "counts"},
@@ -83,7 +84,7 @@ int main() {
         const int k = 1 + (int)(next() % std::min(E, 8));
         const int T = (int)(next() % 2000);
         const int ntn = 1 + (int)(next() % 40);
-        const int BM = moe::kWideBM;
+        const int BM = trial % 2 ? moe::kWideBM : moe::kTallBM;
         std::vector<int> counts(E, 0);
         const bool skew = trial % 3 == 0;
         for (int t = 0; t < T * k; ++t) counts[skew ? (int)(next() % 4) % E : (int)(next() % E)]++;

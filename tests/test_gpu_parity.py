@@ -113,7 +113,7 @@ def test_forward_parity(moe, name):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("glm5_decode", 16), ("mid", 384)])
-@pytest.mark.parametrize("path", ["wide", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
 def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
     say("[gemm path %s] %s T=%d" % (path, name, T))
     monkeypatch.setenv("MOE_GEMM_PATH", path)
@@ -165,7 +165,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("path", ["wide", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
 @pytest.mark.parametrize("shape", EDGE, ids=[e[-1] for e in EDGE])
 def test_edge_shapes(moe, monkeypatch, shape, path):
     T, H, E, k, I, Is, what = shape
@@ -184,7 +184,7 @@ def test_edge_shapes(moe, monkeypatch, shape, path):
     compare_out(out[same], ref["out"][same], what)
 
 
-@pytest.mark.parametrize("path", ["wide", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
 def test_identical_tokens_one_giant_group(moe, monkeypatch, path):
     say("[giant group %s]" % path)
     monkeypatch.setenv("MOE_GEMM_PATH", path)
