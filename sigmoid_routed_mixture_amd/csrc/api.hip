@@ -205,7 +205,7 @@ moe_status forward_impl(const Request& q) {
         xin = xn;
     }
     if (!given) {
-        const int S = moe::router_splits(T, H);
+        const int S = moe::router_splits(T, H, E);
         MOE_HIP(moe::launch_router(xin, q.w_router, q.bias, T, H, E, k, q.scale, ids_out, gates_out, nullptr,
                                    static_cast<float*>(at(L.partial)), S, s0),
                 "router");

@@ -1,7 +1,6 @@
 // Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t] (+ x'[t]), in
 // fp32 with the k slots added in slot order, then the shared expert, then (block entry point) the residual
 // stream. The per-slot expert outputs y are fp32 rows.
-// One workgroup per token; each thread owns 8-column chunks (16-byte loads and stores).
 // Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (y_routed = sum_i G_i E_i,
 // delta_ffn = y_routed + y_shared, x_{n+1} = x'_n + delta_ffn); nnterp encyclopedia glm_moe_dsa, "The
 // mixture" (routed + shared == out).
@@ -12,6 +11,9 @@
 namespace moe {
 namespace {
 
+// One workgroup per (token, column range); each thread owns 8-column chunks (16-byte loads and stores).
+// The k slot rows of a chunk are loaded eight at a time before any is added, so their latencies overlap;
+// they are added in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ y_shared,
@@ -26,18 +28,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         rr[tid] = slot_row[(size_t)t * k + tid];
     }
     __syncthreads();
-    for (int c = tid; c < H / 8; c += 256) {
+    for (int c = blockIdx.y * 256 + tid; c < H / 8; c += 256 * gridDim.y) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int r = rr[j];
-            if (r < 0) continue;
-            const float4 v0 = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8);
-            const float4 v1 = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8 + 4);
-            const float gj = g[j];
-            acc[0] += gj * v0.x; acc[1] += gj * v0.y; acc[2] += gj * v0.z; acc[3] += gj * v0.w;
-            acc[4] += gj * v1.x; acc[5] += gj * v1.y; acc[6] += gj * v1.z; acc[7] += gj * v1.w;
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float4 v0[8], v1[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = j0 + jj;
+                const int r = j < k ? rr[j] : -1;
+                if (r >= 0) {
+                    v0[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8);
+                    v1[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8 + 4);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = j0 + jj;
+                if (j < k && rr[j] >= 0) {
+                    const float gj = g[j];
+                    acc[0] += gj * v0[jj].x; acc[1] += gj * v0[jj].y; acc[2] += gj * v0[jj].z; acc[3] += gj * v0[jj].w;
+                    acc[4] += gj * v1[jj].x; acc[5] += gj * v1[jj].y; acc[6] += gj * v1[jj].z; acc[7] += gj * v1[jj].w;
+                }
+            }
         }
         float* o = out + (size_t)t * H + c * 8;
         if (y_shared) {
@@ -64,7 +78,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
                           const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    combine_kernel<<<T, 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out);
+    // few tokens: spread each token's row over several workgroups so every thread has one chunk
+    const int ysplit = T < 1024 ? (H / 8 + 255) / 256 : 1;
+    combine_kernel<<<dim3(T, ysplit), 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out);
     return hipGetLastError();
 }
 

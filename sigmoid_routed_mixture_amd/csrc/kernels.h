@@ -8,9 +8,10 @@
 
 namespace moe {
 
-// Router: logits, sigmoid, biased top-k, gates. With `partial` ([S, T, E] fp32 scratch) the logits run
-// as a K-split dense GEMM on the grouped-GEMM kernel and a top-k kernel sums the S partials in order;
-// without it one fused kernel (32 tokens per workgroup) does everything.
+// Router: logits, sigmoid, biased top-k, gates. With `partial` ([S, T, E] fp32 scratch, S from
+// router_splits) the logits run K-split into fp32 partials (up to 16 tokens: one-wave workgroups of 16
+// experts; above: the wide GEMM kernel) and a top-k kernel sums the S partials in order; without it one
+// fused kernel (32 tokens per workgroup) does everything.
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
                          float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
                          hipStream_t stream);

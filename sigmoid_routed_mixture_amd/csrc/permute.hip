@@ -115,6 +115,57 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
     }
 }
 
+// The whole permutation in one workgroup when all tokens fit one chunk (decode): histogram, offsets and
+// tile list, then the scatter, with the bit matrix kept in LDS between them.
+__global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                          int BM, int32_t* __restrict__ row_token,
+                                                          int32_t* __restrict__ slot_row) {
+    __shared__ uint32_t mask[kMaxE][8];
+    __shared__ int sh[256];
+    __shared__ int offs[kMaxE];
+    build_mask(mask, ids, T, E, k);
+    const int tid = threadIdx.x;
+    int n = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) n += __popc(mask[tid][w]);
+        counts[tid] = n;
+    }
+    int total = 0;
+    const int off = block_exclusive_scan(tid < E ? n : 0, sh, &total);
+    if (tid < E) {
+        offsets[tid] = off;
+        offs[tid] = off;
+    }
+    if (tid == 0) offsets[E] = total;
+    if (tiles != nullptr) {
+        const int nt = (tid < E && BM > 0) ? (n + BM - 1) / BM : 0;
+        int tiles_total = 0;
+        const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
+        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid, i * BM);
+        if (tid == 0) ntiles[0] = tiles_total;
+    }
+    __syncthreads();
+    const int t = tid;
+    if (t >= T) return;
+    const int w = tid >> 5;
+    const uint32_t below = (1u << (tid & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        if (e < 0 || e >= E) {
+            slot_row[(size_t)t * k + j] = -1;
+            continue;
+        }
+        int rank = __popc(mask[e][w] & below);
+        for (int v = 0; v < w; ++v) rank += __popc(mask[e][v]);
+        const int row = offs[e] + rank;
+        row_token[row] = t;
+        slot_row[(size_t)t * k + j] = row;
+    }
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
                                                           const int32_t* __restrict__ offsets, int E, int T, int H,
@@ -140,6 +191,11 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
                           int32_t* ntiles, int BM, hipStream_t stream) {
     const int chunks = (T + kChunk - 1) / kChunk;
+    if (chunks == 1) {
+        perm_single_kernel<<<1, 256, 0, stream>>>(ids, T, E, k, counts, offsets, tiles, ntiles, BM, row_token,
+                                                  slot_row);
+        return hipGetLastError();
+    }
     perm_count_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, chunk_scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

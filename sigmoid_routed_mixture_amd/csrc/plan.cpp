@@ -33,7 +33,13 @@ Check check_aligned(const void* p, const char* name, size_t align) {
     return Check{};
 }
 
-int router_splits(int T, int H) {
+int router_splits(int T, int H, int E) {
+    if (T <= kRouterSmallT) {
+        const int64_t groups = (std::max(E, 1) + 15) / 16;
+        int64_t s = (256 + groups - 1) / groups;
+        s = std::max<int64_t>(1, std::min<int64_t>(s, std::min(kRouterMaxSplits, H / 32)));
+        return (int)s;
+    }
     // enough K ranges that the logits GEMM has >= 256 workgroups of 128 tokens, at most 32 and at most one
     // per 64-wide K chunk
     const int64_t tiles = ((int64_t)T + kWideBM - 1) / kWideBM;
@@ -73,7 +79,7 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     // room for the longest tile list either grouped-GEMM kernel can ask for (the smallest BM)
     L.tiles = take((size_t)max_tiles(T, E, k, std::min(std::min(kWideBM, kTallBM), kSkinnyBM)) * 8);
     L.ntiles = take(4);
-    L.partial = take((size_t)router_splits(T, H) * (size_t)T * (size_t)E * 4);
+    L.partial = take((size_t)router_splits(T, H, E) * (size_t)T * (size_t)E * 4);
     L.h_perm = take(Tk * (size_t)I * 2);
     L.y_perm = take(Tk * (size_t)H * 4);
     L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);

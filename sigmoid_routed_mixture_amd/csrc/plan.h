@@ -32,8 +32,12 @@ struct Check {
 Check check_sizes(int T, int H, int E, int k, int I, int Is, bool need_I);
 Check check_aligned(const void* p, const char* name, size_t align = 16);
 
-// K-split of the router's logit GEMM: the number of K ranges (each a whole number of 64-wide chunks).
-int router_splits(int T, int H);
+// K-split of the router's logit GEMM: the number of K ranges. Up to kRouterSmallT tokens the logits run on
+// one-wave workgroups of 16 experts x 32-wide K chunks, split so the launch has >= 256 workgroups (at most
+// kRouterMaxSplits ranges); above, on the wide GEMM kernel with 64-wide chunks (at most 32 ranges).
+constexpr int kRouterSmallT = 16;
+constexpr int kRouterMaxSplits = 64;
+int router_splits(int T, int H, int E);
 // Weight-streaming kernel when experts average at most 16 rows, the LDS-tiled one with 128-token tiles
 // below 192 rows on average, and with 256-token tiles from there (it loads a third fewer bytes per FLOP).
 GemmPath gemm_path(int T, int E, int k);

@@ -182,7 +182,49 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const uint16_t* __res
     }
 }
 
-// Sums the S partial logits of each token in split order, then routes it (one wave per token).
+// Logits for at most 16 tokens: one wave per (16 experts, K range) workgroup, 16x16x32 MFMAs over
+// 32-wide K chunks (experts are the A rows, tokens the B columns), every chunk's loads issued before its
+// MFMAs; each workgroup writes its fp32 partial z for its experts. Many small workgroups keep the whole
+// of W_r streaming at once, which a few large ones cannot at decode sizes.
+__global__ __launch_bounds__(64) void router_small_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr, int T, int H, int E, int S,
+                                                          float* __restrict__ partial) {
+    const int groups = (E + 15) / 16;
+    const int eg = blockIdx.x % groups;
+    const int s = blockIdx.x / groups;
+    const int lane = threadIdx.x;
+    const int rl = lane & 15, kg = lane >> 4;
+    const int C = H / 32;
+    const int c0 = (int)((int64_t)s * C / S), c1 = (int)((int64_t)(s + 1) * C / S);
+    int e = eg * 16 + rl;
+    e = e < E ? e : E - 1;
+    int t = rl < T ? rl : T - 1;
+    const uint16_t* wrow = wr + (size_t)e * H + kg * 8;
+    const uint16_t* xrow = x + (size_t)t * H + kg * 8;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = c0; c < c1; c += 4) {
+        Pack16 a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (c + i < c1) {
+                a[i] = load16(wrow + (c + i) * 32);
+                b[i] = load16(xrow + (c + i) * 32);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (c + i < c1) acc = mfma16x16x32(a[i], b[i], acc);
+    }
+    // element r: expert eg * 16 + 4 kg + r, token rl
+    if (rl >= T) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int ee = eg * 16 + 4 * kg + r;
+        if (ee < E) partial[((size_t)s * T + rl) * E + ee] = acc[r];
+    }
+}
+
+// Sums the S partial logits of each token in split order, then routes it (one wave per token, four
+// tokens per workgroup; many tokens).
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int S,
                                                           const float* __restrict__ bias, int T, int E, int k,
                                                           float scale, int32_t* __restrict__ ids,
@@ -214,6 +256,37 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
 }
 
+// The same for a few tokens: one workgroup per token, one thread per expert with all S loads in flight
+// at once (latency, not throughput, bounds decode), then one wave routes the token.
+__global__ __launch_bounds__(256) void router_topk_few_kernel(const float* __restrict__ partial, int S,
+                                                          const float* __restrict__ bias, int T, int E, int k,
+                                                          float scale, int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates, float* __restrict__ logits) {
+    __shared__ float zs[kMaxE];
+    const int t = blockIdx.x;
+    const int e = threadIdx.x;
+    if (e < E) {
+        const size_t stride = (size_t)T * E;
+        const float* p = partial + (size_t)t * E + e;
+        float v[kRouterMaxSplits];
+#pragma unroll
+        for (int i = 0; i < kRouterMaxSplits; ++i)
+            if (i < S) v[i] = p[(size_t)i * stride];
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRouterMaxSplits; ++i)
+            if (i < S) z += v[i];
+        zs[e] = z;
+    }
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    float z4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) z4[q] = lane + 64 * q < E ? zs[lane + 64 * q] : 0.f;
+    topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
+}
+
 } // namespace
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E, int k,
@@ -222,6 +295,14 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
     if (partial == nullptr) {
         const int tblocks = (T + kBT - 1) / kBT;
         router_fused_kernel<<<tblocks, 256, 0, stream>>>(x, wr, bias, T, H, E, k, scale, ids, gates, logits);
+        return hipGetLastError();
+    }
+    if (T <= kRouterSmallT) {
+        const int groups = (E + 15) / 16;
+        router_small_kernel<<<groups * S, 64, 0, stream>>>(x, wr, T, H, E, S, partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        router_topk_few_kernel<<<T, 256, 0, stream>>>(partial, S, bias, T, E, k, scale, ids, gates, logits);
         return hipGetLastError();
     }
     // logits as a dense GEMM (W_r rows x token tiles), K split S ways into fp32 partials, then the top-k

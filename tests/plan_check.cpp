@@ -51,7 +51,7 @@ int main() {
                                 {L.offsets, ((size_t)E + 1) * 4, "offsets"}, {L.row_token, Tk * 4, "row_token"},
                                 {L.slot_row, Tk * 4, "slot_row"}, {L.chunk_base, chunks * E * 4, "chunk_base"},
                                 {L.tiles, tiles_need, "tiles"}, {L.ntiles, 4, "ntiles"},
-                                {L.partial, (size_t)moe::router_splits(T, H) * T * E * 4, "partial"},
+                                {L.partial, (size_t)moe::router_splits(T, H, E) * T * E * 4, "partial"},
                                 {L.h_perm, Tk * I * 2, "h_perm"}, {L.y_perm, Tk * H * 4, "y_perm"}};
                             if (Is > 0) {
                                 rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
@@ -64,8 +64,9 @@ int main() {
                                 CHECK(end >= rs[i].off + rs[i].need, "T=%d H=%d E=%d k=%d I=%d Is=%d: %s has %zu < %zu",
                                       T, H, E, k, I, Is, rs[i].name, end - rs[i].off, rs[i].need);
                             }
-                            const int S = moe::router_splits(T, H);
-                            CHECK(S >= 1 && S <= H / 64, "splits %d for H=%d", S, H);
+                            const int S = moe::router_splits(T, H, E);
+                            CHECK(S >= 1 && S <= moe::kRouterMaxSplits && S <= (T <= moe::kRouterSmallT ? H / 32 : H / 64),
+                                  "splits %d for T=%d H=%d", S, T, H);
                         }
                 }
     // Workgroup order of the LDS-tiled grouped GEMM: with the grid padded to a multiple of kXcds, every
