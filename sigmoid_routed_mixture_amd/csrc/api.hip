@@ -85,6 +85,42 @@ moe::GemmPath pick_path(int T, int E, int k) {
     return moe::gemm_path(T, E, k);
 }
 
+// A dense SwiGLU MLP (the shared expert, or the dense-first blocks' MLP): gate/up into h, then down into
+// the fp32 out. On the weight-streaming kernel with few workgroups each GEMM splits K into fp32 partials
+// (`part`, sized by dense_partial_bytes) reduced in split order.
+moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, const uint16_t* w3,
+                     const uint16_t* w2, int T, int H, int I, uint16_t* h, float* out, float* part, hipStream_t s,
+                     const char* what) {
+    const int BM = moe::path_bm(path);
+    const int64_t tiles = ((int64_t)T + BM - 1) / BM;
+    const bool skinny = path == moe::GemmPath::Skinny;
+    const int s1 = skinny && part ? moe::dense_splits(true, T, I, H) : 1;
+    const int s2 = skinny && part ? moe::dense_splits(false, T, H, I) : 1;
+    moe::GemmArgs g1{};
+    g1.act = x;
+    g1.w_a = w1;
+    g1.w_b = w3;
+    g1.out = s1 > 1 ? static_cast<void*>(part) : static_cast<void*>(h);
+    g1.dense_rows = T;
+    g1.N = I;
+    g1.K = H;
+    g1.ksplit = s1;
+    const std::string w(what);
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), (w + " gate/up GEMM").c_str());
+    if (s1 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::GateUp, part, s1, T, I, h, s), (w + " gate/up reduce").c_str());
+    moe::GemmArgs g2{};
+    g2.act = h;
+    g2.w_a = w2;
+    g2.out = s2 > 1 ? static_cast<void*>(part) : static_cast<void*>(out);
+    g2.dense_rows = T;
+    g2.N = H;
+    g2.K = I;
+    g2.ksplit = s2;
+    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, tiles, s), (w + " down GEMM").c_str());
+    if (s2 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::DownF32, part, s2, T, H, out, s), (w + " down reduce").c_str());
+    return MOE_OK;
+}
+
 } // namespace
 
 namespace {
@@ -220,24 +256,8 @@ moe_status forward_impl(const Request& q) {
     if (two_streams) MOE_TRY(order_after(s1, s0, ev->fork));
     if (Is > 0) {
         hipStream_t ss = two_streams ? s1 : s0;
-        moe::GemmArgs g1{};
-        g1.act = xin;
-        g1.w_a = q.ws1;
-        g1.w_b = q.ws3;
-        g1.out = h_sh;
-        g1.dense_rows = T;
-        g1.N = Is;
-        g1.K = H;
-        const int64_t dense_tiles = ((int64_t)T + BM - 1) / BM;
-        MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, dense_tiles, ss), "shared gate/up GEMM");
-        moe::GemmArgs g2{};
-        g2.act = h_sh;
-        g2.w_a = q.ws2;
-        g2.out = y_sh;
-        g2.dense_rows = T;
-        g2.N = H;
-        g2.K = Is;
-        MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, dense_tiles, ss), "shared down GEMM");
+        float* part = L.sh_partial != size_t(-1) ? static_cast<float*>(at(L.sh_partial)) : nullptr;
+        MOE_TRY(dense_mlp(path, xin, q.ws1, q.ws3, q.ws2, T, H, Is, h_sh, y_sh, part, ss, "shared"));
     }
     MOE_TRY(mark(3));
 
@@ -435,7 +455,7 @@ moe_status moe_block_forward(const moe_bf16* resid, const moe_bf16* gamma, doubl
 
 size_t moe_dense_mlp_workspace_bytes(int T, int H, int I) {
     if (!moe::check_dense_sizes(T, H, I).ok()) return 0;
-    return moe::dense_workspace_bytes(T, I);
+    return moe::dense_workspace_bytes(T, H, I);
 }
 
 moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2, int T,
@@ -450,29 +470,14 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     MOE_TRY(need(out, "out"));
     if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is null");
     MOE_TRY(from_check(moe::check_aligned(workspace, "workspace", 256)));
-    if (workspace_bytes < moe::dense_workspace_bytes(T, I))
+    if (workspace_bytes < moe::dense_workspace_bytes(T, H, I))
         return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dense_mlp_workspace_bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const moe::GemmPath path = pick_path(T, 1, 1);
-    const int BM = moe::path_bm(path);
-    const int64_t tiles = ((int64_t)T + BM - 1) / BM;
-    moe::GemmArgs g1{};
-    g1.act = x;
-    g1.w_a = w1;
-    g1.w_b = w3;
-    g1.out = workspace;
-    g1.dense_rows = T;
-    g1.N = I;
-    g1.K = H;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), "dense gate/up GEMM");
-    moe::GemmArgs g2{};
-    g2.act = static_cast<const uint16_t*>(workspace);
-    g2.w_a = w2;
-    g2.out = out;
-    g2.dense_rows = T;
-    g2.N = H;
-    g2.K = I;
-    MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, tiles, s), "dense down GEMM");
+    char* ws = static_cast<char*>(workspace);
+    const size_t hbytes = ((size_t)T * (size_t)I * 2 + 255) / 256 * 256;
+    float* part = moe::dense_partial_bytes(T, H, I) > 0 ? reinterpret_cast<float*>(ws + hbytes) : nullptr;
+    MOE_TRY(dense_mlp(path, x, w1, w3, w2, T, H, I, reinterpret_cast<uint16_t*>(ws), out, part, s, "dense"));
     return MOE_OK;
 }
 

@@ -355,8 +355,16 @@ static_assert(kSBM == 16, "skinny tiling assumes one 16-token MFMA column block"
 constexpr int kSU = 1;          // 64-wide K chunks per pipeline stage (K is a multiple of 64)
 
 template <GemmKind KIND, bool DENSE>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
-    const int64_t bid = blockIdx.x;
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn, int64_t tiles_per_split) {
+    int64_t bid = blockIdx.x;
+    // dense GEMMs with few workgroups split K: split s covers 64-wide chunks [s C / S, (s + 1) C / S) and
+    // writes fp32 partials (gate/up: g and u side by side) for a reduction kernel
+    int split = 0;
+    const bool partials = DENSE && a.ksplit > 1;
+    if (partials) {
+        split = (int)(bid / (tiles_per_split * ntn));
+        bid -= (int64_t)split * tiles_per_split * ntn;
+    }
     const int ntile = (int)(bid % ntn);
     TileInfo ti;
     if (!tile_info<DENSE, kSBM>(a, bid / ntn, ti)) return;
@@ -391,10 +399,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
     struct Stage {
         Pack16 w[kSU][2][2], x[kSU][2];
     };
-    const int nst = K / (64 * kSU);
+    const int C = K / (64 * kSU);
+    const int cb = partials ? (int)((int64_t)split * C / a.ksplit) : 0;
+    const int nst = partials ? (int)((int64_t)(split + 1) * C / a.ksplit) - cb : C;
     auto load = [&](Stage& s, int st) {
         st = st < nst ? st : nst - 1;
-        const int kk = st * 64 * kSU;
+        const int kk = (cb + st) * 64 * kSU;
 #pragma unroll
         for (int u = 0; u < kSU; ++u) {
 #pragma unroll
@@ -429,6 +439,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
 
     if (rl >= ti.rows) return;
     const size_t row = (size_t)ti.off + ti.m0 + rl;
+    if (partials) {
+        float* base = static_cast<float*>(a.out) + (size_t)split * a.dense_rows * (KIND == GemmKind::GateUp ? 2 * N : N);
+        if (KIND == GemmKind::GateUp) {
+            const int col = col0 + 4 * kg;
+            float* o = base + row * 2 * N;
+            *reinterpret_cast<float4*>(o + col) = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+            *reinterpret_cast<float4*>(o + N + col) = make_float4(acc[1][0], acc[1][1], acc[1][2], acc[1][3]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int col = col0 + b * 16 + 4 * kg;
+                if (col >= N) continue;
+                *reinterpret_cast<float4*>(base + row * N + col) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+            }
+        }
+        return;
+    }
     if (KIND == GemmKind::GateUp) {
         const int col = col0 + 4 * kg;
         uint2 v;
@@ -454,6 +481,41 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn) {
     }
 }
 
+// Reductions of the split-K partials, in split order: gate/up -> h = bf16(silu(g) * u); down -> fp32 out.
+__global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restrict__ part, int S, int rows, int N,
+                                                            uint16_t* __restrict__ h) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; // 4 consecutive columns of one row
+    if (i >= (int64_t)rows * N) return;
+    const int64_t row = i / N, col = i % N;
+    float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < S; ++sp) {
+        const float* p = part + ((size_t)sp * rows + row) * 2 * N + col;
+        const float4 gv = *reinterpret_cast<const float4*>(p);
+        const float4 uv = *reinterpret_cast<const float4*>(p + N);
+        g[0] += gv.x; g[1] += gv.y; g[2] += gv.z; g[3] += gv.w;
+        u[0] += uv.x; u[1] += uv.y; u[2] += uv.z; u[3] += uv.w;
+    }
+    uint2 v;
+    v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+    v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+    *reinterpret_cast<uint2*>(h + row * N + col) = v;
+}
+
+__global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                         float* __restrict__ out) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 acc = *reinterpret_cast<const float4*>(part + i);
+    for (int sp = 1; sp < S; ++sp) {
+        const float4 v = *reinterpret_cast<const float4*>(part + (size_t)sp * n + i);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + i) = acc;
+}
+
 template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     const bool wide = path != GemmPath::Skinny;
@@ -462,7 +524,7 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         ntn = KIND == GemmKind::GateUp ? (a.N + kWBN / 2 - 1) / (kWBN / 2) : (a.N + kWBN - 1) / kWBN;
     else
         ntn = KIND == GemmKind::GateUp ? a.N / 64 : (a.N + 127) / 128;
-    const int splits = KIND == GemmKind::Logits ? a.ksplit : 1;
+    const int splits = (KIND == GemmKind::Logits || (!wide && DENSE)) && a.ksplit > 1 ? a.ksplit : 1;
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
     if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
@@ -477,12 +539,23 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         else if (path == GemmPath::Tall)
             gemm_wide_kernel<KIND, DENSE, kTallBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
         else
-            gemm_skinny_kernel<KIND, DENSE><<<grid, 256, 0, stream>>>(a, ntn);
+            gemm_skinny_kernel<KIND, DENSE><<<grid, 256, 0, stream>>>(a, ntn, grid_tiles);
     }
     return hipGetLastError();
 }
 
 } // namespace
+
+hipError_t launch_reduce(GemmKind kind, const float* partial, int S, int rows, int N, void* out, hipStream_t stream) {
+    const int64_t n = (int64_t)rows * N;
+    if (n <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
+    if (kind == GemmKind::GateUp)
+        reduce_swiglu_kernel<<<blocks, 256, 0, stream>>>(partial, S, rows, N, static_cast<uint16_t*>(out));
+    else
+        reduce_sum_kernel<<<blocks, 256, 0, stream>>>(partial, S, n, static_cast<float*>(out));
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     const bool dense = a.counts == nullptr;

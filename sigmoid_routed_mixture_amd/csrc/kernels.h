@@ -41,10 +41,15 @@ struct GemmArgs {
     int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped
     int N, K;                  // output width (gate/up: I, h columns), reduction length
-    int ksplit;                // logits only: K ranges, each writing its own [dense_rows, N] fp32 partial
+    int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
+                               // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
 };
 enum class GemmKind { GateUp, Down, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
+
+// In-order reduction of a split dense GEMM's partials (dense_splits in plan.h) into h (gate/up, bf16 after
+// the SwiGLU) or the fp32 output (down).
+hipError_t launch_reduce(GemmKind kind, const float* partial, int S, int rows, int N, void* out, hipStream_t stream);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
 // residual (bf16) added last.

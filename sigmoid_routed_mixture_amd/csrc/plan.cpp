@@ -84,6 +84,8 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     L.y_perm = take(Tk * (size_t)H * 4);
     L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
     L.y_sh = Is > 0 ? take((size_t)T * (size_t)H * 4) : size_t(-1);
+    const size_t shp = Is > 0 ? dense_partial_bytes(T, H, Is) : 0;
+    L.sh_partial = shp > 0 ? take(shp) : size_t(-1);
     L.x_norm = with_norm ? take((size_t)T * (size_t)H * 2) : size_t(-1);
     L.total = off;
     return L;
@@ -99,7 +101,27 @@ Check check_dense_sizes(int T, int H, int Id) {
     return Check{};
 }
 
-size_t dense_workspace_bytes(int T, int Id) { return align_up(std::max<size_t>((size_t)T * (size_t)Id * 2, 1), 256); }
+int dense_splits(bool gate_up, int rows, int N, int K) {
+    if (rows <= 0 || N <= 0 || K <= 0) return 1;
+    const int64_t tiles = ((int64_t)rows + kSkinnyBM - 1) / kSkinnyBM;
+    const int64_t ntn = gate_up ? N / 64 : (N + 127) / 128;
+    const int64_t blocks = std::max<int64_t>(1, tiles * ntn);
+    const int64_t want = (1024 + blocks - 1) / blocks;
+    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(kMaxDenseSplits, K / 256));
+    return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+size_t dense_partial_bytes(int T, int H, int Id) {
+    const int s1 = dense_splits(true, T, Id, H), s2 = dense_splits(false, T, H, Id);
+    const size_t a = s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0;
+    const size_t b = s2 > 1 ? (size_t)s2 * T * H * 4 : 0;
+    return std::max(a, b);
+}
+
+size_t dense_workspace_bytes(int T, int H, int Id) {
+    const size_t hb = align_up(std::max<size_t>((size_t)T * (size_t)Id * 2, 1), 256);
+    return hb + align_up(dense_partial_bytes(T, H, Id), 256);
+}
 
 size_t permute_scratch_bytes(int T, int E) {
     const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;

@@ -18,6 +18,7 @@ constexpr int kRouterBT = 32;   // tokens per router workgroup
 constexpr int kPermChunk = 256; // tokens per permutation chunk
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
+constexpr int kMaxDenseSplits = 16; // K ranges of a dense GEMM on the weight-streaming kernel
 
 enum class GemmPath { Wide, Tall, Skinny };
 constexpr int path_bm(GemmPath p) { return p == GemmPath::Tall ? kTallBM : p == GemmPath::Wide ? kWideBM : kSkinnyBM; }
@@ -68,15 +69,22 @@ constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
     size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,
-        y_perm, h_sh, y_sh, x_norm;
+        y_perm, h_sh, y_sh, sh_partial, x_norm;
     size_t total;
 };
 // with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.
 Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm = false);
 size_t permute_scratch_bytes(int T, int E);
 
-// Dense SwiGLU MLP: T >= 0, H and Id positive multiples of 64. Its workspace is h [T, Id] bf16.
+// K ranges of a dense GEMM (rows x N outputs, reduction K) on the weight-streaming kernel: enough for
+// ~1024 workgroups, at most kMaxDenseSplits, each range at least 256 wide. 1 = no split.
+int dense_splits(bool gate_up, int rows, int N, int K);
+// fp32 partials of a dense SwiGLU MLP (gate/up then down, one region reused) on that kernel; 0 if unsplit.
+size_t dense_partial_bytes(int T, int H, int Id);
+
+// Dense SwiGLU MLP: T >= 0, H and Id positive multiples of 64. Its workspace is h [T, Id] bf16 and the
+// split partials.
 Check check_dense_sizes(int T, int H, int Id);
-size_t dense_workspace_bytes(int T, int Id);
+size_t dense_workspace_bytes(int T, int H, int Id);
 
 } // namespace moe

@@ -57,6 +57,8 @@ int main() {
                                 rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
                                 rs.push_back({L.y_sh, (size_t)T * H * 4, "y_sh"});
                             }
+                            if (L.sh_partial != size_t(-1))
+                                rs.push_back({L.sh_partial, moe::dense_partial_bytes(T, H, Is), "sh_partial"});
                             rs.push_back({L.x_norm, (size_t)T * H * 2, "x_norm"});
                             for (size_t i = 0; i < rs.size(); ++i) {
                                 const size_t end = i + 1 < rs.size() ? rs[i + 1].off : L.total;
@@ -120,6 +122,29 @@ int main() {
         ++orders;
     }
     std::printf("%d block orders checked\n", orders);
+
+    // split dense GEMMs on the weight-streaming kernel: every K range is non-empty and the partial region
+    // holds both GEMMs' partials; a forward layout with a shared expert holds them too
+    int dense = 0;
+    for (int T : {1, 7, 16, 64, 129, 384, 1000, 4096})
+        for (int H : {64, 256, 2048, 6144})
+            for (int Id : {64, 384, 1536, 2048, 10240, 12288}) {
+                ++dense;
+                const int s1 = moe::dense_splits(true, T, Id, H), s2 = moe::dense_splits(false, T, H, Id);
+                CHECK(s1 >= 1 && s1 <= moe::kMaxDenseSplits && (s1 == 1 || H / 64 >= s1),
+                      "gate/up splits %d (T=%d H=%d I=%d)", s1, T, H, Id);
+                CHECK(s2 >= 1 && s2 <= moe::kMaxDenseSplits && (s2 == 1 || Id / 64 >= s2),
+                      "down splits %d (T=%d H=%d I=%d)", s2, T, H, Id);
+                const size_t need = std::max(s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0,
+                                             s2 > 1 ? (size_t)s2 * T * H * 4 : 0);
+                CHECK(moe::dense_partial_bytes(T, H, Id) >= need, "partials T=%d H=%d I=%d", T, H, Id);
+                CHECK(moe::dense_workspace_bytes(T, H, Id) >= (size_t)T * Id * 2 + need, "dense workspace");
+                const moe::Layout L = moe::forward_layout(T, H, 8, 2, 64, Id);
+                CHECK(need == 0 || (L.sh_partial != size_t(-1) && L.x_norm == size_t(-1) &&
+                                    L.total >= L.sh_partial + need),
+                      "shared partials T=%d H=%d Is=%d", T, H, Id);
+            }
+    std::printf("%d dense splits checked\n", dense);
     std::printf("%d layouts checked, %d failures\n", n, fails);
     return fails ? 1 : 0;
 }
