@@ -4,9 +4,12 @@
 A step is one pass of the whole layer (router, top-k and gates, permutation, SwiGLU routed experts, shared
 expert, combine) over one batch of seeded synthetic tokens already resident in HBM. The default workload
 is the GLM-5-shape prefill (T = 8192 tokens, H 6144, 256 experts top-8, I = Is = 2048, scale 2.5); the
-GLM-5 decode step (T = 16) is measured in the same run and reported under "decode".
+GLM-5 decode step (T = 16) is measured in the same run and reported under "decode". The shared expert runs on
+the main stream unless --two-streams is given.
 
-Prints one JSON line. `value` is prefill tokens/s. `roofline` is the dominant kernel (the routed gate/up
+Prints one JSON line. `value` is prefill tokens/s. `next` holds the entry points around the mixture, each
+timed on its own workload after the main measurement: the GLM-4.7-Flash layer, the block pass (RMSNorm +
+mixture + residual) and the routing override at the GLM-5 shapes, and the dense SwiGLU MLP. `roofline` is the dominant kernel (the routed gate/up
 SwiGLU grouped GEMM): algorithmic FLOPs per launch / its mean launch time from HIP events recorded on the
 kernel's stream inside the timed region. `cpu_baseline` is the CPU oracle timed on a bounded sample of the
 same workload on this host.
@@ -146,6 +149,121 @@ def gate_up_bytes(cfg, active):
     return active * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * cfg.T * cfg.k * cfg.I
 
 
+def time_call(fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls after `warmup`, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        fn()
+    s1.record()
+    torch.cuda.synchronize()
+    return s0.elapsed_time(s1) / steps
+
+
+def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
+    """The entry points around the mixture, each on its own workload: the GLM-4.7-Flash layer (decode and
+    prefill), the block (RMSNorm + mixture + residual) and the routing override at the GLM-5 shapes, and
+    the dense SwiGLU MLP of the dense-first blocks."""
+    import torch
+
+    res = {}
+    s1 = None  # shared expert on the main stream, as in the main measurement
+
+    def layer_inputs(cfg, w):
+        host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
+        d = {k: to_dev_bf16(v, device) for k, v in host_t.items() if k != "b"}
+        d["b"] = torch.from_numpy(host_t["b"]).to(device)
+        d.update(w)
+        return d
+
+    def mixture(cfg, d, nsteps):
+        T = cfg.T
+        out = torch.empty(T, cfg.H, dtype=torch.float32, device=device)
+        ids = torch.empty(T, cfg.k, dtype=torch.int32, device=device)
+        gates = torch.empty(T, cfg.k, dtype=torch.float32, device=device)
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=device)
+        ws = torch.empty(m.moe_block_workspace_bytes(T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.Is), dtype=torch.uint8,
+                         device=device)
+        w = (d["w1"], d["w3"], d["w2"], d["ws1"], d["ws3"], d["ws2"])
+
+        def fwd():
+            m.moe_forward(d["x"], d["wr"], d["b"], *w, cfg.k, cfg.scale, out, ws, ids, gates, counts,
+                          stream_shared=s1)
+
+        ms = time_call(fwd, nsteps, warmup)
+        active = int((counts.cpu().numpy() > 0).sum())
+        r = {"T": T, "ms": ms, "tokens_per_s": T / (ms * 1e-3), "active_experts": active}
+        if T <= 64:
+            gbs = layer_bytes(cfg, active) / (ms * 1e-3) / 1e9
+            r.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
+        else:
+            tf = cfg.flops() / (ms * 1e-3) / 1e12
+            r.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        return r, fwd, (out, ids, gates, ws, w)
+
+    # GLM-4.7-Flash layer (H 2048, 64 experts top-4, I = Is = 1536, scale 1.8)
+    c47d, c47p = wl.BY_NAME["glm47_decode"], wl.BY_NAME["glm47_prefill"]
+    log("generating GLM-4.7-Flash expert weights")
+    w47 = {n: to_dev_bf16(wl.weight(c47d, n), device) for n in WEIGHT_NAMES}
+    for cfg, n in ((c47d, decode_steps), (c47p, steps)):
+        res[cfg.name], _, _ = mixture(cfg, layer_inputs(cfg, w47), n)
+        log("%s: %s" % (cfg.name, res[cfg.name]))
+    del w47
+
+    # block pass and routing override at the GLM-5 shapes, against the plain mixture on the same tokens
+    for name, n in (("glm5_prefill", steps), ("glm5_decode", decode_steps)):
+        cfg = wl.BY_NAME[name]
+        d = layer_inputs(cfg, dev_w)
+        base, fwd, (out, ids, gates, ws, w) = mixture(cfg, d, n)
+        gamma = to_dev_bf16(wl.norm_weight(cfg.H, cfg.seed), device)
+        xn = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=device)
+
+        def blk():
+            m.moe_block_forward(d["x"], gamma, wl.NORM_EPS, d["wr"], d["b"], *w, cfg.k, cfg.scale, out, ws,
+                                x_norm=xn, stream_shared=s1)
+
+        ms_b = time_call(blk, n, warmup)
+        fwd()
+        g2 = gates.clone()
+        g2[ids == 0] = 0.0  # the pages' ablation of one expert
+
+        def rtd():
+            m.moe_forward_routed(d["x"], ids, g2, *w, out, ws, stream_shared=s1)
+
+        ms_r = time_call(rtd, n, warmup)
+        res["block_" + name] = {"ms": ms_b, "tokens_per_s": cfg.T / (ms_b * 1e-3), "mixture_ms": base["ms"],
+                                "norm_and_residual_ms": ms_b - base["ms"]}
+        res["routed_" + name] = {"ms": ms_r, "tokens_per_s": cfg.T / (ms_r * 1e-3), "mixture_ms": base["ms"]}
+        log("block/routed %s: %s %s" % (name, res["block_" + name], res["routed_" + name]))
+
+    # dense SwiGLU MLP of the dense-first blocks
+    for name, n in (("glm5_dense_prefill", steps), ("glm5_dense_decode", decode_steps),
+                    ("glm47_dense_prefill", steps)):
+        cfg = wl.DENSE_BY_NAME[name]
+        w = {k: to_dev_bf16(wl.dense_weight(cfg, k), device) for k in ("w1", "w3", "w2")}
+        x = to_dev_bf16(wl.dense_tokens(cfg), device)
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
+        ws = torch.empty(m.moe_dense_mlp_workspace_bytes(cfg.T, cfg.H, cfg.Id), dtype=torch.uint8, device=device)
+        ms = time_call(lambda: m.moe_dense_mlp(x, w["w1"], w["w3"], w["w2"], out, ws), n, warmup)
+        r = {"T": cfg.T, "H": cfg.H, "I": cfg.Id, "ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3)}
+        if cfg.T <= 64:
+            gbs = (3 * cfg.H * cfg.Id * 2 + 2 * cfg.T * cfg.H + 4 * cfg.T * cfg.H) / (ms * 1e-3) / 1e9
+            r.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
+        else:
+            tf = cfg.flops() / (ms * 1e-3) / 1e12
+            r.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        res[name] = r
+        log("%s: %s" % (name, r))
+        del w
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, host, budget_s):
     import oracle
 
@@ -172,8 +290,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--single-stream", action="store_true", help="run the shared expert on the main stream")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="run the shared expert on a second stream, overlapping the routed experts (by default it "
+                         "runs on the main stream: at the GLM-5 shapes the overlap slows the routed GEMMs as much as "
+                         "it hides)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the GLM-4.7-Flash, block, routing-override and dense-MLP measurements")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=float, default=None, metavar="GIB",
                     help="time a plain device-to-device copy of this many GiB (HBM ceiling, and the known-size "
@@ -219,7 +342,7 @@ def main():
     dev_w = {n: to_dev_bf16(a, device) for n, a in host_w.items()}
     torch.cuda.synchronize()
     log("weights ready in %.1f s" % (time.perf_counter() - t0))
-    two = not args.single_stream
+    two = args.two_streams
 
     results = {}
     plan = ((cfg_p, args.steps), (cfg_d, args.decode_steps))
@@ -272,8 +395,12 @@ def main():
                    "active_experts": act_d, "stages_ms": st_d,
                    "gate_up_roofline": {"bound": "hbm", "achieved": dec_gu_gbs, "peak": PEAK_HBM_GBS,
                                         "unit": "GB/s", "frac": dec_gu_gbs / PEAK_HBM_GBS}},
+        "next": None,
         "cpu_baseline": None,
     }
+    if not args.no_next:
+        line["next"] = bench_next(m, wl, dev_w, host_w, device, max(3, args.steps // 2),
+                                  max(10, args.decode_steps // 4), args.warmup)
     if not args.no_cpu_baseline:
         host = dict(host_tp)
         host.update(host_w)
