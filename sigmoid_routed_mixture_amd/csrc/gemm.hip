@@ -42,11 +42,12 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
     }
     if (mtile >= a.ntiles[0]) return false;
     const int2 t = a.tiles[mtile];
-    if (t.x < 0 || t.x >= a.groups || t.y < 0) return false;
-    ti.g = t.x;
+    const int g = t.x & 0xFFFF, ht = t.x >> 16;
+    if (g >= a.groups || ht <= 0 || ht > BM || t.y < 0) return false;
+    ti.g = g;
     ti.m0 = t.y;
-    ti.off = a.offsets[t.x];
-    ti.rows = min(BM, a.counts[t.x] - t.y);
+    ti.off = a.offsets[g];
+    ti.rows = min(ht, a.counts[g] - t.y);
     return ti.rows > 0;
 }
 
@@ -60,10 +61,11 @@ __device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_
     const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
     if (L < 0) return false;
     const int2 entry = a.tiles[L / ntn];
-    if (entry.x < 0 || entry.x >= a.groups || entry.y < 0) return false;
-    const int m = (a.counts[entry.x] + BM - 1) / BM;
+    const int g = entry.x & 0xFFFF, ht = entry.x >> 16;
+    if (g >= a.groups || ht <= 0 || ht > BM || entry.y < 0) return false;
+    const int m = (a.counts[g] + ht - 1) / ht;
     if (m <= 0) return false;
-    mtile = expert_major_tile(L, ntn, entry.y / BM, m, ntile);
+    mtile = expert_major_tile(L, ntn, entry.y / ht, m, ntile);
     return true;
 }
 
@@ -118,7 +120,8 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // use is over); at its end it stores X(s + 1) into LDS buffer (s + 1) % 2, whose last reader was step
 // s - 1, and a barrier publishes it. Loads past the end re-read the last chunk (in bounds, unused); the
 // scheduling barrier keeps each step's loads ahead of its MFMAs.
-// Only NB of the token blocks (the ones holding valid rows, rounded up to a compiled count) are computed.
+// Only NB of the token blocks (the ones holding valid rows, rounded up to a compiled count: any even
+// count at BM 256, a power of two at BM 128) are computed.
 template <GemmKind KIND, bool DENSE, int BM, int NB>
 __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti, int split, int col0,
                                           const uint16_t* const (&wsrc)[2],
@@ -323,12 +326,18 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
 
     const int nbj = (ti.rows + 15) >> 4;
     if constexpr (BM == kTallBM) {
-        if (nbj > 12)
+        if (nbj > 14)
             wide_tile<KIND, DENSE, BM, 16>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 8)
+        else if (nbj > 12)
+            wide_tile<KIND, DENSE, BM, 14>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 10)
             wide_tile<KIND, DENSE, BM, 12>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 4)
+        else if (nbj > 8)
+            wide_tile<KIND, DENSE, BM, 10>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 6)
             wide_tile<KIND, DENSE, BM, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        else if (nbj > 4)
+            wide_tile<KIND, DENSE, BM, 6>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
         else if (nbj > 2)
             wide_tile<KIND, DENSE, BM, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
         else if (nbj > 1)

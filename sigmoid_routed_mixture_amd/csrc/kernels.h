@@ -36,7 +36,7 @@ struct GemmArgs {
     void* out;                 // [rows, N]: bf16 (h or per-slot outputs) or fp32
     const int32_t* counts;     // rows per group, or null for one dense group
     const int32_t* offsets;    // first row of each group
-    const int2* tiles;         // {group, first row in group} per tile
+    const int2* tiles;         // {group | tile height << 16, first row in group} per tile
     const int32_t* ntiles;     // number of valid tiles
     int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped

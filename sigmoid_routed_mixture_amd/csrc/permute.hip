@@ -2,7 +2,8 @@
 // within each expert (a stable counting sort). Work is split in chunks of 256 tokens: each chunk builds
 // an LDS bit matrix (expert x token-in-chunk), whose popcounts give the chunk's per-expert histogram and,
 // below a token's bit, that token's rank inside the chunk. One workgroup then turns the histograms into
-// per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles.
+// per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles
+// ({expert | tile height << 16, first row}).
 // Pages: the routed experts receive (hidden, indices, weights) (nnterp encyclopedia glm_moe_dsa, support():
 // expert_indices and expert_weights are the experts' inputs); grouping rows by expert is how this build
 // hands each expert its tokens.
@@ -82,10 +83,11 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     if (e < E) offsets[e] = off;
     if (e == 0) offsets[E] = total;
     if (tiles == nullptr) return;
-    const int nt = (e < E && BM > 0) ? (n + BM - 1) / BM : 0;
+    const int ht = tile_height(n, BM);
+    const int nt = (e < E && BM > 0) ? (n + ht - 1) / ht : 0;
     int tiles_total = 0;
     const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e, i * BM);
+    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e | (ht << 16), i * ht);
     if (e == 0) ntiles[0] = tiles_total;
 }
 
@@ -141,10 +143,11 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
     }
     if (tid == 0) offsets[E] = total;
     if (tiles != nullptr) {
-        const int nt = (tid < E && BM > 0) ? (n + BM - 1) / BM : 0;
+        const int ht = tile_height(n, BM);
+        const int nt = (tid < E && BM > 0) ? (n + ht - 1) / ht : 0;
         int tiles_total = 0;
         const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid, i * BM);
+        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid | (ht << 16), i * ht);
         if (tid == 0) ntiles[0] = tiles_total;
     }
     __syncthreads();

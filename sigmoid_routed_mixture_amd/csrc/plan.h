@@ -45,6 +45,17 @@ GemmPath gemm_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);
 
+// Height of the tiles an expert with n rows is cut into (the last tile may be shorter). With 256-token
+// tiles the rows are split evenly over ceil(n / 256) tiles, rounded up to 32 rows: an expert's tiles then
+// compute the same number of 16-row blocks, run in step and share its weights in L2. Other heights cut
+// at BM. The tile count is ceil(n / height) <= ceil(n / BM).
+constexpr int tile_height(int n, int BM) {
+    if (BM != kTallBM || n <= 0) return BM;
+    const int nt = (n + BM - 1) / BM;
+    const int h = ((n + nt - 1) / nt + 31) / 32 * 32;
+    return h < BM ? h : BM;
+}
+
 // Workgroup order of the LDS-tiled grouped GEMM (pure arithmetic, also used by the kernel).
 // The hardware hands workgroup b to XCD b % kXcds and each XCD has its own L2, so the `live` blocks are
 // put in one order and XCD x takes the x-th contiguous chunk of it. Returns the block's position L in

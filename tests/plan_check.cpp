@@ -92,8 +92,11 @@ int main() {
         const bool skew = trial % 3 == 0;
         for (int t = 0; t < T * k; ++t) counts[skew ? (int)(next() % 4) % E : (int)(next() % E)]++;
         std::vector<std::pair<int, int>> tiles; // {expert, first row}
-        for (int e = 0; e < E; ++e)
-            for (int r = 0; r < counts[e]; r += BM) tiles.push_back({e, r});
+        std::vector<int> height(E);
+        for (int e = 0; e < E; ++e) {
+            height[e] = moe::tile_height(counts[e], BM);
+            for (int r = 0; r < counts[e]; r += height[e]) tiles.push_back({e, r});
+        }
         const int64_t live = (int64_t)tiles.size() * ntn;
         int64_t grid = moe::max_tiles(T, E, k, BM) * ntn;
         CHECK(grid >= live, "grid %lld < live %lld", (long long)grid, (long long)live);
@@ -108,9 +111,10 @@ int main() {
             hi[x] = std::max(hi[x], L);
             ++cnt[x];
             const auto entry = tiles[L / ntn];
-            const int m = (counts[entry.first] + BM - 1) / BM;
+            const int ht = height[entry.first];
+            const int m = (counts[entry.first] + ht - 1) / ht;
             int nt = -1;
-            const int64_t mt = moe::expert_major_tile(L, ntn, entry.second / BM, m, nt);
+            const int64_t mt = moe::expert_major_tile(L, ntn, entry.second / ht, m, nt);
             CHECK(mt >= 0 && mt < (int64_t)tiles.size() && tiles[mt].first == entry.first,
                   "block %lld: tile %lld outside expert %d", (long long)b, (long long)mt, entry.first);
             CHECK(nt >= 0 && nt < ntn, "block %lld: column tile %d of %d", (long long)b, nt, ntn);
@@ -122,6 +126,23 @@ int main() {
         ++orders;
     }
     std::printf("%d block orders checked\n", orders);
+
+    // tile heights: at most BM, never more tiles than ceil(n / BM), no empty last tile; at 256 rows the
+    // height is a multiple of 32 (an even number of 16-row blocks) and the last tile is shorter by less
+    // than 32 rows per tile
+    for (int BM : {moe::kSkinnyBM, moe::kWideBM, moe::kTallBM})
+        for (int n = 1; n <= 40000; n += (n < 3000 ? 1 : 97)) {
+            const int ht = moe::tile_height(n, BM);
+            const int nt = (n + ht - 1) / ht;
+            CHECK(ht > 0 && ht <= BM && nt <= (n + BM - 1) / BM && (nt - 1) * ht < n, "n=%d BM=%d ht=%d", n, BM, ht);
+            if (BM == moe::kTallBM) {
+                CHECK(ht % 32 == 0, "n=%d height %d", n, ht);
+                const int last = n - (nt - 1) * ht;
+                CHECK(nt == 1 || ht - last < 32 * nt, "n=%d uneven tiles (height %d, last %d)", n, ht, last);
+            } else {
+                CHECK(ht == BM, "n=%d BM=%d height %d", n, BM, ht);
+            }
+        }
 
     // split dense GEMMs on the weight-streaming kernel: every K range is non-empty and the partial region
     // holds both GEMMs' partials; a forward layout with a shared expert holds them too
