@@ -120,8 +120,8 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // use is over); at its end it stores X(s + 1) into LDS buffer (s + 1) % 2, whose last reader was step
 // s - 1, and a barrier publishes it. Loads past the end re-read the last chunk (in bounds, unused); the
 // scheduling barrier keeps each step's loads ahead of its MFMAs.
-// Only NB of the token blocks (the ones holding valid rows, rounded up to a compiled count: any even
-// count at BM 256, a power of two at BM 128) are computed.
+// Only NB of the token blocks (the ones holding valid rows, rounded up to a compiled count: any count at
+// BM 128, an even one at BM 256, a power of two for dense tiles) are computed.
 template <GemmKind KIND, bool DENSE, int BM, int NB>
 __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti, int split, int col0,
                                           const uint16_t* const (&wsrc)[2],
@@ -325,35 +325,38 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
     for (int q = 0; q < XQ; ++q) xsrc[q] = act_row<KIND, DENSE>(a, ti, (tid >> 3) + 64 * q) + lc * 8;
 
     const int nbj = (ti.rows + 15) >> 4;
-    if constexpr (BM == kTallBM) {
-        if (nbj > 14)
-            wide_tile<KIND, DENSE, BM, 16>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 12)
-            wide_tile<KIND, DENSE, BM, 14>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 10)
-            wide_tile<KIND, DENSE, BM, 12>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 8)
-            wide_tile<KIND, DENSE, BM, 10>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 6)
-            wide_tile<KIND, DENSE, BM, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 4)
-            wide_tile<KIND, DENSE, BM, 6>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 2)
-            wide_tile<KIND, DENSE, BM, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 1)
-            wide_tile<KIND, DENSE, BM, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else
-            wide_tile<KIND, DENSE, BM, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+#define MOE_WIDE_TILE(NBV) wide_tile<KIND, DENSE, BM, NBV>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1)
+    if constexpr (DENSE) {
+        // dense tiles are full but for the last: power-of-two block counts
+        if (nbj > BM / 32) MOE_WIDE_TILE(BM / 16);
+        else if (nbj > 4) MOE_WIDE_TILE(8);
+        else if (nbj > 2) MOE_WIDE_TILE(4);
+        else if (nbj > 1) MOE_WIDE_TILE(2);
+        else MOE_WIDE_TILE(1);
+    } else if constexpr (BM == kTallBM) {
+        // tile heights are multiples of 32 rows: even block counts (a shorter last tile rounds up)
+        if (nbj > 14) MOE_WIDE_TILE(16);
+        else if (nbj > 12) MOE_WIDE_TILE(14);
+        else if (nbj > 10) MOE_WIDE_TILE(12);
+        else if (nbj > 8) MOE_WIDE_TILE(10);
+        else if (nbj > 6) MOE_WIDE_TILE(8);
+        else if (nbj > 4) MOE_WIDE_TILE(6);
+        else if (nbj > 2) MOE_WIDE_TILE(4);
+        else if (nbj > 1) MOE_WIDE_TILE(2);
+        else MOE_WIDE_TILE(1);
     } else {
-        if (nbj > 4)
-            wide_tile<KIND, DENSE, BM, 8>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 2)
-            wide_tile<KIND, DENSE, BM, 4>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else if (nbj > 1)
-            wide_tile<KIND, DENSE, BM, 2>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
-        else
-            wide_tile<KIND, DENSE, BM, 1>(a, ti, split, col0, wsrc, xsrc, kbeg, kend, xs0, xs1);
+        switch (nbj) {
+        case 1: MOE_WIDE_TILE(1); break;
+        case 2: MOE_WIDE_TILE(2); break;
+        case 3: MOE_WIDE_TILE(3); break;
+        case 4: MOE_WIDE_TILE(4); break;
+        case 5: MOE_WIDE_TILE(5); break;
+        case 6: MOE_WIDE_TILE(6); break;
+        case 7: MOE_WIDE_TILE(7); break;
+        default: MOE_WIDE_TILE(8); break;
+        }
     }
+#undef MOE_WIDE_TILE
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -45,14 +45,16 @@ GemmPath gemm_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);
 
-// Height of the tiles an expert with n rows is cut into (the last tile may be shorter). With 256-token
-// tiles the rows are split evenly over ceil(n / 256) tiles, rounded up to 32 rows: an expert's tiles then
-// compute the same number of 16-row blocks, run in step and share its weights in L2. Other heights cut
-// at BM. The tile count is ceil(n / height) <= ceil(n / BM).
+// Height of the tiles an expert with n rows is cut into (the last tile may be shorter). For the LDS-tiled
+// kernel the rows are split evenly over ceil(n / BM) tiles, rounded up to 16 rows (BM 128) or 32 rows
+// (BM 256, whose kernel is compiled for even block counts): an expert's tiles then compute about the same
+// number of 16-row blocks, run in step and share its weights in L2. The 16-row kernel cuts at BM. The tile
+// count is ceil(n / height) <= ceil(n / BM).
 constexpr int tile_height(int n, int BM) {
-    if (BM != kTallBM || n <= 0) return BM;
+    if ((BM != kTallBM && BM != kWideBM) || n <= 0) return BM;
+    const int q = BM == kTallBM ? 32 : 16;
     const int nt = (n + BM - 1) / BM;
-    const int h = ((n + nt - 1) / nt + 31) / 32 * 32;
+    const int h = ((n + nt - 1) / nt + q - 1) / q * q;
     return h < BM ? h : BM;
 }
 

@@ -127,18 +127,18 @@ int main() {
     }
     std::printf("%d block orders checked\n", orders);
 
-    // tile heights: at most BM, never more tiles than ceil(n / BM), no empty last tile; at 256 rows the
-    // height is a multiple of 32 (an even number of 16-row blocks) and the last tile is shorter by less
-    // than 32 rows per tile
+    // tile heights: at most BM, never more tiles than ceil(n / BM), no empty last tile; for the LDS-tiled
+    // kernel a multiple of 16 rows (128) or 32 rows (256), the last tile shorter by less than that per tile
     for (int BM : {moe::kSkinnyBM, moe::kWideBM, moe::kTallBM})
         for (int n = 1; n <= 40000; n += (n < 3000 ? 1 : 97)) {
             const int ht = moe::tile_height(n, BM);
             const int nt = (n + ht - 1) / ht;
             CHECK(ht > 0 && ht <= BM && nt <= (n + BM - 1) / BM && (nt - 1) * ht < n, "n=%d BM=%d ht=%d", n, BM, ht);
-            if (BM == moe::kTallBM) {
-                CHECK(ht % 32 == 0, "n=%d height %d", n, ht);
+            if (BM != moe::kSkinnyBM) {
+                const int q = BM == moe::kTallBM ? 32 : 16;
+                CHECK(ht % q == 0, "n=%d BM=%d height %d", n, BM, ht);
                 const int last = n - (nt - 1) * ht;
-                CHECK(nt == 1 || ht - last < 32 * nt, "n=%d uneven tiles (height %d, last %d)", n, ht, last);
+                CHECK(nt == 1 || ht - last < q * nt, "n=%d BM=%d uneven tiles (height %d, last %d)", n, BM, ht, last);
             } else {
                 CHECK(ht == BM, "n=%d BM=%d height %d", n, BM, ht);
             }
