@@ -166,13 +166,15 @@ def time_call(fn, steps, warmup):
 
 
 def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
-    """The entry points around the mixture, each on its own workload: the GLM-4.7-Flash layer (decode and
-    prefill), the block (RMSNorm + mixture + residual) and the routing override at the GLM-5 shapes, and
-    the dense SwiGLU MLP of the dense-first blocks."""
+    """The other workloads and the entry points around the mixture, each timed on its own: tiny, mid and
+    skewed, the GLM-4.7-Flash layer (decode and prefill), the block (RMSNorm + mixture + residual) and the
+    routing override at the GLM-5 shapes, and the dense SwiGLU MLP of the dense-first blocks. Every mixture
+    entry reports both the MFMA and the HBM fraction."""
     import torch
 
     res = {}
     s1 = None  # shared expert on the main stream, as in the main measurement
+    cfg_glm5_H = wl.BY_NAME["glm5_decode"].H
 
     def layer_inputs(cfg, w):
         host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
@@ -198,13 +200,23 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
         ms = time_call(fwd, nsteps, warmup)
         active = int((counts.cpu().numpy() > 0).sum())
         r = {"T": T, "ms": ms, "tokens_per_s": T / (ms * 1e-3), "active_experts": active}
-        if T <= 64:
-            gbs = layer_bytes(cfg, active) / (ms * 1e-3) / 1e9
-            r.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
-        else:
-            tf = cfg.flops() / (ms * 1e-3) / 1e12
-            r.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        gbs = layer_bytes(cfg, active) / (ms * 1e-3) / 1e9
+        tf = cfg.flops() / (ms * 1e-3) / 1e12
+        r.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS, tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
         return r, fwd, (out, ids, gates, ws, w)
+
+    # the other workloads of the measurement table: tiny (latency), mid (GLM-4.7-Flash shape at scale 1.0,
+    # near the ridge: both fractions), skewed (32768 tokens, expert 0 takes every token)
+    for name, n in (("tiny", decode_steps), ("mid", steps), ("glm5_skewed", max(2, steps // 2))):
+        cfg = wl.BY_NAME[name]
+        if cfg.H == cfg_glm5_H and cfg.E == 256:
+            w = dev_w
+        else:
+            w = {k: to_dev_bf16(wl.weight(cfg, k), device) for k in WEIGHT_NAMES}
+        res[name], _, _ = mixture(cfg, layer_inputs(cfg, w), n)
+        log("%s: %s" % (name, res[name]))
+        del w
+    torch.cuda.empty_cache()
 
     # GLM-4.7-Flash layer (H 2048, 64 experts top-4, I = Is = 1536, scale 1.8)
     c47d, c47p = wl.BY_NAME["glm47_decode"], wl.BY_NAME["glm47_prefill"]

@@ -199,6 +199,41 @@ def test_identical_tokens_one_giant_group(moe, monkeypatch, path):
     compare_out(out, np.repeat(ref["out"], cfg.T, axis=0), "same")
 
 
+@pytest.mark.parametrize("name", ["tiny", "glm5_decode", "mid"])
+def test_graph_capture_replays_match_eager(moe, name):
+    """The library neither allocates nor synchronises, so a forward pass can be captured in a HIP graph:
+    every replay, with eager work and synchronisations between them, gives the eager bytes."""
+    say("[graph capture] %s" % name)
+    cfg, h, d = case(name)
+    T = cfg.T
+    out = torch.empty(T, cfg.H, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.Is), dtype=torch.uint8, device="cuda")
+    args = (d["x"], d["wr"], d["b"], d["w1"], d["w3"], d["w2"], d["ws1"], d["ws3"], d["ws2"], cfg.k, cfg.scale, out, ws,
+            ids, gates)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            moe.moe_forward(*args, stream=s)
+    torch.cuda.synchronize()
+    eager, eager_ids = out.clone(), ids.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_forward(*args, stream=s)
+    torch.cuda.synchronize()
+    other = run_forward(moe, cfg, d, T=max(1, T // 2))[0]
+    for i in range(3):
+        out.fill_(float("nan"))
+        ids.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d differs" % i
+        assert torch.equal(ids, eager_ids), "replay %d routed differently" % i
+        assert np.array_equal(run_forward(moe, cfg, d, T=max(1, T // 2))[0], other)  # eager work in between
+
+
 def test_zero_tokens_and_errors(moe):
     say("[zero tokens / errors]")
     cfg, h, d = case("tiny")
