@@ -4,8 +4,9 @@
 A step is one pass of the whole layer (router, top-k and gates, permutation, SwiGLU routed experts, shared
 expert, combine) over one batch of seeded synthetic tokens already resident in HBM. The default workload
 is the GLM-5-shape prefill (T = 8192 tokens, H 6144, 256 experts top-8, I = Is = 2048, scale 2.5); the
-GLM-5 decode step (T = 16) is measured in the same run and reported under "decode". The shared expert runs on
-the main stream unless --two-streams is given.
+GLM-5 decode step (T = 16) is measured in the same run and reported under "decode". At decode the shared expert
+(Is = I) runs as one more group of the routed experts' grouped GEMMs; at prefill as a dense MLP on the main
+stream unless --two-streams is given.
 
 Prints one JSON line. `value` is prefill tokens/s. `next` holds the entry points around the mixture, each
 timed on its own workload after the main measurement: the GLM-4.7-Flash layer, the block pass (RMSNorm +
@@ -133,8 +134,18 @@ def measured_traffic():
         return None
 
 
+def shared_folded(cfg):
+    """The shared expert runs as one more group of the routed GEMMs when it has the routed width and the
+    layer takes the weight-streaming path (at most 16 routed rows per expert on average)."""
+    return cfg.Is > 0 and cfg.Is == cfg.I and cfg.T * cfg.k <= 16 * cfg.E
+
+
+def gate_up_rows(cfg):
+    return cfg.T * cfg.k + (cfg.T if shared_folded(cfg) else 0)
+
+
 def gate_up_flops(cfg):
-    return 4 * cfg.T * cfg.k * cfg.H * cfg.I
+    return 4 * gate_up_rows(cfg) * cfg.H * cfg.I
 
 
 def layer_bytes(cfg, active):
@@ -145,8 +156,10 @@ def layer_bytes(cfg, active):
 
 
 def gate_up_bytes(cfg, active):
-    """Algorithmic bytes of one routed gate/up launch: W1 and W3 of the active experts, x once, h written."""
-    return active * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * cfg.T * cfg.k * cfg.I
+    """Algorithmic bytes of one grouped gate/up launch: W1 and W3 of the active experts (and Ws1, Ws3 when
+    the shared expert is folded in), x once, h written."""
+    groups = active + (1 if shared_folded(cfg) else 0)
+    return groups * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * gate_up_rows(cfg) * cfg.I
 
 
 def time_call(fn, steps, warmup):
@@ -303,9 +316,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--two-streams", action="store_true",
-                    help="run the shared expert on a second stream, overlapping the routed experts (by default it "
-                         "runs on the main stream: at the GLM-5 shapes the overlap slows the routed GEMMs as much as "
-                         "it hides)")
+                    help="run the shared expert on a second stream, overlapping the routed experts, where it is a "
+                         "dense MLP of its own (prefill; by default it runs on the main stream: at the GLM-5 shapes "
+                         "the overlap slows the routed GEMMs as much as it hides)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the GLM-4.7-Flash, block, routing-override and dense-MLP measurements")
@@ -395,7 +408,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg_p.name, "T": cfg_p.T, "H": cfg_p.H, "E": cfg_p.E, "k": cfg_p.k, "I": cfg_p.I,
                    "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none"},
-        "roofline": {"bound": "mfma", "kernel": "routed gate/up SwiGLU grouped GEMM", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "gate/up SwiGLU grouped GEMM (routed experts%s)"
+                     % (" + shared expert" if shared_folded(cfg_p) else ""), "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(), "launch_ms": gu_ms,
                      "algorithmic_bytes": gate_up_bytes(cfg_p, act_p)},

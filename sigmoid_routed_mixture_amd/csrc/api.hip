@@ -216,12 +216,17 @@ moe_status forward_impl(const Request& q) {
     int32_t* ntiles = static_cast<int32_t*>(at(L.ntiles));
     uint16_t* h_perm = static_cast<uint16_t*>(at(L.h_perm));
     float* y_perm = static_cast<float*>(at(L.y_perm));
-    uint16_t* h_sh = Is > 0 ? static_cast<uint16_t*>(at(L.h_sh)) : nullptr;
-    float* y_sh = Is > 0 ? static_cast<float*>(at(L.y_sh)) : nullptr;
+    // The shared expert: one more group of the routed GEMMs (rows T * k onwards of h_perm and y_perm) when
+    // it has the routed width, else a dense MLP of its own.
+    const bool fold = moe::shared_fold(T, E, k, I, Is);
+    const bool dense_shared = Is > 0 && !fold;
+    uint16_t* h_sh = dense_shared ? static_cast<uint16_t*>(at(L.h_sh)) : nullptr;
+    float* y_sh = dense_shared ? static_cast<float*>(at(L.y_sh)) : nullptr;
+    if (fold) y_sh = y_perm + (size_t)T * k * H;
 
     hipStream_t s0 = static_cast<hipStream_t>(q.stream);
     hipStream_t s1 = static_cast<hipStream_t>(q.stream_shared);
-    const bool two_streams = Is > 0 && s1 != nullptr && s1 != s0;
+    const bool two_streams = dense_shared && s1 != nullptr && s1 != s0;
     DeviceEvents* ev = nullptr;
     if (two_streams) MOE_TRY(device_events(&ev));
 
@@ -248,20 +253,27 @@ moe_status forward_impl(const Request& q) {
     }
     MOE_TRY(mark(1));
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, s0),
+                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, s0),
             "permute");
     MOE_TRY(mark(2));
     // The shared expert needs no routing: with a second stream it forks here, after the router and the
     // permutation (so it cannot delay them), and overlaps the routed experts.
     if (two_streams) MOE_TRY(order_after(s1, s0, ev->fork));
-    if (Is > 0) {
+    if (dense_shared) {
         hipStream_t ss = two_streams ? s1 : s0;
         float* part = L.sh_partial != size_t(-1) ? static_cast<float*>(at(L.sh_partial)) : nullptr;
         MOE_TRY(dense_mlp(path, xin, q.ws1, q.ws3, q.ws2, T, H, Is, h_sh, y_sh, part, ss, "shared"));
     }
     MOE_TRY(mark(3));
 
-    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM);
+    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (fold ? moe::shared_tiles(T, BM) : 0);
+    auto add_shared = [&](moe::GemmArgs& a, const moe_bf16* wa, const moe_bf16* wb) {
+        if (!fold) return;
+        a.ws_a = wa;
+        a.ws_b = wb;
+        a.shared_rows = T;
+        a.shared_off = T * k;
+    };
     moe::GemmArgs r1{};
     r1.act = xin;
     r1.row_token = row_token;
@@ -275,6 +287,7 @@ moe_status forward_impl(const Request& q) {
     r1.groups = E;
     r1.N = I;
     r1.K = H;
+    add_shared(r1, q.ws1, q.ws3);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
@@ -288,6 +301,7 @@ moe_status forward_impl(const Request& q) {
     r2.groups = E;
     r2.N = H;
     r2.K = I;
+    add_shared(r2, q.ws2, nullptr);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
@@ -397,7 +411,7 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
     if (T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     MOE_HIP(moe::launch_permute(topk_ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(workspace), nullptr, nullptr, 0, s),
+                                static_cast<int32_t*>(workspace), nullptr, nullptr, 0, 0, s),
             "permute");
     if (x_perm) MOE_HIP(moe::launch_gather_rows(x, row_token, offsets, E, T, H, T * k, x_perm, s), "gather rows");
     return MOE_OK;

@@ -29,7 +29,19 @@ constexpr int kBK = 64;
 
 struct TileInfo {
     int g, m0, rows, off;
+    bool shared; // the folded shared expert (group index == groups)
 };
+
+// Row n of a group's weights: routed experts from w ([groups][N][K]), the folded shared expert from ws.
+__device__ __forceinline__ const uint16_t* weight_row(const uint16_t* w, const uint16_t* ws, const TileInfo& ti,
+                                                      int N, int n, int K) {
+    return ti.shared ? ws + (size_t)n * K : w + ((size_t)ti.g * N + n) * K;
+}
+
+// Rows of group g: the routed counts, or all shared_rows tokens for the folded shared expert.
+__device__ __forceinline__ int group_rows(const GemmArgs& a, int g) {
+    return g < a.groups ? a.counts[g] : a.shared_rows;
+}
 
 template <bool DENSE, int BM>
 __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, TileInfo& ti) {
@@ -38,16 +50,19 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
         ti.m0 = (int)(mtile * BM);
         ti.off = 0;
         ti.rows = min(BM, a.dense_rows - ti.m0);
+        ti.shared = false;
         return ti.rows > 0;
     }
     if (mtile >= a.ntiles[0]) return false;
     const int2 t = a.tiles[mtile];
     const int g = t.x & 0xFFFF, ht = t.x >> 16;
-    if (g >= a.groups || ht <= 0 || ht > BM || t.y < 0) return false;
+    const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
+    if (g >= ngroups || ht <= 0 || ht > BM || t.y < 0) return false;
     ti.g = g;
     ti.m0 = t.y;
-    ti.off = a.offsets[g];
-    ti.rows = min(ht, a.counts[g] - t.y);
+    ti.shared = g == a.groups;
+    ti.off = ti.shared ? a.shared_off : a.offsets[g];
+    ti.rows = min(ht, group_rows(a, g) - t.y);
     return ti.rows > 0;
 }
 
@@ -62,8 +77,9 @@ __device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_
     if (L < 0) return false;
     const int2 entry = a.tiles[L / ntn];
     const int g = entry.x & 0xFFFF, ht = entry.x >> 16;
-    if (g >= a.groups || ht <= 0 || ht > BM || entry.y < 0) return false;
-    const int m = (a.counts[g] + ht - 1) / ht;
+    const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
+    if (g >= ngroups || ht <= 0 || ht > BM || entry.y < 0) return false;
+    const int m = (group_rows(a, g) + ht - 1) / ht;
     if (m <= 0) return false;
     mtile = expert_major_tile(L, ntn, entry.y / ht, m, ntile);
     return true;
@@ -75,7 +91,8 @@ template <GemmKind KIND, bool DENSE>
 __device__ __forceinline__ const uint16_t* act_row(const GemmArgs& a, const TileInfo& ti, int m) {
     m = m < ti.rows ? m : ti.rows - 1;
     const int r = ti.off + ti.m0 + m;
-    if (KIND == GemmKind::GateUp && !DENSE) return a.act + (size_t)a.row_token[r] * a.K;
+    if (KIND == GemmKind::GateUp && !DENSE)
+        return a.act + (size_t)(ti.shared ? ti.m0 + m : a.row_token[r]) * a.K; // the shared group takes every token
     return a.act + (size_t)r * a.K;
 }
 
@@ -308,15 +325,15 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
         col0 = ntile * (kWBN / 2) + wave * 16;
         int n = col0 + rl;
         n = n < N ? n : N - 1;
-        wsrc[0] = a.w_a + ((size_t)ti.g * N + n) * K + kg * 16;
-        wsrc[1] = a.w_b + ((size_t)ti.g * N + n) * K + kg * 16;
+        wsrc[0] = weight_row(a.w_a, a.ws_a, ti, N, n, K) + kg * 16;
+        wsrc[1] = weight_row(a.w_b, a.ws_b, ti, N, n, K) + kg * 16;
     } else {
         col0 = ntile * kWBN + wave * kWaveRows;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int n = col0 + i * 16 + rl;
             n = n < N ? n : N - 1;
-            wsrc[i] = a.w_a + ((size_t)ti.g * N + n) * K + kg * 16;
+            wsrc[i] = weight_row(a.w_a, a.ws_a, ti, N, n, K) + kg * 16;
         }
     }
     const int lc = tid & 7;
@@ -390,16 +407,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn, i
     int col0;
     if (KIND == GemmKind::GateUp) {
         col0 = ntile * 64 + wave * 16;
-        const size_t rowoff = ((size_t)ti.g * N + col0 + rl) * K + kg * 16;
-        wsrc[0] = a.w_a + rowoff;
-        wsrc[1] = a.w_b + rowoff;
+        wsrc[0] = weight_row(a.w_a, a.ws_a, ti, N, col0 + rl, K) + kg * 16;
+        wsrc[1] = weight_row(a.w_b, a.ws_b, ti, N, col0 + rl, K) + kg * 16;
     } else {
         col0 = ntile * 128 + wave * 32;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             int n = col0 + b * 16 + rl;
             n = n < N ? n : N - 1;
-            wsrc[b] = a.w_a + ((size_t)ti.g * N + n) * K + kg * 16;
+            wsrc[b] = weight_row(a.w_a, a.ws_a, ti, N, n, K) + kg * 16;
         }
     }
     const uint16_t* xsrc = act_row<KIND, DENSE>(a, ti, rl) + kg * 16;

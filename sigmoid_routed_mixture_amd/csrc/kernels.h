@@ -19,9 +19,10 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // Permutation: per-chunk expert histograms, the prefix sums (and, when `tiles` is non-null, the list of
 // BM-row grouped-GEMM tiles), then the stable scatter of slots into expert-contiguous rows.
 // chunk_scratch holds ceil(T / 256) * E ints.
+// With shared_rows > 0 the tile list ends with the folded shared expert's tiles (group E).
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
-                          int32_t* ntiles, int BM, hipStream_t stream);
+                          int32_t* ntiles, int BM, int shared_rows, hipStream_t stream);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E].
 hipError_t launch_gather_rows(const uint16_t* x, const int32_t* row_token, const int32_t* offsets, int E, int T,
@@ -41,6 +42,10 @@ struct GemmArgs {
     int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped
     int N, K;                  // output width (gate/up: I, h columns), reduction length
+    const uint16_t* ws_a;      // grouped: the folded shared expert's weights (group `groups`), [N][K]: Ws1 / Ws2
+    const uint16_t* ws_b;      // gate/up: Ws3
+    int shared_rows;           // grouped: tokens of the folded shared expert (0: none), taken in token order
+    int shared_off;            // its first row in the permuted buffers (T * k)
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
 };

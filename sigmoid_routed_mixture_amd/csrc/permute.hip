@@ -62,10 +62,23 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
     return incl - v;
 }
 
+// Appends the folded shared expert's tiles (group E, all shared_rows tokens) after the routed ones.
+__device__ __forceinline__ void append_shared_tiles(int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                    int routed_tiles, int E, int shared_rows, int BM) {
+    const int tid = threadIdx.x;
+    int ns = 0;
+    if (shared_rows > 0) {
+        const int hs = tile_height(shared_rows, BM);
+        ns = (shared_rows + hs - 1) / hs;
+        for (int i = tid; i < ns; i += 256) tiles[routed_tiles + i] = make_int2(E | (hs << 16), i * hs);
+    }
+    if (tid == 0) ntiles[0] = routed_tiles + ns;
+}
+
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int chunks, int E,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int BM) {
+                                                        int BM, int shared_rows) {
     __shared__ int sh[256];
     const int e = threadIdx.x;
     int n = 0;
@@ -88,7 +101,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     int tiles_total = 0;
     const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
     for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e | (ht << 16), i * ht);
-    if (e == 0) ntiles[0] = tiles_total;
+    append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                          int BM, int32_t* __restrict__ row_token,
+                                                          int BM, int shared_rows, int32_t* __restrict__ row_token,
                                                           int32_t* __restrict__ slot_row) {
     __shared__ uint32_t mask[kMaxE][8];
     __shared__ int sh[256];
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         int tiles_total = 0;
         const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
         for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid | (ht << 16), i * ht);
-        if (tid == 0) ntiles[0] = tiles_total;
+        append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
     }
     __syncthreads();
     const int t = tid;
@@ -192,17 +205,18 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
-                          int32_t* ntiles, int BM, hipStream_t stream) {
+                          int32_t* ntiles, int BM, int shared_rows, hipStream_t stream) {
     const int chunks = (T + kChunk - 1) / kChunk;
     if (chunks == 1) {
-        perm_single_kernel<<<1, 256, 0, stream>>>(ids, T, E, k, counts, offsets, tiles, ntiles, BM, row_token,
-                                                  slot_row);
+        perm_single_kernel<<<1, 256, 0, stream>>>(ids, T, E, k, counts, offsets, tiles, ntiles, BM, shared_rows,
+                                                  row_token, slot_row);
         return hipGetLastError();
     }
     perm_count_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, chunk_scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    perm_scan_kernel<<<1, 256, 0, stream>>>(chunk_scratch, chunks, E, counts, offsets, tiles, ntiles, BM);
+    perm_scan_kernel<<<1, 256, 0, stream>>>(chunk_scratch, chunks, E, counts, offsets, tiles, ntiles, BM,
+                                            shared_rows);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scatter_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, offsets, chunk_scratch, row_token, slot_row);

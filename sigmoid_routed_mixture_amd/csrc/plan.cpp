@@ -76,15 +76,20 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     L.row_token = take(Tk * 4);
     L.slot_row = take(Tk * 4);
     L.chunk_base = take(chunks * (size_t)E * 4);
-    // room for the longest tile list either grouped-GEMM kernel can ask for (the smallest BM)
-    L.tiles = take((size_t)max_tiles(T, E, k, std::min(std::min(kWideBM, kTallBM), kSkinnyBM)) * 8);
+    // room for the longest tile list any grouped-GEMM kernel can ask for (the smallest BM), with the
+    // shared expert's tiles when it is folded in
+    const int bm_min = std::min(std::min(kWideBM, kTallBM), kSkinnyBM);
+    const bool fold = shared_fold(T, E, k, I, Is);
+    L.tiles = take((size_t)(max_tiles(T, E, k, bm_min) + (fold ? shared_tiles(T, bm_min) : 0)) * 8);
     L.ntiles = take(4);
     L.partial = take((size_t)router_splits(T, H, E) * (size_t)T * (size_t)E * 4);
-    L.h_perm = take(Tk * (size_t)I * 2);
-    L.y_perm = take(Tk * (size_t)H * 4);
-    L.h_sh = Is > 0 ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
-    L.y_sh = Is > 0 ? take((size_t)T * (size_t)H * 4) : size_t(-1);
-    const size_t shp = Is > 0 ? dense_partial_bytes(T, H, Is) : 0;
+    const size_t rows = Tk + (fold ? (size_t)T : 0);
+    L.h_perm = take(rows * (size_t)I * 2);
+    L.y_perm = take(rows * (size_t)H * 4);
+    const bool dense_shared = Is > 0 && !fold;
+    L.h_sh = dense_shared ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
+    L.y_sh = dense_shared ? take((size_t)T * (size_t)H * 4) : size_t(-1);
+    const size_t shp = dense_shared ? dense_partial_bytes(T, H, Is) : 0;
     L.sh_partial = shp > 0 ? take(shp) : size_t(-1);
     L.x_norm = with_norm ? take((size_t)T * (size_t)H * 2) : size_t(-1);
     L.total = off;

@@ -79,6 +79,15 @@ constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile
     return first + r % m;
 }
 
+// On the weight-streaming path (few tokens per expert) the shared expert joins the routed experts' grouped
+// GEMMs as one more group (index E, all T tokens, its rows after the T * k routed rows) when it has the
+// routed experts' width: its weights then stream with theirs in one launch. Otherwise it runs as two dense
+// GEMMs of its own (with many tokens the dense tile order reuses its weights better than one more group).
+inline bool shared_fold(int T, int E, int k, int I, int Is) {
+    return Is > 0 && Is == I && gemm_path(T, E, k) == GemmPath::Skinny;
+}
+constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
+
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
     size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,

@@ -33,7 +33,7 @@ int main() {
                 for (int k : ks) {
                     if (k > E) continue;
                     for (int I : Is_)
-                        for (int Is : {0, I}) {
+                        for (int Is : {0, I, 2 * I}) {
                             if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) continue;
                             ++n;
                             const moe::Layout L = moe::forward_layout(T, H, E, k, I, Is, true);
@@ -42,9 +42,16 @@ int main() {
                                   "the norm region must only extend the plain layout");
                             const size_t Tk = (size_t)T * k;
                             const size_t chunks = ((size_t)T + moe::kPermChunk - 1) / moe::kPermChunk;
-                            const size_t tiles_need = (size_t)std::max(moe::max_tiles(T, E, k, moe::kSkinnyBM),
-                                                                       std::max(moe::max_tiles(T, E, k, moe::kWideBM),
-                                                                                moe::max_tiles(T, E, k, moe::kTallBM))) * 8;
+                            // the shared expert with the routed width is one more group of the routed GEMMs:
+                            // T more rows in h_perm / y_perm and its tiles after the routed ones
+                            const bool fold = moe::shared_fold(T, E, k, I, Is);
+                            CHECK(fold == (Is == I && moe::gemm_path(T, E, k) == moe::GemmPath::Skinny),
+                                  "fold T=%d E=%d k=%d I=%d Is=%d", T, E, k, I, Is);
+                            const size_t rows = Tk + (fold ? (size_t)T : 0);
+                            size_t tiles_need = 0;
+                            for (int BM : {moe::kSkinnyBM, moe::kWideBM, moe::kTallBM})
+                                tiles_need = std::max(tiles_need, (size_t)(moe::max_tiles(T, E, k, BM) +
+                                                                           (fold ? moe::shared_tiles(T, BM) : 0)) * 8);
                             struct R { size_t off, need; const char* name; };
                             std::vector<R> rs = {
                                 {L.ids, Tk * 4, "ids"}, {L.gates, Tk * 4, "gates"}, {L.counts, (size_t)E * 4, "counts"},
@@ -52,8 +59,10 @@ int main() {
                                 {L.slot_row, Tk * 4, "slot_row"}, {L.chunk_base, chunks * E * 4, "chunk_base"},
                                 {L.tiles, tiles_need, "tiles"}, {L.ntiles, 4, "ntiles"},
                                 {L.partial, (size_t)moe::router_splits(T, H, E) * T * E * 4, "partial"},
-                                {L.h_perm, Tk * I * 2, "h_perm"}, {L.y_perm, Tk * H * 4, "y_perm"}};
-                            if (Is > 0) {
+                                {L.h_perm, rows * I * 2, "h_perm"}, {L.y_perm, rows * H * 4, "y_perm"}};
+                            CHECK(fold == (L.h_sh == size_t(-1) && L.y_sh == size_t(-1) && Is > 0),
+                                  "dense shared buffers only without the fold (I=%d Is=%d)", I, Is);
+                            if (Is > 0 && !fold) {
                                 rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
                                 rs.push_back({L.y_sh, (size_t)T * H * 4, "y_sh"});
                             }
@@ -88,17 +97,20 @@ int main() {
         const int T = (int)(next() % 2000);
         const int ntn = 1 + (int)(next() % 40);
         const int BM = trial % 2 ? moe::kWideBM : moe::kTallBM;
-        std::vector<int> counts(E, 0);
+        // every other trial with a folded shared expert: group E, all T tokens, its tiles last
+        const bool shared = trial % 4 < 2;
+        std::vector<int> counts(E + 1, 0);
         const bool skew = trial % 3 == 0;
         for (int t = 0; t < T * k; ++t) counts[skew ? (int)(next() % 4) % E : (int)(next() % E)]++;
+        counts[E] = shared ? T : 0;
         std::vector<std::pair<int, int>> tiles; // {expert, first row}
-        std::vector<int> height(E);
-        for (int e = 0; e < E; ++e) {
+        std::vector<int> height(E + 1);
+        for (int e = 0; e <= E; ++e) {
             height[e] = moe::tile_height(counts[e], BM);
             for (int r = 0; r < counts[e]; r += height[e]) tiles.push_back({e, r});
         }
         const int64_t live = (int64_t)tiles.size() * ntn;
-        int64_t grid = moe::max_tiles(T, E, k, BM) * ntn;
+        int64_t grid = (moe::max_tiles(T, E, k, BM) + (shared ? moe::shared_tiles(T, BM) : 0)) * ntn;
         CHECK(grid >= live, "grid %lld < live %lld", (long long)grid, (long long)live);
         grid = (grid + moe::kXcds - 1) / moe::kXcds * moe::kXcds;
         std::vector<int> seen(live, 0);
@@ -160,7 +172,7 @@ int main() {
                                              s2 > 1 ? (size_t)s2 * T * H * 4 : 0);
                 CHECK(moe::dense_partial_bytes(T, H, Id) >= need, "partials T=%d H=%d I=%d", T, H, Id);
                 CHECK(moe::dense_workspace_bytes(T, H, Id) >= (size_t)T * Id * 2 + need, "dense workspace");
-                const moe::Layout L = moe::forward_layout(T, H, 8, 2, 64, Id);
+                const moe::Layout L = moe::forward_layout(T, H, 8, 2, Id == 64 ? 128 : 64, Id);
                 CHECK(need == 0 || (L.sh_partial != size_t(-1) && L.x_norm == size_t(-1) &&
                                     L.total >= L.sh_partial + need),
                       "shared partials T=%d H=%d Is=%d", T, H, Id);

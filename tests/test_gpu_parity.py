@@ -138,6 +138,21 @@ def test_second_stream_and_determinism(moe, name):
         assert np.array_equal(x, y)
 
 
+def test_second_stream_with_dense_shared_expert(moe):
+    # Is != I: the shared expert runs as a dense MLP of its own, on the second stream when one is given
+    say("[streams] Is != I")
+    cfg = wl.MoEConfig(52, "dense_shared", T=1000, H=256, E=32, k=2, I=128, Is=320, scale=2.5)
+    h = config_host(cfg)
+    d = to_device(h)
+    a = run_forward(moe, cfg, d)
+    b = run_forward(moe, cfg, d, stream_shared=torch.cuda.Stream())
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(0, cfg.T, 5))
+    same, _, _ = compare_routing(a[1][::5], a[2][::5], ref, "dense_shared")
+    compare_out(a[0][::5][same], ref["out"][same], "dense_shared")
+
+
 def test_crafted_ties_on_gpu(moe):
     path = os.path.join(os.path.dirname(__file__), "golden", "tie_cases.json")
     cases = json.load(open(path))["cases"]
