@@ -75,14 +75,19 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
     return MOE_OK;
 }
 
-// Test knob: MOE_GEMM_PATH=wide|tall|skinny forces one grouped-GEMM kernel for every size (all are exact
-// implementations of the same GEMMs; the default picks by rows per expert).
-moe::GemmPath pick_path(int T, int E, int k) {
+// Test knob: MOE_GEMM_PATH=wide|tall|dma|skinny forces one grouped-GEMM kernel for every size (all are
+// exact implementations of the same GEMMs; the default picks by rows per expert). The Dma kernel is used
+// only when every operand fits its 32-bit offsets: x [T, H], h [T k + T, I] and [T, Is], the weights.
+moe::GemmPath pick_path(int T, int E, int k, int H, int I, int Is) {
+    const bool fits = moe::dma_fits(T, H) && moe::dma_fits((int64_t)T * k + T, I) && moe::dma_fits(T, Is) &&
+                      moe::dma_fits(I, H) && moe::dma_fits(H, I) && moe::dma_fits(Is, H) && moe::dma_fits(H, Is);
     const char* f = std::getenv("MOE_GEMM_PATH");
-    if (f && std::strcmp(f, "wide") == 0) return moe::GemmPath::Wide;
-    if (f && std::strcmp(f, "tall") == 0) return moe::GemmPath::Tall;
-    if (f && std::strcmp(f, "skinny") == 0) return moe::GemmPath::Skinny;
-    return moe::gemm_path(T, E, k);
+    moe::GemmPath p = moe::gemm_path(T, E, k);
+    if (f && std::strcmp(f, "wide") == 0) p = moe::GemmPath::Wide;
+    if (f && std::strcmp(f, "tall") == 0) p = moe::GemmPath::Tall;
+    if (f && std::strcmp(f, "dma") == 0) p = moe::GemmPath::Dma;
+    if (f && std::strcmp(f, "skinny") == 0) p = moe::GemmPath::Skinny;
+    return p == moe::GemmPath::Dma && !fits ? moe::fallback_path(T, E, k) : p;
 }
 
 // A dense SwiGLU MLP (the shared expert, or the dense-first blocks' MLP): gate/up into h, then down into
@@ -230,7 +235,7 @@ moe_status forward_impl(const Request& q) {
     DeviceEvents* ev = nullptr;
     if (two_streams) MOE_TRY(device_events(&ev));
 
-    const moe::GemmPath path = pick_path(T, E, k);
+    const moe::GemmPath path = pick_path(T, E, k, H, I, Is);
     const int BM = moe::path_bm(path);
 
     auto mark = [&](int i) -> moe_status {
@@ -487,7 +492,7 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     if (workspace_bytes < moe::dense_workspace_bytes(T, H, I))
         return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dense_mlp_workspace_bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const moe::GemmPath path = pick_path(T, 1, 1);
+    const moe::GemmPath path = pick_path(T, 1, 1, H, I, 0);
     char* ws = static_cast<char*>(workspace);
     const size_t hbytes = ((size_t)T * (size_t)I * 2 + 255) / 256 * 256;
     float* part = moe::dense_partial_bytes(T, H, I) > 0 ? reinterpret_cast<float*>(ws + hbytes) : nullptr;

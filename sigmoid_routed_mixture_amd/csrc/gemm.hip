@@ -9,15 +9,21 @@
 // Weights are the MFMA A operand (rows = output features) and tokens the B operand (columns), so a lane's
 // four accumulator elements are four consecutive output features of one token row: 8-byte bf16 stores.
 //
-// Two kernels:
+// Three kernels:
+//  * dma    : up to 256 tokens x 256 weight rows per 8-wave workgroup, both operands copied from global
+//             memory straight into LDS (global_load_lds), weights two K steps ahead, tokens one; the
+//             prefill kernel.
 //  * wide   : 128 or 256 tokens x 256 weight rows per 8-wave workgroup. Each wave streams its own 32
 //             weight rows from HBM into MFMA registers; the token tile goes through double-buffered LDS.
-//             The 128-token form also computes the router logits (dense, K split across workgroups).
+//             The router logits (dense, K split across workgroups), and the fallback for operands past
+//             the dma kernel's 32-bit offsets.
 //  * skinny : 16 tokens per tile for experts with few rows (decode). No LDS: each wave streams its own
 //             weight rows straight from HBM with 32-byte loads per lane, two 64-wide K chunks in flight
 //             ahead of its MFMAs, so the kernel runs at the weight-streaming bound.
-// Both take their (expert, first row) tiles from the device-side list the permutation builds; the grid is
+// All take their (expert, first row) tiles from the device-side list the permutation builds; the grid is
 // an upper bound and workgroups past the list's length exit at once.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -377,6 +383,256 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
 }
 
 // ------------------------------------------------------------------------------------------------
+// dma kernel
+
+// Loads into VGPRs reach about 16 B/clk per CU from L2; copies straight into LDS (global_load_lds, 16
+// bytes per lane) about 50. So both operands of a 256 x 256 tile go through LDS this way. Wave
+// (wm = wave % 4, wn = wave / 4) computes 64 weight rows (gate/up: 32 features of W1 and the same 32 of
+// W3) x the token blocks 2 jj + wn, from 16-byte LDS fragments; each accumulator sums its products in
+// the same order as the wide kernel's, so both give the same bits.
+constexpr int kDThreads = 512;
+constexpr int kDRows = 256; // weight rows and token rows per tile
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// LDS layout of both operands: [256 rows][64 k] bf16, 16-byte chunk c of row r at slot c ^ dswz(r) (the
+// wide kernel's swizzle: conflict-free fragment reads).
+__device__ __forceinline__ int dswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <GemmKind KIND, bool DENSE, int NBW>
+__device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, int ntile, uint16_t* ws0,
+                                         uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1) {
+    constexpr int XI = (NBW + 1) / 2; // token load instructions per wave and K step
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rl = lane & 15, kg = lane >> 4;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int K = a.K, N = a.N;
+    const int nk = K / kBK;
+
+    // Load instruction t (8 rows = 1 KB of LDS) of an operand is issued by wave t % 8: 4 weight loads and
+    // XI token loads per wave and step (token rows past the computed blocks are not loaded, but for an odd
+    // instruction's, which clamp to the tile's rows). Lane l fills slot l % 8 of row 8 t + l / 8 with
+    // global chunk (l % 8) ^ dswz(row). Addresses: a wave-uniform base plus a 32-bit per-lane byte offset.
+    const int lr = lane >> 3, ls = lane & 7;
+    const char* wbase0 = reinterpret_cast<const char*>(weight_row(a.w_a, a.ws_a, ti, N, 0, K));
+    const char* wbase1 =
+        KIND == GemmKind::GateUp ? reinterpret_cast<const char*>(weight_row(a.w_b, a.ws_b, ti, N, 0, K)) : wbase0;
+    const char* xbase = reinterpret_cast<const char*>(a.act);
+    uint32_t woff[4], xoff[XI];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 8 * (wave + 8 * q) + lr;
+        // gate/up: LDS weight rows 0..127 are W1 rows (instructions 0..15), 128..255 the same W3 rows
+        int n = KIND == GemmKind::GateUp ? ntile * 128 + (r & 127) : ntile * 256 + r;
+        n = n < N ? n : N - 1;
+        woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(ls ^ dswz(r)) * 16u;
+    }
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+        const int r = 8 * (wave + 8 * q) + lr;
+        xoff[q] = (uint32_t)(reinterpret_cast<const char*>(act_row<KIND, DENSE>(a, ti, r)) - xbase) +
+                  (uint32_t)(ls ^ dswz(r)) * 16u;
+    }
+    auto load_x = [&](uint16_t* xl, int st) {
+#pragma unroll
+        for (int q = 0; q < XI; ++q)
+            __builtin_amdgcn_global_load_lds((gptr_t)(xbase + 2 * st * kBK + xoff[q]),
+                                             (lptr_t)(xl + 8 * (wave + 8 * q) * kBK), 16, 0, 0);
+    };
+    auto load_w = [&](uint16_t* wl, int st) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const char* wb = (KIND == GemmKind::GateUp && q >= 2 ? wbase1 : wbase0) + 2 * st * kBK;
+            __builtin_amdgcn_global_load_lds((gptr_t)(wb + woff[q]), (lptr_t)(wl + 8 * (wave + 8 * q) * kBK), 16,
+                                             0, 0);
+        }
+    };
+
+    // fragments: block bases are multiples of 16 rows, so the swizzle depends on the lane only
+    auto arow = [&](int i) {
+        if (KIND == GemmKind::GateUp) return (i < 2 ? 0 : 128) + 32 * wm + 16 * (i & 1);
+        return 64 * wm + 16 * i;
+    };
+    auto brow = [&](int jj) { return 16 * (2 * jj + wn); };
+    const int lo0 = rl * kBK + (((2 * kg) ^ dswz(rl)) << 3), lo1 = rl * kBK + (((2 * kg + 1) ^ dswz(rl)) << 3);
+    auto frag = [&](const uint16_t* l, int row0, int h) { return load16(&l[row0 * kBK + (h ? lo1 : lo0)]); };
+
+    f32x4 acc[4][NBW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Pack16 f0a[4], f0b[NBW], f1a[4], f1b[NBW]; // fragments of the two K halves of a step
+    auto read = [&](Pack16 (&fa)[4], Pack16 (&fb)[NBW], const uint16_t* wl, const uint16_t* xl, int h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = frag(wl, arow(i), h);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) fb[j] = frag(xl, brow(j), h);
+    };
+    auto mma = [&](const Pack16 (&fa)[4], const Pack16 (&fb)[NBW]) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    };
+    // the fragment reads of one half spread evenly among the other half's MFMAs
+    auto interleave = [&]() {
+        constexpr int R = 4 + NBW, M = 4 * NBW, Q = M / R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, Q, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, M - Q * R, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Pipeline. Weights go into a ring of three LDS buffers (step s in ws[s % 3]), tokens into two
+    // (xs[s % 2]). Step s: read the second-half fragments of step s, MFMAs of its first half; then the
+    // barrier that opens step s + 1: each wave first waits until at most its 4 youngest loads (the
+    // weights of step s + 2) are in flight, so after the barrier step s + 1 is in LDS for everyone and
+    // nobody reads step s's buffers any more; the tokens of step s + 2 and the weights of step s + 3 go
+    // into those buffers; then the MFMAs of step s's second half, with the first-half fragments of step
+    // s + 1 read among them. Weights are thus loaded two steps ahead, tokens one. CHECKED steps (the last
+    // eight) skip loads and reads past the last step and wait for all loads where no weights are younger.
+    auto step = [&](auto checked, uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, int s) {
+        constexpr bool C = decltype(checked)::value;
+        read(f1a, f1b, wc, xc, 1);
+        mma(f0a, f0b);
+        interleave();
+        if (!C || s + 1 < nk) {
+            if (!C || s + 2 < nk)
+                __builtin_amdgcn_s_waitcnt(0x0074); // vmcnt(4) lgkmcnt(0)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            if (!C || s + 2 < nk) load_x(xc, s + 2);
+            if (!C || s + 3 < nk) load_w(wc, s + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            read(f0a, f0b, wn1, xn1, 0);
+        }
+        mma(f1a, f1b);
+        interleave();
+    };
+    using unchecked = std::false_type;
+    using checked = std::true_type;
+    load_x(xs0, 0);
+    load_w(ws0, 0);
+    if (nk > 1) {
+        load_w(ws1, 1);
+        __builtin_amdgcn_s_waitcnt(0x0074); // vmcnt(4) lgkmcnt(0)
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
+    }
+    __builtin_amdgcn_s_barrier();
+    if (nk > 1) load_x(xs1, 1);
+    if (nk > 2) load_w(ws2, 2);
+    read(f0a, f0b, ws0, xs0, 0);
+    // six steps per iteration (weight buffers cycle with period 3, token buffers with 2) while every load
+    // of the iteration is in range; then up to eight checked steps
+    int s = 0;
+    for (; s + 9 <= nk; s += 6) {
+        step(unchecked{}, ws0, xs0, ws1, xs1, s);
+        step(unchecked{}, ws1, xs1, ws2, xs0, s + 1);
+        step(unchecked{}, ws2, xs0, ws0, xs1, s + 2);
+        step(unchecked{}, ws0, xs1, ws1, xs0, s + 3);
+        step(unchecked{}, ws1, xs0, ws2, xs1, s + 4);
+        step(unchecked{}, ws2, xs1, ws0, xs0, s + 5);
+    }
+    if (s < nk) step(checked{}, ws0, xs0, ws1, xs1, s);
+    if (s + 1 < nk) step(checked{}, ws1, xs1, ws2, xs0, s + 1);
+    if (s + 2 < nk) step(checked{}, ws2, xs0, ws0, xs1, s + 2);
+    if (s + 3 < nk) step(checked{}, ws0, xs1, ws1, xs0, s + 3);
+    if (s + 4 < nk) step(checked{}, ws1, xs0, ws2, xs1, s + 4);
+    if (s + 5 < nk) step(checked{}, ws2, xs1, ws0, xs0, s + 5);
+    if (s + 6 < nk) step(checked{}, ws0, xs0, ws1, xs1, s + 6);
+    if (s + 7 < nk) step(checked{}, ws1, xs1, ws2, xs0, s + 7);
+    __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
+
+    // epilogue: lane holds features 4 kg + r of weight block i and token rl of token block 2 jj + wn
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int m = 16 * (2 * j + wn) + rl;
+        if (m >= ti.rows) continue;
+        const size_t row = (size_t)ti.off + ti.m0 + m;
+        if (KIND == GemmKind::GateUp) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int col = ntile * 128 + 32 * wm + 16 * i + 4 * kg;
+                if (col >= N) continue;
+                const f32x4 g = acc[i][j], u = acc[i + 2][j];
+                uint2 v;
+                v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+                v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = ntile * 256 + 64 * wm + 16 * i + 4 * kg;
+                if (col >= N) continue;
+                const f32x4 y = acc[i][j];
+                if (KIND == GemmKind::Down) {
+                    uint2 v;
+                    v.x = pack_bf16x2(y[0], y[1]);
+                    v.y = pack_bf16x2(y[2], y[3]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                } else {
+                    float* o = static_cast<float*>(a.out) + row * N + col;
+                    if (col + 3 < N) {
+                        *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (col + r < N) o[r] = y[r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <GemmKind KIND, bool DENSE>
+__global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
+    const int64_t bid = blockIdx.x;
+    int ntile;
+    int64_t mtile;
+    if (DENSE) {
+        ntile = (int)(bid % ntn);
+        mtile = bid / ntn;
+    } else if (!grouped_block<kDRows>(a, ntn, bid, mtile, ntile)) {
+        return;
+    }
+    TileInfo ti;
+    if (!tile_info<DENSE, kDRows>(a, mtile, ti)) return;
+
+    // 160 KB: three weight buffers and two token buffers of [256][64] bf16
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws2[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[kDRows * kBK];
+
+    // 16-row token blocks per wave: tiles up to 256 rows, 32 per pair of token waves
+    const int nb = (ti.rows + 31) >> 5;
+#define MOE_DMA_TILE(NBV) dma_tile<KIND, DENSE, NBV>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1)
+    switch (nb) {
+    case 1: MOE_DMA_TILE(1); break;
+    case 2: MOE_DMA_TILE(2); break;
+    case 3: MOE_DMA_TILE(3); break;
+    case 4: MOE_DMA_TILE(4); break;
+    case 5: MOE_DMA_TILE(5); break;
+    case 6: MOE_DMA_TILE(6); break;
+    case 7: MOE_DMA_TILE(7); break;
+    default: MOE_DMA_TILE(8); break;
+    }
+#undef MOE_DMA_TILE
+}
+
+// ------------------------------------------------------------------------------------------------
 // skinny kernel
 
 constexpr int kSBM = kSkinnyBM; // tokens per tile
@@ -562,7 +818,9 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         if (path != GemmPath::Wide) return hipErrorInvalidValue;
         gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
     } else {
-        if (path == GemmPath::Wide)
+        if (path == GemmPath::Dma)
+            gemm_dma_kernel<KIND, DENSE><<<grid, kDThreads, 0, stream>>>(a, ntn);
+        else if (path == GemmPath::Wide)
             gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
         else if (path == GemmPath::Tall)
             gemm_wide_kernel<KIND, DENSE, kTallBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);

@@ -50,6 +50,11 @@ int router_splits(int T, int H, int E) {
 
 GemmPath gemm_path(int T, int E, int k) {
     const int64_t slots = (int64_t)T * k;
+    return slots <= (int64_t)kSkinnyBM * E ? GemmPath::Skinny : GemmPath::Dma;
+}
+
+GemmPath fallback_path(int T, int E, int k) {
+    const int64_t slots = (int64_t)T * k;
     if (slots <= (int64_t)kSkinnyBM * E) return GemmPath::Skinny;
     return slots < (int64_t)192 * E ? GemmPath::Wide : GemmPath::Tall;
 }

@@ -20,8 +20,16 @@ constexpr int kMaxE = 256;
 constexpr int kMaxK = 32;
 constexpr int kMaxDenseSplits = 16; // K ranges of a dense GEMM on the weight-streaming kernel
 
-enum class GemmPath { Wide, Tall, Skinny };
-constexpr int path_bm(GemmPath p) { return p == GemmPath::Tall ? kTallBM : p == GemmPath::Wide ? kWideBM : kSkinnyBM; }
+// Grouped-GEMM kernels: Dma (256-token tiles, both operands loaded straight into LDS), Wide and Tall (128-
+// and 256-token tiles, weights streamed through registers: the fallback when an operand is too large for
+// Dma's 32-bit offsets, and Wide for the router logits), Skinny (16-token tiles, decode).
+enum class GemmPath { Wide, Tall, Dma, Skinny };
+constexpr int path_bm(GemmPath p) {
+    return p == GemmPath::Tall || p == GemmPath::Dma ? kTallBM : p == GemmPath::Wide ? kWideBM : kSkinnyBM;
+}
+// The Dma kernel addresses each operand as a 32-bit byte offset from a base: a matrix of `rows` rows of K
+// bf16 must stay below 4 GiB.
+constexpr bool dma_fits(int64_t rows, int64_t K) { return rows * K * 2 < (int64_t(1) << 32); }
 
 struct Check {
     moe_status status = MOE_OK;
@@ -42,6 +50,8 @@ int router_splits(int T, int H, int E);
 // Weight-streaming kernel when experts average at most 16 rows, the LDS-tiled one with 128-token tiles
 // below 192 rows on average, and with 256-token tiles from there (it loads a third fewer bytes per FLOP).
 GemmPath gemm_path(int T, int E, int k);
+// The register-streaming kernel for the same tiles when an operand does not fit the Dma kernel.
+GemmPath fallback_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);
 

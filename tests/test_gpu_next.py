@@ -255,7 +255,7 @@ def test_dense_mlp_parity(moe, name):
     compare_out(out[rows], ref, name)
 
 
-@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 @pytest.mark.parametrize("T", [1, 16, 100])
 def test_dense_mlp_both_kernels_and_ragged(moe, monkeypatch, path, T):
     monkeypatch.setenv("MOE_GEMM_PATH", path)

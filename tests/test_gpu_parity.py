@@ -113,7 +113,7 @@ def test_forward_parity(moe, name):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("glm5_decode", 16), ("mid", 384)])
-@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
     say("[gemm path %s] %s T=%d" % (path, name, T))
     monkeypatch.setenv("MOE_GEMM_PATH", path)
@@ -122,6 +122,19 @@ def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
     ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(T))
     same, _, _ = compare_routing(ids, gates, ref, name)
     compare_out(out[same], ref["out"][same], "%s/%s" % (name, path))
+
+
+@pytest.mark.parametrize("name,T", [("mid", 700), ("glm47_prefill", 2048)])
+def test_dma_kernel_matches_register_kernel_bitwise(moe, monkeypatch, name, T):
+    # the LDS-copy kernel sums every accumulator in the register-streaming kernel's order
+    say("[dma vs tall] %s T=%d" % (name, T))
+    cfg, h, d = case(name)
+    monkeypatch.setenv("MOE_GEMM_PATH", "tall")
+    a = run_forward(moe, cfg, d, T=T)
+    monkeypatch.setenv("MOE_GEMM_PATH", "dma")
+    b = run_forward(moe, cfg, d, T=T)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "mid"])
@@ -180,7 +193,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 @pytest.mark.parametrize("shape", EDGE, ids=[e[-1] for e in EDGE])
 def test_edge_shapes(moe, monkeypatch, shape, path):
     T, H, E, k, I, Is, what = shape
@@ -199,7 +212,7 @@ def test_edge_shapes(moe, monkeypatch, shape, path):
     compare_out(out[same], ref["out"][same], what)
 
 
-@pytest.mark.parametrize("path", ["wide", "tall", "skinny"])
+@pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 def test_identical_tokens_one_giant_group(moe, monkeypatch, path):
     say("[giant group %s]" % path)
     monkeypatch.setenv("MOE_GEMM_PATH", path)
