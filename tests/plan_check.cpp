@@ -178,6 +178,25 @@ int main() {
                       "shared partials T=%d H=%d Is=%d", T, H, Id);
             }
     std::printf("%d dense splits checked\n", dense);
+
+    // the DMA kernel's 32-bit byte offsets: a matrix fits while rows * K * 2 < 2^32, exactly at the edge;
+    // the default path is the DMA kernel or, for few rows per expert, the weight-streaming one, and the
+    // fallback keeps the same tile height
+    CHECK(moe::dma_fits(1, 64) && moe::dma_fits(8192, 6144) && moe::dma_fits(589824, 2048), "dma_fits small");
+    CHECK(moe::dma_fits((int64_t(1) << 31) / 6144, 6144) && !moe::dma_fits((int64_t(1) << 31) / 4096 + 1, 4096) &&
+              moe::dma_fits((int64_t(1) << 31) / 4096, 4096 - 1) && !moe::dma_fits(int64_t(1) << 20, 4096),
+          "dma_fits edge");
+    for (int T : {1, 16, 17, 64, 1000, 8192})
+        for (int E : {1, 16, 64, 256})
+            for (int k : {1, 4, 8}) {
+                if (k > E) continue;
+                const moe::GemmPath p = moe::gemm_path(T, E, k), f = moe::fallback_path(T, E, k);
+                const bool skinny = (int64_t)T * k <= (int64_t)moe::kSkinnyBM * E;
+                CHECK(p == (skinny ? moe::GemmPath::Skinny : moe::GemmPath::Dma), "path T=%d E=%d k=%d", T, E, k);
+                CHECK(skinny ? f == moe::GemmPath::Skinny : (f == moe::GemmPath::Wide || f == moe::GemmPath::Tall),
+                      "fallback T=%d E=%d k=%d", T, E, k);
+                CHECK(moe::path_bm(moe::GemmPath::Dma) == moe::kTallBM, "dma tile height");
+            }
     std::printf("%d layouts checked, %d failures\n", n, fails);
     return fails ? 1 : 0;
 }
