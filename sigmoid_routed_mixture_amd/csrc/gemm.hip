@@ -552,6 +552,34 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     if (s + 7 < nk) step(checked{}, ws1, xs1, ws2, xs0, s + 7);
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
 
+    if constexpr (KIND == GemmKind::DownF32) {
+        // fp32 rows leave through LDS: each wave turns one 16-token block at a time into 16 rows of its 64
+        // features (256 contiguous bytes per row) in a private 4.25 KB area of ws0 / ws1 (row stride 68
+        // floats), then stores whole rows
+        __syncthreads(); // every wave is done reading the operand buffers
+        float* stg = reinterpret_cast<float*>(wave < 4 ? ws0 : ws1) + (wave & 3) * (16 * 68);
+        const int c4 = lane & 15, r4 = lane >> 4;
+        const int colw = ntile * 256 + 64 * wm;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(stg + rl * 68 + 16 * i + 4 * kg) = acc[i][j];
+            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the block is in LDS
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int t = 4 * p + r4;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 68 + 4 * c4);
+                const int m = 16 * (2 * j + wn) + t;
+                const int col = colw + 4 * c4;
+                if (m < ti.rows && col < N)
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next block overwrites the area
+        }
+        return;
+    }
+
     // epilogue: lane holds features 4 kg + r of weight block i and token rl of token block 2 jj + wn
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
