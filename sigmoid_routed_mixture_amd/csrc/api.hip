@@ -257,8 +257,20 @@ moe_status forward_impl(const Request& q) {
                 "router");
     }
     MOE_TRY(mark(1));
+    // the DMA kernel's work-balanced XCD split (computed for both grouped GEMMs, used by the down GEMM)
+    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (fold ? moe::shared_tiles(T, BM) : 0);
+    const char* xs = std::getenv("MOE_XCD_SPLIT"); // test knob: "count" keeps the block-count split
+    const bool balanced = path == moe::GemmPath::Dma && !fold && !(xs && std::strcmp(xs, "count") == 0);
+    moe::XcdSplit split{};
+    if (balanced) {
+        split.bounds = static_cast<int32_t*>(at(L.xcd_bounds));
+        split.ntn[0] = moe::dma_ntn(true, I);
+        split.ntn[1] = moe::dma_ntn(false, H);
+        for (int v = 0; v < 2; ++v) split.cap[v] = (int)moe::dma_xcd_cap(grid_tiles, split.ntn[v]);
+    }
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, s0),
+                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, split,
+                                s0),
             "permute");
     MOE_TRY(mark(2));
     // The shared expert needs no routing: with a second stream it forks here, after the router and the
@@ -271,7 +283,6 @@ moe_status forward_impl(const Request& q) {
     }
     MOE_TRY(mark(3));
 
-    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (fold ? moe::shared_tiles(T, BM) : 0);
     auto add_shared = [&](moe::GemmArgs& a, const moe_bf16* wa, const moe_bf16* wb) {
         if (!fold) return;
         a.ws_a = wa;
@@ -292,6 +303,8 @@ moe_status forward_impl(const Request& q) {
     r1.groups = E;
     r1.N = I;
     r1.K = H;
+    // gate/up keeps the block-count split: its long weight stream makes blocks of any height cost about the
+    // same (the work-balanced split measured 2 % slower there, 2 % faster on the down GEMM)
     add_shared(r1, q.ws1, q.ws3);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     MOE_TRY(mark(4));
@@ -306,6 +319,7 @@ moe_status forward_impl(const Request& q) {
     r2.groups = E;
     r2.N = H;
     r2.K = I;
+    r2.xcd_bounds = balanced ? split.bounds + (moe::kXcds + 1) : nullptr;
     add_shared(r2, q.ws2, nullptr);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
@@ -416,7 +430,7 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
     if (T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     MOE_HIP(moe::launch_permute(topk_ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(workspace), nullptr, nullptr, 0, 0, s),
+                                static_cast<int32_t*>(workspace), nullptr, nullptr, 0, 0, moe::XcdSplit{}, s),
             "permute");
     if (x_perm) MOE_HIP(moe::launch_gather_rows(x, row_token, offsets, E, T, H, T * k, x_perm, s), "gather rows");
     return MOE_OK;

@@ -77,10 +77,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
 // of an expert's weights run side by side on one XCD, and so do the column tiles that share a token
 // tile, so both come from HBM about once instead of once per XCD.
 template <int BM>
-__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
-                                              int& ntile) {
-    const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
-    if (L < 0) return false;
+__device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, int64_t& mtile, int& ntile) {
     const int2 entry = a.tiles[L / ntn];
     const int g = entry.x & 0xFFFF, ht = entry.x >> 16;
     const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
@@ -89,6 +86,25 @@ __device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_
     if (m <= 0) return false;
     mtile = expert_major_tile(L, ntn, entry.y / ht, m, ntile);
     return true;
+}
+
+template <int BM>
+__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
+                                              int& ntile) {
+    const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
+    if (L < 0) return false;
+    return block_at<BM>(a, ntn, L, mtile, ntile);
+}
+
+// The same order with the work-balanced XCD split the permutation wrote: XCD x = bid % kXcds takes the
+// blocks [bounds[x], bounds[x + 1]).
+template <int BM>
+__device__ __forceinline__ bool balanced_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
+                                               int& ntile) {
+    const int x = (int)(bid % kXcds);
+    const int64_t L = a.xcd_bounds[x] + bid / kXcds;
+    if (L >= a.xcd_bounds[x + 1]) return false;
+    return block_at<BM>(a, ntn, L, mtile, ntile);
 }
 
 // Activation row for tile row m (clamped to the tile's last valid row: padded columns of the MFMA tile
@@ -510,6 +526,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
                 __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             if (!C || s + 2 < nk) load_x(xc, s + 2);
+            __builtin_amdgcn_sched_barrier(0); // the weights must be the youngest copies (the vmcnt(4) above)
             if (!C || s + 3 < nk) load_w(wc, s + 3);
             __builtin_amdgcn_sched_barrier(0);
             read(f0a, f0b, wn1, xn1, 0);
@@ -520,6 +537,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     using unchecked = std::false_type;
     using checked = std::true_type;
     load_x(xs0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(ws0, 0);
     if (nk > 1) {
         load_w(ws1, 1);
@@ -529,6 +547,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     }
     __builtin_amdgcn_s_barrier();
     if (nk > 1) load_x(xs1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     if (nk > 2) load_w(ws2, 2);
     read(f0a, f0b, ws0, xs0, 0);
     // six steps per iteration (weight buffers cycle with period 3, token buffers with 2) while every load
@@ -631,7 +650,8 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn
     if (DENSE) {
         ntile = (int)(bid % ntn);
         mtile = bid / ntn;
-    } else if (!grouped_block<kDRows>(a, ntn, bid, mtile, ntile)) {
+    } else if (a.xcd_bounds != nullptr ? !balanced_block<kDRows>(a, ntn, bid, mtile, ntile)
+                                       : !grouped_block<kDRows>(a, ntn, bid, mtile, ntile)) {
         return;
     }
     TileInfo ti;
@@ -840,6 +860,10 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
     if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+    if (path == GemmPath::Dma && !DENSE && a.xcd_bounds != nullptr) {
+        if (ntn != dma_ntn(KIND == GemmKind::GateUp, a.N)) return hipErrorInvalidValue;
+        blocks = kXcds * dma_xcd_cap(grid_tiles, ntn);
+    }
     if (blocks > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     if constexpr (KIND == GemmKind::Logits) {

@@ -19,10 +19,18 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // Permutation: per-chunk expert histograms, the prefix sums (and, when `tiles` is non-null, the list of
 // BM-row grouped-GEMM tiles), then the stable scatter of slots into expert-contiguous rows.
 // chunk_scratch holds ceil(T / 256) * E ints.
-// With shared_rows > 0 the tile list ends with the folded shared expert's tiles (group E).
+// With shared_rows > 0 the tile list ends with the folded shared expert's tiles (group E). With `bounds`
+// (no folded shared expert) it also writes, for the two column-tile counts ntn[0] and ntn[1] of the DMA
+// kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
+// at most cap[i] blocks).
+struct XcdSplit {
+    int32_t* bounds;
+    int ntn[2];
+    int cap[2];
+};
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
-                          int32_t* ntiles, int BM, int shared_rows, hipStream_t stream);
+                          int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split, hipStream_t stream);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E].
 hipError_t launch_gather_rows(const uint16_t* x, const int32_t* row_token, const int32_t* offsets, int E, int T,
@@ -46,6 +54,7 @@ struct GemmArgs {
     const uint16_t* ws_b;      // gate/up: Ws3
     int shared_rows;           // grouped: tokens of the folded shared expert (0: none), taken in token order
     int shared_off;            // its first row in the permuted buffers (T * k)
+    const int32_t* xcd_bounds; // DMA kernel, grouped: the XCD split of the blocks (kXcds + 1 ints), or null
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
 };

@@ -75,10 +75,49 @@ __device__ __forceinline__ void append_shared_tiles(int2* __restrict__ tiles, in
     if (tid == 0) ntiles[0] = routed_tiles + ns;
 }
 
+// The work-balanced XCD split (plan.h) of the tile list just built, for both column-tile counts. Thread e
+// holds expert e's row count n, tile height ht, tile count nt and first tile t0. Each boundary
+// x * total / kXcds (in work units) falls inside one expert and is rounded down to one of its column
+// tiles; thread 0 then clamps the boundaries so no XCD gets more than cap blocks.
+__device__ void xcd_split(const XcdSplit& sp, int E, int n, int ht, int nt, int t0, int tiles_total, int* sh) {
+    __shared__ int raw[2][kXcds + 1];
+    __shared__ int totals[2];
+    const int e = threadIdx.x;
+    int c = 0; // work of one column of expert e's tiles
+    if (e < E)
+        for (int i = 0; i < nt; ++i) c += (min(ht, n - i * ht) + 31) / 32 + kDmaBlockCost;
+    for (int v = 0; v < 2; ++v) {
+        const int ntn = sp.ntn[v];
+        int total = 0;
+        const int w0 = block_exclusive_scan(e < E ? ntn * c : 0, sh, &total);
+        if (e == 0) totals[v] = total;
+        if (e < E && c > 0)
+            for (int x = 1; x < kXcds; ++x) {
+                const int B = (int)((int64_t)x * total / kXcds);
+                if (B >= w0 && B < w0 + ntn * c) raw[v][x] = ntn * t0 + ((B - w0) / c) * nt;
+            }
+    }
+    __syncthreads();
+    if (e == 0)
+        for (int v = 0; v < 2; ++v) {
+            const int live = tiles_total * sp.ntn[v], cap = sp.cap[v];
+            int32_t* b = sp.bounds + v * (kXcds + 1);
+            int prev = 0;
+            b[0] = 0;
+            for (int x = 1; x < kXcds; ++x) {
+                const int lo = max(prev, live - (kXcds - x) * cap), hi = min(prev + cap, live);
+                const int r = totals[v] > 0 ? raw[v][x] : 0;
+                prev = min(max(r, lo), hi);
+                b[x] = prev;
+            }
+            b[kXcds] = live;
+        }
+}
+
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int chunks, int E,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int BM, int shared_rows) {
+                                                        int BM, int shared_rows, XcdSplit split) {
     __shared__ int sh[256];
     const int e = threadIdx.x;
     int n = 0;
@@ -102,6 +141,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
     for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e | (ht << 16), i * ht);
     append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
+    if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -135,7 +175,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                          int BM, int shared_rows, int32_t* __restrict__ row_token,
+                                                          int BM, int shared_rows, XcdSplit split,
+                                                          int32_t* __restrict__ row_token,
                                                           int32_t* __restrict__ slot_row) {
     __shared__ uint32_t mask[kMaxE][8];
     __shared__ int sh[256];
@@ -162,6 +203,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
         for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid | (ht << 16), i * ht);
         append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
+        if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
     }
     __syncthreads();
     const int t = tid;
@@ -205,18 +247,18 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
-                          int32_t* ntiles, int BM, int shared_rows, hipStream_t stream) {
+                          int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split, hipStream_t stream) {
     const int chunks = (T + kChunk - 1) / kChunk;
     if (chunks == 1) {
         perm_single_kernel<<<1, 256, 0, stream>>>(ids, T, E, k, counts, offsets, tiles, ntiles, BM, shared_rows,
-                                                  row_token, slot_row);
+                                                  split, row_token, slot_row);
         return hipGetLastError();
     }
     perm_count_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, chunk_scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scan_kernel<<<1, 256, 0, stream>>>(chunk_scratch, chunks, E, counts, offsets, tiles, ntiles, BM,
-                                            shared_rows);
+                                            shared_rows, split);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scatter_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, offsets, chunk_scratch, row_token, slot_row);

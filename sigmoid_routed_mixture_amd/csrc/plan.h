@@ -89,6 +89,17 @@ constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile
     return first + r % m;
 }
 
+// Work-balanced split of the DMA kernel's grouped blocks over the XCDs: XCD x takes blocks
+// [bounds[x], bounds[x + 1]) of the expert-major order, at most dma_xcd_cap(...) of them (the grid gives
+// each XCD that many workgroups). A block's work is counted as its 32-row token blocks plus
+// kDmaBlockCost for the weight slice every block streams.
+constexpr int kDmaBlockCost = 2;
+constexpr int dma_ntn(bool gate_up, int N) { return gate_up ? (N + 127) / 128 : (N + 255) / 256; }
+constexpr int64_t dma_xcd_cap(int64_t grid_tiles, int ntn) {
+    const int64_t avg = (grid_tiles * ntn + kXcds - 1) / kXcds;
+    return avg + avg / 4 + 1;
+}
+
 // On the weight-streaming path (few tokens per expert) the shared expert joins the routed experts' grouped
 // GEMMs as one more group (index E, all T tokens, its rows after the T * k routed rows) when it has the
 // routed experts' width: its weights then stream with theirs in one launch. Otherwise it runs as two dense
@@ -100,8 +111,8 @@ constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / B
 
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
-    size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, partial, h_perm,
-        y_perm, h_sh, y_sh, sh_partial, x_norm;
+    size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, xcd_bounds, partial,
+        h_perm, y_perm, h_sh, y_sh, sh_partial, x_norm;
     size_t total;
 };
 // with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.

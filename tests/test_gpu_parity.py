@@ -137,6 +137,17 @@ def test_dma_kernel_matches_register_kernel_bitwise(moe, monkeypatch, name, T):
         assert np.array_equal(x, y)
 
 
+def test_xcd_split_does_not_change_results(moe, monkeypatch):
+    # the work-balanced and the block-count XCD split only reorder the same blocks
+    say("[xcd split] mid")
+    cfg, h, d = case("mid")
+    a = run_forward(moe, cfg, d)
+    monkeypatch.setenv("MOE_XCD_SPLIT", "count")
+    b = run_forward(moe, cfg, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "mid"])
 def test_second_stream_and_determinism(moe, name):
     say("[streams] %s" % name)
