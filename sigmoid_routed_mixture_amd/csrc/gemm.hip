@@ -536,19 +536,32 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     };
     using unchecked = std::false_type;
     using checked = std::true_type;
+    // Prologue: every buffer is free at the start of a tile, so steps 0 and 1 (and the weights of step 2)
+    // are requested at once, in the order X0 W0 X1 W1 W2; the barrier that opens step 0 waits for X0 and W0
+    // only (the 4 XI + 8 younger copies may stay in flight), the one that opens step 1 (inside step 0)
+    // for X1 and W1 (W2 may stay in flight), as in every later step.
+    constexpr int V1 = XI + 4, V2 = XI + 8;
+    static_assert(V2 <= 15, "vmcnt immediates below hold 4 bits");
     load_x(xs0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_w(ws0, 0);
-    if (nk > 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk > 2) {
+        load_x(xs1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         load_w(ws1, 1);
-        __builtin_amdgcn_s_waitcnt(0x0074); // vmcnt(4) lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws2, 2);
+        __builtin_amdgcn_s_waitcnt(0x0070 | V2); // vmcnt(XI + 8) lgkmcnt(0)
+    } else if (nk > 1) {
+        load_x(xs1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws1, 1);
+        __builtin_amdgcn_s_waitcnt(0x0070 | V1); // vmcnt(XI + 4) lgkmcnt(0)
     } else {
         __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
     }
     __builtin_amdgcn_s_barrier();
-    if (nk > 1) load_x(xs1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (nk > 2) load_w(ws2, 2);
     read(f0a, f0b, ws0, xs0, 0);
     // six steps per iteration (weight buffers cycle with period 3, token buffers with 2) while every load
     // of the iteration is in range; then up to eight checked steps
