@@ -1,8 +1,8 @@
 // Grouped GEMMs of the SwiGLU experts on gfx950 (bf16 MFMA 16x16x32, fp32 accumulation).
 //
 // Gate/up GEMM: for the rows of one expert, g = x W1^T and u = x W3^T for the same output columns in one
-// workgroup, and the epilogue writes h = silu(g) * u as bf16. Down GEMM: y = h W2^T, written as bf16
-// per-slot rows (routed) or fp32 (shared expert). Pages: open-model-atlas GLM-5 "MoE transformer block",
+// workgroup, and the epilogue writes h = silu(g) * u as bf16. Down GEMM: y = h W2^T, written as fp32 rows
+// (per slot for the routed experts). Pages: open-model-atlas GLM-5 "MoE transformer block",
 // "All 43 steps": g = x W1, u = x W3, a = g sigma(g), h = a * u, E_i = h W2, and the same four steps for
 // the shared expert.
 //
@@ -283,20 +283,13 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
                 const int col = col0 + i * 16 + 4 * kg;
                 if (col >= N) continue;
                 const f32x4 y = acc[i][j];
-                if (KIND == GemmKind::Down) {
-                    uint2 v;
-                    v.x = pack_bf16x2(y[0], y[1]);
-                    v.y = pack_bf16x2(y[2], y[3]);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                float* o = static_cast<float*>(a.out) + (size_t)split * a.dense_rows * N + row * N + col;
+                if (col + 3 < N) {
+                    *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
                 } else {
-                    float* o = static_cast<float*>(a.out) + (size_t)split * a.dense_rows * N + row * N + col;
-                    if (col + 3 < N) {
-                        *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (col + r < N) o[r] = y[r];
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        if (col + r < N) o[r] = y[r];
                 }
             }
         }
@@ -609,16 +602,15 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
             }
             __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next block overwrites the area
         }
-        return;
-    }
-
-    // epilogue: lane holds features 4 kg + r of weight block i and token rl of token block 2 jj + wn
+    } else {
+        // gate/up: lane holds features 4 kg + r of weight blocks i (g) and i + 2 (u), token rl of token
+        // block 2 jj + wn
+        static_assert(KIND == GemmKind::GateUp, "the dma kernel computes gate/up and fp32 down GEMMs");
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        const int m = 16 * (2 * j + wn) + rl;
-        if (m >= ti.rows) continue;
-        const size_t row = (size_t)ti.off + ti.m0 + m;
-        if (KIND == GemmKind::GateUp) {
+        for (int j = 0; j < NBW; ++j) {
+            const int m = 16 * (2 * j + wn) + rl;
+            if (m >= ti.rows) continue;
+            const size_t row = (size_t)ti.off + ti.m0 + m;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int col = ntile * 128 + 32 * wm + 16 * i + 4 * kg;
@@ -628,28 +620,6 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
                 v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
                 v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = ntile * 256 + 64 * wm + 16 * i + 4 * kg;
-                if (col >= N) continue;
-                const f32x4 y = acc[i][j];
-                if (KIND == GemmKind::Down) {
-                    uint2 v;
-                    v.x = pack_bf16x2(y[0], y[1]);
-                    v.y = pack_bf16x2(y[2], y[3]);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
-                } else {
-                    float* o = static_cast<float*>(a.out) + row * N + col;
-                    if (col + 3 < N) {
-                        *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (col + r < N) o[r] = y[r];
-                    }
-                }
             }
         }
     }
@@ -813,15 +783,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn, i
             const int col = col0 + b * 16 + 4 * kg;
             if (col >= N) continue;
             const f32x4 y = acc[b];
-            if (KIND == GemmKind::Down) {
-                uint2 v;
-                v.x = pack_bf16x2(y[0], y[1]);
-                v.y = pack_bf16x2(y[2], y[3]);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
-            } else {
-                *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * N + col) =
-                    make_float4(y[0], y[1], y[2], y[3]);
-            }
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * N + col) = make_float4(y[0], y[1], y[2], y[3]);
         }
     }
 }
@@ -914,9 +876,6 @@ hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t 
     case GemmKind::GateUp:
         return dense ? launch_one<GemmKind::GateUp, true>(path, a, grid_tiles, stream)
                      : launch_one<GemmKind::GateUp, false>(path, a, grid_tiles, stream);
-    case GemmKind::Down:
-        return dense ? launch_one<GemmKind::Down, true>(path, a, grid_tiles, stream)
-                     : launch_one<GemmKind::Down, false>(path, a, grid_tiles, stream);
     case GemmKind::DownF32:
         return dense ? launch_one<GemmKind::DownF32, true>(path, a, grid_tiles, stream)
                      : launch_one<GemmKind::DownF32, false>(path, a, grid_tiles, stream);

@@ -58,7 +58,7 @@ struct GemmArgs {
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
 };
-enum class GemmKind { GateUp, Down, DownF32, Logits };
+enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
 
 // In-order reduction of a split dense GEMM's partials (dense_splits in plan.h) into h (gate/up, bf16 after
