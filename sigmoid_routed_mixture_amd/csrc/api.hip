@@ -75,14 +75,15 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
     return MOE_OK;
 }
 
-// Test knob: MOE_GEMM_PATH=wide|tall|dma|skinny forces one grouped-GEMM kernel for every size (all are
-// exact implementations of the same GEMMs; the default picks by rows per expert). The Dma kernel is used
-// only when every operand fits its 32-bit offsets: x [T, H], h [T k + T, I] and [T, Is], the weights.
-moe::GemmPath pick_path(int T, int E, int k, int H, int I, int Is) {
+// Test knob: MOE_GEMM_PATH=wide|tall|dma|skinny forces one GEMM kernel for every size (all are exact
+// implementations of the same GEMMs; the default is gemm_path for the grouped GEMMs, dense_path for a
+// dense MLP of T rows). The Dma kernel is used only when every operand fits its 32-bit offsets: x [T, H],
+// h [T k + T, I] and [T, Is], the weights.
+moe::GemmPath pick_path(int T, int E, int k, int H, int I, int Is, bool dense = false) {
     const bool fits = moe::dma_fits(T, H) && moe::dma_fits((int64_t)T * k + T, I) && moe::dma_fits(T, Is) &&
                       moe::dma_fits(I, H) && moe::dma_fits(H, I) && moe::dma_fits(Is, H) && moe::dma_fits(H, Is);
     const char* f = std::getenv("MOE_GEMM_PATH");
-    moe::GemmPath p = moe::gemm_path(T, E, k);
+    moe::GemmPath p = dense ? moe::dense_path(T) : moe::gemm_path(T, E, k);
     if (f && std::strcmp(f, "wide") == 0) p = moe::GemmPath::Wide;
     if (f && std::strcmp(f, "tall") == 0) p = moe::GemmPath::Tall;
     if (f && std::strcmp(f, "dma") == 0) p = moe::GemmPath::Dma;
@@ -279,7 +280,8 @@ moe_status forward_impl(const Request& q) {
     if (dense_shared) {
         hipStream_t ss = two_streams ? s1 : s0;
         float* part = L.sh_partial != size_t(-1) ? static_cast<float*>(at(L.sh_partial)) : nullptr;
-        MOE_TRY(dense_mlp(path, xin, q.ws1, q.ws3, q.ws2, T, H, Is, h_sh, y_sh, part, ss, "shared"));
+        const moe::GemmPath spath = pick_path(T, 1, 1, H, Is, 0, true);
+        MOE_TRY(dense_mlp(spath, xin, q.ws1, q.ws3, q.ws2, T, H, Is, h_sh, y_sh, part, ss, "shared"));
     }
     MOE_TRY(mark(3));
 
@@ -506,7 +508,7 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     if (workspace_bytes < moe::dense_workspace_bytes(T, H, I))
         return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_dense_mlp_workspace_bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const moe::GemmPath path = pick_path(T, 1, 1, H, I, 0);
+    const moe::GemmPath path = pick_path(T, 1, 1, H, I, 0, true);
     char* ws = static_cast<char*>(workspace);
     const size_t hbytes = ((size_t)T * (size_t)I * 2 + 255) / 256 * 256;
     float* part = moe::dense_partial_bytes(T, H, I) > 0 ? reinterpret_cast<float*>(ws + hbytes) : nullptr;

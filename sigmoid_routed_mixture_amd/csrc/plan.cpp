@@ -48,10 +48,9 @@ int router_splits(int T, int H, int E) {
     return (int)s;
 }
 
-GemmPath gemm_path(int T, int E, int k) {
-    const int64_t slots = (int64_t)T * k;
-    return slots <= (int64_t)kSkinnyBM * E ? GemmPath::Skinny : GemmPath::Dma;
-}
+GemmPath gemm_path(int, int, int) { return GemmPath::Dma; }
+
+GemmPath dense_path(int T) { return T <= kSkinnyBM ? GemmPath::Skinny : GemmPath::Dma; }
 
 GemmPath fallback_path(int T, int E, int k) {
     const int64_t slots = (int64_t)T * k;

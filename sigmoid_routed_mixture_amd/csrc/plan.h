@@ -47,10 +47,15 @@ Check check_aligned(const void* p, const char* name, size_t align = 16);
 constexpr int kRouterSmallT = 16;
 constexpr int kRouterMaxSplits = 64;
 int router_splits(int T, int H, int E);
-// Weight-streaming kernel when experts average at most 16 rows, the LDS-tiled one with 128-token tiles
-// below 192 rows on average, and with 256-token tiles from there (it loads a third fewer bytes per FLOP).
+// Grouped GEMMs take the Dma kernel at every size (measured faster than the weight-streaming kernel from
+// one token to 512 at the GLM-5 and GLM-4.7-Flash shapes, decode included).
 GemmPath gemm_path(int T, int E, int k);
-// The register-streaming kernel for the same tiles when an operand does not fit the Dma kernel.
+// A dense GEMM of T rows (shared expert, dense MLP): the weight-streaming kernel with split K up to 16 rows
+// (one token tile cannot fill the GPU otherwise), else the Dma kernel.
+GemmPath dense_path(int T);
+// When an operand does not fit the Dma kernel: the weight-streaming kernel when experts average at most 16
+// rows, else the register-streaming one with 128-token tiles below 192 rows on average and 256-token
+// tiles from there.
 GemmPath fallback_path(int T, int E, int k);
 // Upper bound of grouped-GEMM tiles of BM rows over all experts: sum_e ceil(n_e / BM).
 int64_t max_tiles(int T, int E, int k, int BM);
@@ -100,12 +105,12 @@ constexpr int64_t dma_xcd_cap(int64_t grid_tiles, int ntn) {
     return avg + avg / 4 + 1;
 }
 
-// On the weight-streaming path (few tokens per expert) the shared expert joins the routed experts' grouped
+// With few tokens per expert (at most 16 on average) the shared expert joins the routed experts' grouped
 // GEMMs as one more group (index E, all T tokens, its rows after the T * k routed rows) when it has the
 // routed experts' width: its weights then stream with theirs in one launch. Otherwise it runs as two dense
 // GEMMs of its own (with many tokens the dense tile order reuses its weights better than one more group).
-inline bool shared_fold(int T, int E, int k, int I, int Is) {
-    return Is > 0 && Is == I && gemm_path(T, E, k) == GemmPath::Skinny;
+constexpr bool shared_fold(int T, int E, int k, int I, int Is) {
+    return Is > 0 && Is == I && (int64_t)T * k <= (int64_t)kSkinnyBM * E;
 }
 constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
 

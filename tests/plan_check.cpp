@@ -45,7 +45,7 @@ int main() {
                             // the shared expert with the routed width is one more group of the routed GEMMs:
                             // T more rows in h_perm / y_perm and its tiles after the routed ones
                             const bool fold = moe::shared_fold(T, E, k, I, Is);
-                            CHECK(fold == (Is == I && moe::gemm_path(T, E, k) == moe::GemmPath::Skinny),
+                            CHECK(fold == (Is == I && (int64_t)T * k <= (int64_t)moe::kSkinnyBM * E),
                                   "fold T=%d E=%d k=%d I=%d Is=%d", T, E, k, I, Is);
                             const size_t rows = Tk + (fold ? (size_t)T : 0);
                             size_t tiles_need = 0;
@@ -180,8 +180,8 @@ int main() {
     std::printf("%d dense splits checked\n", dense);
 
     // the DMA kernel's 32-bit byte offsets: a matrix fits while rows * K * 2 < 2^32, exactly at the edge;
-    // the default path is the DMA kernel or, for few rows per expert, the weight-streaming one, and the
-    // fallback keeps the same tile height
+    // the grouped GEMMs default to the DMA kernel, dense ones of up to 16 rows to the weight-streaming
+    // kernel; the fallback picks by rows per expert
     CHECK(moe::dma_fits(1, 64) && moe::dma_fits(8192, 6144) && moe::dma_fits(589824, 2048), "dma_fits small");
     CHECK(moe::dma_fits((int64_t(1) << 31) / 6144, 6144) && !moe::dma_fits((int64_t(1) << 31) / 4096 + 1, 4096) &&
               moe::dma_fits((int64_t(1) << 31) / 4096, 4096 - 1) && !moe::dma_fits(int64_t(1) << 20, 4096),
@@ -192,7 +192,9 @@ int main() {
                 if (k > E) continue;
                 const moe::GemmPath p = moe::gemm_path(T, E, k), f = moe::fallback_path(T, E, k);
                 const bool skinny = (int64_t)T * k <= (int64_t)moe::kSkinnyBM * E;
-                CHECK(p == (skinny ? moe::GemmPath::Skinny : moe::GemmPath::Dma), "path T=%d E=%d k=%d", T, E, k);
+                CHECK(p == moe::GemmPath::Dma, "path T=%d E=%d k=%d", T, E, k);
+                CHECK(moe::dense_path(T) == (T <= moe::kSkinnyBM ? moe::GemmPath::Skinny : moe::GemmPath::Dma),
+                      "dense path T=%d", T);
                 CHECK(skinny ? f == moe::GemmPath::Skinny : (f == moe::GemmPath::Wide || f == moe::GemmPath::Tall),
                       "fallback T=%d E=%d k=%d", T, E, k);
                 CHECK(moe::path_bm(moe::GemmPath::Dma) == moe::kTallBM, "dma tile height");
