@@ -22,8 +22,6 @@
 //             ahead of its MFMAs, so the kernel runs at the weight-streaming bound.
 // All take their (expert, first row) tiles from the device-side list the permutation builds; the grid is
 // an upper bound and workgroups past the list's length exit at once.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -402,8 +400,13 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
 constexpr int kDThreads = 512;
 constexpr int kDRows = 256; // weight rows and token rows per tile
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Raw buffer resource over 4 GiB from `base` (stride 0, 32-bit offsets; word 3 as gfx9-family raw buffers
+// take it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+}
 
 // LDS layout of both operands: [256 rows][64 k] bf16, 16-byte chunk c of row r at slot c ^ dswz(r) (the
 // wide kernel's swizzle: conflict-free fragment reads).
@@ -445,19 +448,22 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         xoff[q] = (uint32_t)(reinterpret_cast<const char*>(act_row<KIND, DENSE>(a, ti, r)) - xbase) +
                   (uint32_t)(ls ^ dswz(r)) * 16u;
     }
+    // The copies are raw buffer loads: the per-lane offsets stay fixed 32-bit registers and the K step goes
+    // into the scalar offset (no per-lane 64-bit addresses to advance).
+    const __amdgpu_buffer_rsrc_t rx = dma_rsrc(xbase), rw0 = dma_rsrc(wbase0),
+                                 rw1 = KIND == GemmKind::GateUp ? dma_rsrc(wbase1) : rw0;
     auto load_x = [&](uint16_t* xl, int st) {
 #pragma unroll
         for (int q = 0; q < XI; ++q)
-            __builtin_amdgcn_global_load_lds((gptr_t)(xbase + 2 * st * kBK + xoff[q]),
-                                             (lptr_t)(xl + 8 * (wave + 8 * q) * kBK), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lptr_t)(xl + 8 * (wave + 8 * q) * kBK), 16, xoff[q],
+                                                     2 * st * kBK, 0, 0);
     };
     auto load_w = [&](uint16_t* wl, int st) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const char* wb = (KIND == GemmKind::GateUp && q >= 2 ? wbase1 : wbase0) + 2 * st * kBK;
-            __builtin_amdgcn_global_load_lds((gptr_t)(wb + woff[q]), (lptr_t)(wl + 8 * (wave + 8 * q) * kBK), 16,
-                                             0, 0);
-        }
+        for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(KIND == GemmKind::GateUp && q >= 2 ? rw1 : rw0,
+                                                     (lptr_t)(wl + 8 * (wave + 8 * q) * kBK), 16, woff[q],
+                                                     2 * st * kBK, 0, 0);
     };
 
     // fragments: block bases are multiples of 16 rows, so the swizzle depends on the lane only
@@ -505,76 +511,59 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     // weights of step s + 2) are in flight, so after the barrier step s + 1 is in LDS for everyone and
     // nobody reads step s's buffers any more; the tokens of step s + 2 and the weights of step s + 3 go
     // into those buffers; then the MFMAs of step s's second half, with the first-half fragments of step
-    // s + 1 read among them. Weights are thus loaded two steps ahead, tokens one. CHECKED steps (the last
-    // eight) skip loads and reads past the last step and wait for all loads where no weights are younger.
-    auto step = [&](auto checked, uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, int s) {
-        constexpr bool C = decltype(checked)::value;
+    // s + 1 read among them. Weights are thus loaded two steps ahead, tokens one. Copies of steps past the
+    // last one repeat the last step (data the workgroup has just read, so they come from L2, and nobody
+    // reads them): every step runs the same branch-free code, which keeps the compiler from adding waits or
+    // spills of its own around conditional copies.
+    auto step = [&](uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, int s) {
         read(f1a, f1b, wc, xc, 1);
         mma(f0a, f0b);
         interleave();
-        if (!C || s + 1 < nk) {
-            if (!C || s + 2 < nk)
-                __builtin_amdgcn_s_waitcnt(0x0074); // vmcnt(4) lgkmcnt(0)
-            else
-                __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            if (!C || s + 2 < nk) load_x(xc, s + 2);
-            __builtin_amdgcn_sched_barrier(0); // the weights must be the youngest copies (the vmcnt(4) above)
-            if (!C || s + 3 < nk) load_w(wc, s + 3);
-            __builtin_amdgcn_sched_barrier(0);
-            read(f0a, f0b, wn1, xn1, 0);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0074); // vmcnt(4) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        load_x(xc, min(s + 2, nk - 1));
+        __builtin_amdgcn_sched_barrier(0); // the weights must be the youngest copies (the vmcnt(4) above)
+        load_w(wc, min(s + 3, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        read(f0a, f0b, wn1, xn1, 0);
         mma(f1a, f1b);
         interleave();
     };
-    using unchecked = std::false_type;
-    using checked = std::true_type;
     // Prologue: every buffer is free at the start of a tile, so steps 0 and 1 (and the weights of step 2)
     // are requested at once, in the order X0 W0 X1 W1 W2; the barrier that opens step 0 waits for X0 and W0
     // only (the 4 XI + 8 younger copies may stay in flight), the one that opens step 1 (inside step 0)
-    // for X1 and W1 (W2 may stay in flight), as in every later step.
-    constexpr int V1 = XI + 4, V2 = XI + 8;
+    // for X1 and W1 (W2 may stay in flight), as in every later step. With fewer than three K steps the
+    // copies of steps past the last one repeat the last step (unread; the end of the tile waits for them):
+    // one branch-free sequence lets the compiler see that the first reads need X0 and W0 only.
+    constexpr int V2 = XI + 8;
     static_assert(V2 <= 15, "vmcnt immediates below hold 4 bits");
     load_x(xs0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_w(ws0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (nk > 2) {
-        load_x(xs1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(ws1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(ws2, 2);
-        __builtin_amdgcn_s_waitcnt(0x0070 | V2); // vmcnt(XI + 8) lgkmcnt(0)
-    } else if (nk > 1) {
-        load_x(xs1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(ws1, 1);
-        __builtin_amdgcn_s_waitcnt(0x0070 | V1); // vmcnt(XI + 4) lgkmcnt(0)
-    } else {
-        __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
-    }
+    load_x(xs1, min(1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws1, min(1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws2, min(2, nk - 1));
+    __builtin_amdgcn_s_waitcnt(0x0070 | V2); // vmcnt(XI + 8) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     read(f0a, f0b, ws0, xs0, 0);
-    // six steps per iteration (weight buffers cycle with period 3, token buffers with 2) while every load
-    // of the iteration is in range; then up to eight checked steps
+    // six steps per iteration (weight buffers cycle with period 3, token buffers with 2), then up to five
     int s = 0;
-    for (; s + 9 <= nk; s += 6) {
-        step(unchecked{}, ws0, xs0, ws1, xs1, s);
-        step(unchecked{}, ws1, xs1, ws2, xs0, s + 1);
-        step(unchecked{}, ws2, xs0, ws0, xs1, s + 2);
-        step(unchecked{}, ws0, xs1, ws1, xs0, s + 3);
-        step(unchecked{}, ws1, xs0, ws2, xs1, s + 4);
-        step(unchecked{}, ws2, xs1, ws0, xs0, s + 5);
+    for (; s + 6 <= nk; s += 6) {
+        step(ws0, xs0, ws1, xs1, s);
+        step(ws1, xs1, ws2, xs0, s + 1);
+        step(ws2, xs0, ws0, xs1, s + 2);
+        step(ws0, xs1, ws1, xs0, s + 3);
+        step(ws1, xs0, ws2, xs1, s + 4);
+        step(ws2, xs1, ws0, xs0, s + 5);
     }
-    if (s < nk) step(checked{}, ws0, xs0, ws1, xs1, s);
-    if (s + 1 < nk) step(checked{}, ws1, xs1, ws2, xs0, s + 1);
-    if (s + 2 < nk) step(checked{}, ws2, xs0, ws0, xs1, s + 2);
-    if (s + 3 < nk) step(checked{}, ws0, xs1, ws1, xs0, s + 3);
-    if (s + 4 < nk) step(checked{}, ws1, xs0, ws2, xs1, s + 4);
-    if (s + 5 < nk) step(checked{}, ws2, xs1, ws0, xs0, s + 5);
-    if (s + 6 < nk) step(checked{}, ws0, xs0, ws1, xs1, s + 6);
-    if (s + 7 < nk) step(checked{}, ws1, xs1, ws2, xs0, s + 7);
+    if (s < nk) step(ws0, xs0, ws1, xs1, s);
+    if (s + 1 < nk) step(ws1, xs1, ws2, xs0, s + 1);
+    if (s + 2 < nk) step(ws2, xs0, ws0, xs1, s + 2);
+    if (s + 3 < nk) step(ws0, xs1, ws1, xs0, s + 3);
+    if (s + 4 < nk) step(ws1, xs0, ws2, xs1, s + 4);
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
 
     if constexpr (KIND == GemmKind::DownF32) {
