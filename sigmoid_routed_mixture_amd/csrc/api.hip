@@ -269,6 +269,10 @@ moe_status forward_impl(const Request& q) {
         split.ntn[1] = moe::dma_ntn(false, H);
         for (int v = 0; v < 2; ++v) split.cap[v] = (int)moe::dma_xcd_cap(grid_tiles, split.ntn[v]);
     }
+    // the grouped DMA GEMMs run persistent (one workgroup per CU claiming blocks from per-XCD counters)
+    const char* ps = std::getenv("MOE_PERSIST"); // test knob: "0" keeps one workgroup per block
+    const bool persist = balanced && !(ps && std::strcmp(ps, "0") == 0);
+    if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
                                 static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, split,
                                 s0),
@@ -308,6 +312,7 @@ moe_status forward_impl(const Request& q) {
     // gate/up keeps the block-count split: its long weight stream makes blocks of any height cost about the
     // same (the work-balanced split measured 2 % slower there, 2 % faster on the down GEMM)
     add_shared(r1, q.ws1, q.ws3);
+    if (persist) r1.work_ctr = reinterpret_cast<unsigned long long*>(split.ctr);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
@@ -322,6 +327,7 @@ moe_status forward_impl(const Request& q) {
     r2.N = H;
     r2.K = I;
     r2.xcd_bounds = balanced ? split.bounds + (moe::kXcds + 1) : nullptr;
+    r2.work_ctr = persist ? reinterpret_cast<unsigned long long*>(split.ctr) + moe::kXcds : nullptr;
     add_shared(r2, q.ws2, nullptr);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));

@@ -11,8 +11,9 @@
 //
 // Three kernels:
 //  * dma    : up to 256 tokens x 256 weight rows per 8-wave workgroup, both operands copied from global
-//             memory straight into LDS (global_load_lds), weights two K steps ahead, tokens one; the
-//             prefill kernel.
+//             memory straight into LDS (buffer loads to LDS), weights two K steps ahead, tokens one; the
+//             prefill kernel. The routed GEMMs run it persistent: one workgroup per CU claims blocks from
+//             per-XCD counters.
 //  * wide   : 128 or 256 tokens x 256 weight rows per 8-wave workgroup. Each wave streams its own 32
 //             weight rows from HBM into MFMA registers; the token tile goes through double-buffered LDS.
 //             The router logits (dense, K split across workgroups), and the fallback for operands past
@@ -22,6 +23,8 @@
 //             ahead of its MFMAs, so the kernel runs at the weight-streaming bound.
 // All take their (expert, first row) tiles from the device-side list the permutation builds; the grid is
 // an upper bound and workgroups past the list's length exit at once.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
 // ------------------------------------------------------------------------------------------------
 // dma kernel
 
-// Loads into VGPRs reach about 16 B/clk per CU from L2; copies straight into LDS (global_load_lds, 16
+// Loads into VGPRs reach about 16 B/clk per CU from L2; copies straight into LDS (buffer loads to LDS, 16
 // bytes per lane) about 50. So both operands of a 256 x 256 tile go through LDS this way. Wave
 // (wm = wave % 4, wn = wave / 4) computes 64 weight rows (gate/up: 32 features of W1 and the same 32 of
 // W3) x the token blocks 2 jj + wn, from 16-byte LDS fragments; each accumulator sums its products in
@@ -412,13 +415,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
 // wide kernel's swizzle: conflict-free fragment reads).
 __device__ __forceinline__ int dswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <GemmKind KIND, bool DENSE, int NBW>
+// Blocks [lo, hi) of the expert-major order that XCD x takes: the work-balanced split when the permutation
+// wrote one, else contiguous equal counts (the order grouped_block gives).
+__device__ __forceinline__ void xcd_range(const GemmArgs& a, int ntn, int x, int& lo, int& hi) {
+    if (a.xcd_bounds != nullptr) {
+        lo = a.xcd_bounds[x];
+        hi = a.xcd_bounds[x + 1];
+        return;
+    }
+    const int live = a.ntiles[0] * ntn, chunk = (live + kXcds - 1) / kXcds;
+    lo = min(x * chunk, live);
+    hi = min(lo + chunk, live);
+}
+
+// The block a persistent workgroup of XCD x takes next (thread 0), or -1 when none is left. XCD y's counter
+// work_ctr[y] holds two 32-bit counts: blocks taken from the front of its range (by its own workgroups, in
+// order) and from the back (by workgroups of other XCDs once their own ranges are used up, so they take the
+// blocks the home XCD would reach last). Every increment adds one to front + back, so the first n of them
+// (n = the range's length) get distinct blocks and every later one gets none.
+__device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
+    for (int d = 0; d < kXcds; ++d) {
+        const int y = (x + d) % kXcds;
+        int lo, hi;
+        xcd_range(a, ntn, y, lo, hi);
+        if (lo >= hi) continue;
+        const unsigned long long old = atomicAdd(a.work_ctr + y, d == 0 ? 1ull : 1ull << 32);
+        const int f = (int)(old & 0xFFFFFFFFull), b = (int)(old >> 32);
+        if (f + b < hi - lo) return d == 0 ? lo + f : hi - 1 - b;
+    }
+    return -1;
+}
+
+// Persistent kernel (PERSIST): `wave0` is the wave index (a scalar); after the K loop thread 0 claims the
+// workgroup's next block, which wave 0 holds in `got` (-1: none left).
+template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST>
 __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, int ntile, uint16_t* ws0,
-                                         uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1) {
+                                         uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1, int wave0,
+                                         int ntn, int& got) {
     constexpr int XI = (NBW + 1) / 2; // token load instructions per wave and K step
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // persistent: the lane index comes from mbcnt, so nothing derived from the thread index has to stay in
+    // registers from one tile to the next
+    const int lane =
+        PERSIST ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) : (int)(threadIdx.x & 63);
+    const int wave = PERSIST ? wave0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = wave * 64 + lane;
     const int rl = lane & 15, kg = lane >> 4;
     const int wm = wave & 3, wn = wave >> 2;
     const int K = a.K, N = a.N;
@@ -565,6 +605,11 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     if (s + 3 < nk) step(ws0, xs1, ws1, xs0, s + 3);
     if (s + 4 < nk) step(ws1, xs0, ws2, xs1, s + 4);
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
+    if constexpr (PERSIST) {
+        int claim = -1;
+        if (tid == 0) claim = grab_block(a, ntn, (int)(blockIdx.x % kXcds));
+        if (wave == 0) got = __builtin_amdgcn_readfirstlane(claim);
+    }
 
     if constexpr (KIND == GemmKind::DownF32) {
         // fp32 rows leave through LDS: each wave turns one 16-token block at a time into 16 rows of its 64
@@ -638,7 +683,8 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn
 
     // 16-row token blocks per wave: tiles up to 256 rows, 32 per pair of token waves
     const int nb = (ti.rows + 31) >> 5;
-#define MOE_DMA_TILE(NBV) dma_tile<KIND, DENSE, NBV>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1)
+    int got = 0;
+#define MOE_DMA_TILE(NBV) dma_tile<KIND, DENSE, NBV, false>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, 0, ntn, got)
     switch (nb) {
     case 1: MOE_DMA_TILE(1); break;
     case 2: MOE_DMA_TILE(2); break;
@@ -650,6 +696,53 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn
     default: MOE_DMA_TILE(8); break;
     }
 #undef MOE_DMA_TILE
+}
+
+
+// Persistent form of the grouped DMA GEMM: one workgroup per CU takes blocks from its XCD's counter (then
+// from the other XCDs') until none is left; each tile runs as in the one-shot kernel.
+template <GemmKind KIND>
+__global__ __launch_bounds__(kDThreads) void gemm_dma_persistent_kernel(GemmArgs a, int ntn) {
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws2[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[kDRows * kBK];
+    int* mbox = reinterpret_cast<int*>(ws2); // thread 0 hands the next block to everyone through LDS
+    const int x = (int)(blockIdx.x % kXcds);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int got = 0; // wave 0: the block claimed next
+    if (wave == 0) {
+        int g = -1;
+        if (threadIdx.x == 0) g = grab_block(a, ntn, x);
+        got = __builtin_amdgcn_readfirstlane(g);
+    }
+    for (;;) {
+        if (wave == 0 && __builtin_amdgcn_mbcnt_lo(~0u, 0u) == 0) mbox[0] = got;
+        __syncthreads();
+        const int L = __builtin_amdgcn_readfirstlane(mbox[0]);
+        __syncthreads(); // read by everyone before the next tile's copies land in ws2
+        int64_t mtile;
+        int ntile;
+        TileInfo ti;
+        if (L < 0 || !block_at<kDRows>(a, ntn, L, mtile, ntile) || !tile_info<false, kDRows>(a, mtile, ti)) return;
+        const int nb = (ti.rows + 31) >> 5;
+#define MOE_DMA_TILE(NBV) dma_tile<KIND, false, NBV, true>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, wave, ntn, got)
+        switch (nb) {
+        case 1: MOE_DMA_TILE(1); break;
+        case 2: MOE_DMA_TILE(2); break;
+        case 3: MOE_DMA_TILE(3); break;
+        case 4: MOE_DMA_TILE(4); break;
+        case 5: MOE_DMA_TILE(5); break;
+        case 6: MOE_DMA_TILE(6); break;
+        case 7: MOE_DMA_TILE(7); break;
+        default: MOE_DMA_TILE(8); break;
+        }
+#undef MOE_DMA_TILE
+        // gate/up: a wave may still read the last K step's buffers (ws2 among them) when thread 0 writes the
+        // mailbox (the down GEMM's epilogue starts with a barrier after the K loop and stages in ws0 / ws1)
+        if (KIND == GemmKind::GateUp) __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -812,6 +905,20 @@ __global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict
     *reinterpret_cast<float4*>(out + i) = acc;
 }
 
+// Compute units of the current device, asked once per device.
+hipError_t cu_count(int& cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cus <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     const bool wide = path != GemmPath::Skinny;
@@ -827,6 +934,18 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     if (path == GemmPath::Dma && !DENSE && a.xcd_bounds != nullptr) {
         if (ntn != dma_ntn(KIND == GemmKind::GateUp, a.N)) return hipErrorInvalidValue;
         blocks = kXcds * dma_xcd_cap(grid_tiles, ntn);
+    }
+    if constexpr (KIND != GemmKind::Logits && !DENSE) {
+        if (path == GemmPath::Dma && a.work_ctr != nullptr) {
+            // persistent: one workgroup per CU (fewer when there are fewer blocks)
+            int cus = 0;
+            const hipError_t e = cu_count(cus);
+            if (e != hipSuccess) return e;
+            int64_t g = (int64_t)cus < blocks ? cus : blocks;
+            g = (g + kXcds - 1) / kXcds * kXcds;
+            gemm_dma_persistent_kernel<KIND><<<dim3((unsigned)g), kDThreads, 0, stream>>>(a, ntn);
+            return hipGetLastError();
+        }
     }
     if (blocks > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);

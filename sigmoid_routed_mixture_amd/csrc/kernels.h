@@ -22,11 +22,13 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // With shared_rows > 0 the tile list ends with the folded shared expert's tiles (group E). With `bounds`
 // (no folded shared expert) it also writes, for the two column-tile counts ntn[0] and ntn[1] of the DMA
 // kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
-// at most cap[i] blocks).
+// at most cap[i] blocks). With `ctr` (8-byte aligned) it zeroes the 2 * kXcds 64-bit work counters of the
+// persistent DMA kernel (kXcds for each GEMM).
 struct XcdSplit {
     int32_t* bounds;
     int ntn[2];
     int cap[2];
+    int32_t* ctr;
 };
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
@@ -55,6 +57,8 @@ struct GemmArgs {
     int shared_rows;           // grouped: tokens of the folded shared expert (0: none), taken in token order
     int shared_off;            // its first row in the permuted buffers (T * k)
     const int32_t* xcd_bounds; // DMA kernel, grouped: the XCD split of the blocks (kXcds + 1 ints), or null
+    unsigned long long* work_ctr; // DMA kernel, grouped: kXcds counters, zero at launch, for the persistent
+                                  // form (one workgroup per CU claiming blocks), or null for one block each
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
 };

@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e | (ht << 16), i * ht);
     append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
     if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
+    if (split.ctr != nullptr && e < 4 * kXcds) split.ctr[e] = 0;
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid | (ht << 16), i * ht);
         append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
         if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
+        if (split.ctr != nullptr && tid < 4 * kXcds) split.ctr[tid] = 0;
     }
     __syncthreads();
     const int t = tid;

@@ -148,6 +148,19 @@ def test_xcd_split_does_not_change_results(moe, monkeypatch):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
+def test_persistent_grid_does_not_change_results(moe, monkeypatch, name):
+    # one workgroup per CU claiming blocks from the XCD counters (and from the back of other XCDs' ranges
+    # once its own is used up) computes every block exactly as one workgroup per block does
+    say("[persistent] %s" % name)
+    cfg, h, d = case(name)
+    a = run_forward(moe, cfg, d)
+    monkeypatch.setenv("MOE_PERSIST", "0")
+    b = run_forward(moe, cfg, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "mid"])
 def test_second_stream_and_determinism(moe, name):
     say("[streams] %s" % name)
