@@ -218,7 +218,7 @@ moe_status forward_impl(const Request& q) {
     int32_t* offsets = static_cast<int32_t*>(at(L.offsets));
     int32_t* row_token = static_cast<int32_t*>(at(L.row_token));
     int32_t* slot_row = static_cast<int32_t*>(at(L.slot_row));
-    int2* tiles = static_cast<int2*>(at(L.tiles));
+    int4* tiles = static_cast<int4*>(at(L.tiles));
     int32_t* ntiles = static_cast<int32_t*>(at(L.ntiles));
     uint16_t* h_perm = static_cast<uint16_t*>(at(L.h_perm));
     float* y_perm = static_cast<float*>(at(L.y_perm));

@@ -45,9 +45,13 @@ __device__ __forceinline__ const uint16_t* weight_row(const uint16_t* w, const u
     return ti.shared ? ws + (size_t)n * K : w + ((size_t)ti.g * N + n) * K;
 }
 
-// Rows of group g: the routed counts, or all shared_rows tokens for the folded shared expert.
-__device__ __forceinline__ int group_rows(const GemmArgs& a, int g) {
-    return g < a.groups ? a.counts[g] : a.shared_rows;
+// A tile of the list: {group | tile height << 16, first row in the group, rows of the group, first permuted
+// row of the group}; the folded shared expert is group `groups`.
+template <int BM>
+__device__ __forceinline__ bool entry_ok(const GemmArgs& a, const int4& e) {
+    const int g = e.x & 0xFFFF, ht = e.x >> 16;
+    const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
+    return g < ngroups && ht > 0 && ht <= BM && e.y >= 0 && e.y < e.z && e.w >= 0;
 }
 
 template <bool DENSE, int BM>
@@ -61,51 +65,51 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
         return ti.rows > 0;
     }
     if (mtile >= a.ntiles[0]) return false;
-    const int2 t = a.tiles[mtile];
-    const int g = t.x & 0xFFFF, ht = t.x >> 16;
-    const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
-    if (g >= ngroups || ht <= 0 || ht > BM || t.y < 0) return false;
-    ti.g = g;
+    const int4 t = a.tiles[mtile];
+    if (!entry_ok<BM>(a, t)) return false;
+    ti.g = t.x & 0xFFFF;
     ti.m0 = t.y;
-    ti.shared = g == a.groups;
-    ti.off = ti.shared ? a.shared_off : a.offsets[g];
-    ti.rows = min(ht, group_rows(a, g) - t.y);
-    return ti.rows > 0;
+    ti.shared = ti.g == a.groups;
+    ti.off = t.w;
+    ti.rows = min(t.x >> 16, t.z - t.y);
+    return true;
 }
 
 // Workgroup -> (token tile, output-column tile) of the grouped wide GEMM. The live blocks go in
 // expert-major order and each XCD takes one contiguous eighth of it: the token tiles that share a slice
 // of an expert's weights run side by side on one XCD, and so do the column tiles that share a token
 // tile, so both come from HBM about once instead of once per XCD.
+// Block L of the order, decoded from the one entry at L / ntn (a tile of the same group): every tile of a
+// group starts at a multiple of its height, so the block's tile is known without reading its own entry.
 template <int BM>
-__device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, int64_t& mtile, int& ntile) {
-    const int2 entry = a.tiles[L / ntn];
-    const int g = entry.x & 0xFFFF, ht = entry.x >> 16;
-    const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
-    if (g >= ngroups || ht <= 0 || ht > BM || entry.y < 0) return false;
-    const int m = (group_rows(a, g) + ht - 1) / ht;
-    if (m <= 0) return false;
-    mtile = expert_major_tile(L, ntn, entry.y / ht, m, ntile);
+__device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, TileInfo& ti, int& ntile) {
+    const int4 e = a.tiles[L / ntn];
+    if (!entry_ok<BM>(a, e)) return false;
+    const int ht = e.x >> 16, m = (e.z + ht - 1) / ht;
+    const int64_t mtile = expert_major_tile(L, ntn, e.y / ht, m, ntile);
+    ti.g = e.x & 0xFFFF;
+    ti.m0 = (int)(mtile - (L / ntn - e.y / ht)) * ht;
+    ti.shared = ti.g == a.groups;
+    ti.off = e.w;
+    ti.rows = min(ht, e.z - ti.m0);
     return true;
 }
 
 template <int BM>
-__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
-                                              int& ntile) {
+__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, TileInfo& ti, int& ntile) {
     const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
     if (L < 0) return false;
-    return block_at<BM>(a, ntn, L, mtile, ntile);
+    return block_at<BM>(a, ntn, L, ti, ntile);
 }
 
 // The same order with the work-balanced XCD split the permutation wrote: XCD x = bid % kXcds takes the
 // blocks [bounds[x], bounds[x + 1]).
 template <int BM>
-__device__ __forceinline__ bool balanced_block(const GemmArgs& a, int ntn, int64_t bid, int64_t& mtile,
-                                               int& ntile) {
+__device__ __forceinline__ bool balanced_block(const GemmArgs& a, int ntn, int64_t bid, TileInfo& ti, int& ntile) {
     const int x = (int)(bid % kXcds);
     const int64_t L = a.xcd_bounds[x] + bid / kXcds;
     if (L >= a.xcd_bounds[x + 1]) return false;
-    return block_at<BM>(a, ntn, L, mtile, ntile);
+    return block_at<BM>(a, ntn, L, ti, ntile);
 }
 
 // Activation row for tile row m (clamped to the tile's last valid row: padded columns of the MFMA tile
@@ -307,15 +311,13 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs a, int nt
         bid -= (int64_t)split * tiles_per_split * ntn;
     }
     int ntile;
-    int64_t mtile;
+    TileInfo ti;
     if (DENSE) {
         ntile = (int)(bid % ntn);
-        mtile = bid / ntn;
-    } else if (!grouped_block<BM>(a, ntn, bid, mtile, ntile)) {
+        if (!tile_info<true, BM>(a, bid / ntn, ti)) return;
+    } else if (!grouped_block<BM>(a, ntn, bid, ti, ntile)) {
         return;
     }
-    TileInfo ti;
-    if (!tile_info<DENSE, BM>(a, mtile, ti)) return;
 
     __shared__ __attribute__((aligned(16))) uint16_t xs0[BM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t xs1[BM * kBK];
@@ -663,16 +665,14 @@ template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
     const int64_t bid = blockIdx.x;
     int ntile;
-    int64_t mtile;
+    TileInfo ti;
     if (DENSE) {
         ntile = (int)(bid % ntn);
-        mtile = bid / ntn;
-    } else if (a.xcd_bounds != nullptr ? !balanced_block<kDRows>(a, ntn, bid, mtile, ntile)
-                                       : !grouped_block<kDRows>(a, ntn, bid, mtile, ntile)) {
+        if (!tile_info<true, kDRows>(a, bid / ntn, ti)) return;
+    } else if (a.xcd_bounds != nullptr ? !balanced_block<kDRows>(a, ntn, bid, ti, ntile)
+                                       : !grouped_block<kDRows>(a, ntn, bid, ti, ntile)) {
         return;
     }
-    TileInfo ti;
-    if (!tile_info<DENSE, kDRows>(a, mtile, ti)) return;
 
     // 160 KB: three weight buffers and two token buffers of [256][64] bf16
     __shared__ __attribute__((aligned(16))) uint16_t ws0[kDRows * kBK];
@@ -722,10 +722,9 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_persistent_kernel(GemmArgs
         __syncthreads();
         const int L = __builtin_amdgcn_readfirstlane(mbox[0]);
         __syncthreads(); // read by everyone before the next tile's copies land in ws2
-        int64_t mtile;
         int ntile;
         TileInfo ti;
-        if (L < 0 || !block_at<kDRows>(a, ntn, L, mtile, ntile) || !tile_info<false, kDRows>(a, mtile, ti)) return;
+        if (L < 0 || !block_at<kDRows>(a, ntn, L, ti, ntile)) return;
         const int nb = (ti.rows + 31) >> 5;
 #define MOE_DMA_TILE(NBV) dma_tile<KIND, false, NBV, true>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, wave, ntn, got)
         switch (nb) {

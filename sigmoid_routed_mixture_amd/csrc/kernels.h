@@ -17,7 +17,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
                          hipStream_t stream);
 
 // Permutation: per-chunk expert histograms, the prefix sums (and, when `tiles` is non-null, the list of
-// BM-row grouped-GEMM tiles), then the stable scatter of slots into expert-contiguous rows.
+// BM-row grouped-GEMM tiles, kTileEntryBytes each), then the stable scatter of slots into expert-contiguous
+// rows.
 // chunk_scratch holds ceil(T / 256) * E ints.
 // With shared_rows > 0 the tile list ends with the folded shared expert's tiles (group E). With `bounds`
 // (no folded shared expert) it also writes, for the two column-tile counts ntn[0] and ntn[1] of the DMA
@@ -31,7 +32,7 @@ struct XcdSplit {
     int32_t* ctr;
 };
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
-                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
+                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
                           int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split, hipStream_t stream);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E].
@@ -47,7 +48,8 @@ struct GemmArgs {
     void* out;                 // [rows, N]: bf16 (h or per-slot outputs) or fp32
     const int32_t* counts;     // rows per group, or null for one dense group
     const int32_t* offsets;    // first row of each group
-    const int2* tiles;         // {group | tile height << 16, first row in group} per tile
+    const int4* tiles;         // per tile {group | tile height << 16, first row in the group, rows of the group,
+                               // first permuted row of the group}
     const int32_t* ntiles;     // number of valid tiles
     int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped

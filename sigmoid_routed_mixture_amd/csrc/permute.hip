@@ -62,15 +62,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
     return incl - v;
 }
 
-// Appends the folded shared expert's tiles (group E, all shared_rows tokens) after the routed ones.
-__device__ __forceinline__ void append_shared_tiles(int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                    int routed_tiles, int E, int shared_rows, int BM) {
+// Appends the folded shared expert's tiles (group E, all shared_rows tokens, its rows from shared_off on)
+// after the routed ones.
+__device__ __forceinline__ void append_shared_tiles(int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                    int routed_tiles, int E, int shared_rows, int shared_off,
+                                                    int BM) {
     const int tid = threadIdx.x;
     int ns = 0;
     if (shared_rows > 0) {
         const int hs = tile_height(shared_rows, BM);
         ns = (shared_rows + hs - 1) / hs;
-        for (int i = tid; i < ns; i += 256) tiles[routed_tiles + i] = make_int2(E | (hs << 16), i * hs);
+        for (int i = tid; i < ns; i += 256)
+            tiles[routed_tiles + i] = make_int4(E | (hs << 16), i * hs, shared_rows, shared_off);
     }
     if (tid == 0) ntiles[0] = routed_tiles + ns;
 }
@@ -116,8 +119,8 @@ __device__ void xcd_split(const XcdSplit& sp, int E, int n, int ht, int nt, int 
 
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int chunks, int E,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                        int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int BM, int shared_rows, XcdSplit split) {
+                                                        int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                        int BM, int shared_rows, int shared_off, XcdSplit split) {
     __shared__ int sh[256];
     const int e = threadIdx.x;
     int n = 0;
@@ -139,8 +142,8 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     const int nt = (e < E && BM > 0) ? (n + ht - 1) / ht : 0;
     int tiles_total = 0;
     const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e | (ht << 16), i * ht);
-    append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
+    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(e | (ht << 16), i * ht, n, off);
+    append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, shared_off, BM);
     if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
     if (split.ctr != nullptr && e < 4 * kXcds) split.ctr[e] = 0;
 }
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // tile list, then the scatter, with the bit matrix kept in LDS between them.
 __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                          int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                          int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                                           int BM, int shared_rows, XcdSplit split,
                                                           int32_t* __restrict__ row_token,
                                                           int32_t* __restrict__ slot_row) {
@@ -202,8 +205,8 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         const int nt = (tid < E && BM > 0) ? (n + ht - 1) / ht : 0;
         int tiles_total = 0;
         const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(tid | (ht << 16), i * ht);
-        append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, BM);
+        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(tid | (ht << 16), i * ht, n, off);
+        append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, T * k, BM);
         if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
         if (split.ctr != nullptr && tid < 4 * kXcds) split.ctr[tid] = 0;
     }
@@ -248,7 +251,7 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
 } // namespace
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
-                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int2* tiles,
+                          int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
                           int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split, hipStream_t stream) {
     const int chunks = (T + kChunk - 1) / kChunk;
     if (chunks == 1) {
@@ -260,7 +263,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scan_kernel<<<1, 256, 0, stream>>>(chunk_scratch, chunks, E, counts, offsets, tiles, ntiles, BM,
-                                            shared_rows, split);
+                                            shared_rows, T * k, split);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scatter_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, offsets, chunk_scratch, row_token, slot_row);

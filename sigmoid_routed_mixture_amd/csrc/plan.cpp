@@ -84,7 +84,7 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     // shared expert's tiles when it is folded in
     const int bm_min = std::min(std::min(kWideBM, kTallBM), kSkinnyBM);
     const bool fold = shared_fold(T, E, k, I, Is);
-    L.tiles = take((size_t)(max_tiles(T, E, k, bm_min) + (fold ? shared_tiles(T, bm_min) : 0)) * 8);
+    L.tiles = take((size_t)(max_tiles(T, E, k, bm_min) + (fold ? shared_tiles(T, bm_min) : 0)) * kTileEntryBytes);
     L.ntiles = take(4);
     L.xcd_bounds = take((2 * (kXcds + 1) + 4 * kXcds) * 4); // two XCD splits, then 2 x kXcds 64-bit counters
     L.partial = take((size_t)router_splits(T, H, E) * (size_t)T * (size_t)E * 4);

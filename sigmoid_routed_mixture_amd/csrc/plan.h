@@ -113,6 +113,9 @@ constexpr bool shared_fold(int T, int E, int k, int I, int Is) {
     return Is > 0 && Is == I && (int64_t)T * k <= (int64_t)kSkinnyBM * E;
 }
 constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
+// A tile of the device-side list: {group | tile height << 16, first row in the group, rows of the group,
+// first permuted row of the group} (int4), so a workgroup decodes its block with one load.
+constexpr int kTileEntryBytes = 16;
 
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present

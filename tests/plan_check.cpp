@@ -51,7 +51,8 @@ int main() {
                             size_t tiles_need = 0;
                             for (int BM : {moe::kSkinnyBM, moe::kWideBM, moe::kTallBM})
                                 tiles_need = std::max(tiles_need, (size_t)(moe::max_tiles(T, E, k, BM) +
-                                                                           (fold ? moe::shared_tiles(T, BM) : 0)) * 8);
+                                                                           (fold ? moe::shared_tiles(T, BM) : 0)) *
+                                                                  moe::kTileEntryBytes);
                             struct R { size_t off, need; const char* name; };
                             std::vector<R> rs = {
                                 {L.ids, Tk * 4, "ids"}, {L.gates, Tk * 4, "gates"}, {L.counts, (size_t)E * 4, "counts"},
