@@ -430,20 +430,18 @@ __device__ __forceinline__ void xcd_range(const GemmArgs& a, int ntn, int x, int
     hi = min(lo + chunk, live);
 }
 
-// The block a persistent workgroup of XCD x takes next (thread 0), or -1 when none is left. XCD y's counter
-// work_ctr[y] holds two 32-bit counts: blocks taken from the front of its range (by its own workgroups, in
-// order) and from the back (by workgroups of other XCDs once their own ranges are used up, so they take the
-// blocks the home XCD would reach last). Every increment adds one to front + back, so the first n of them
-// (n = the range's length) get distinct blocks and every later one gets none.
+// The block a persistent workgroup of XCD x takes next (thread 0), or -1 when none is left: the front of its
+// own XCD's range, then the back of the other XCDs' ranges (the blocks their own workgroups would reach
+// last), through the counters of claim_block.
 __device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
     for (int d = 0; d < kXcds; ++d) {
         const int y = (x + d) % kXcds;
         int lo, hi;
         xcd_range(a, ntn, y, lo, hi);
         if (lo >= hi) continue;
-        const unsigned long long old = atomicAdd(a.work_ctr + y, d == 0 ? 1ull : 1ull << 32);
-        const int f = (int)(old & 0xFFFFFFFFull), b = (int)(old >> 32);
-        if (f + b < hi - lo) return d == 0 ? lo + f : hi - 1 - b;
+        const unsigned long long old = atomicAdd(a.work_ctr + y, d == 0 ? kClaimFront : kClaimBack);
+        const int64_t c = claim_block(lo, hi, old, d == 0);
+        if (c >= 0) return (int)c;
     }
     return -1;
 }

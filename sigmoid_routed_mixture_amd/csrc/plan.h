@@ -105,6 +105,17 @@ constexpr int64_t dma_xcd_cap(int64_t grid_tiles, int ntn) {
     return avg + avg / 4 + 1;
 }
 
+// Block claims of the persistent DMA kernel. An XCD's range [lo, hi) is handed out through one 64-bit counter:
+// the home XCD's workgroups add kClaimFront and take the range from the front, workgroups of other XCDs add
+// kClaimBack and take it from the back. Every claim raises front + back by one, so the claims that saw
+// front + back < hi - lo get distinct blocks and all later ones get none. `old` is what the atomic add
+// returned; the result is the claimed block or -1.
+constexpr uint64_t kClaimFront = 1, kClaimBack = uint64_t(1) << 32;
+constexpr int64_t claim_block(int lo, int hi, uint64_t old, bool home) {
+    const int64_t f = (int64_t)(old & 0xFFFFFFFFu), b = (int64_t)(old >> 32);
+    return f + b < (int64_t)hi - lo ? (home ? lo + f : hi - 1 - b) : -1;
+}
+
 // With few tokens per expert (at most 16 on average) the shared expert joins the routed experts' grouped
 // GEMMs as one more group (index E, all T tokens, its rows after the T * k routed rows) when it has the
 // routed experts' width: its weights then stream with theirs in one launch. Otherwise it runs as two dense

@@ -140,6 +140,34 @@ int main() {
     }
     std::printf("%d block orders checked\n", orders);
 
+    // block claims of the persistent kernel: any interleaving of front (home) and back (other XCDs) claims
+    // hands every block of the range out exactly once, and later claims get none
+    {
+        uint64_t rng = 12345;
+        auto next = [&]() { rng = rng * 6364136223846793005ull + 1442695040888963407ull; return rng >> 33; };
+        for (int trial = 0; trial < 2000; ++trial) {
+            const int lo = (int)(next() % 1000), n = (int)(next() % 300);
+            std::vector<int> seen(n, 0);
+            uint64_t ctr = 0; // the claims reach the counter in some order; each sees the sum before it
+            int got = 0;
+            const int claims = n + (int)(next() % 20);
+            const int back_pct = (int)(next() % 101);
+            for (int c = 0; c < claims; ++c) {
+                const bool home = (int)(next() % 100) >= back_pct;
+                const uint64_t old = ctr;
+                ctr += home ? moe::kClaimFront : moe::kClaimBack;
+                const int64_t b = moe::claim_block(lo, lo + n, old, home);
+                if (c < n) {
+                    CHECK(b >= lo && b < lo + n, "claim %d of %d got %lld", c, n, (long long)b);
+                    if (b >= lo && b < lo + n) seen[b - lo]++, got++;
+                } else {
+                    CHECK(b == -1, "claim %d past %d blocks got %lld", c, n, (long long)b);
+                }
+            }
+            for (int i = 0; i < n; ++i) CHECK(seen[i] == 1, "block %d of %d claimed %d times", i, n, seen[i]);
+            CHECK(got == n, "%d of %d blocks claimed", got, n);
+        }
+    }
     // tile heights: at most BM, never more tiles than ceil(n / BM), no empty last tile; for the LDS-tiled
     // kernel a multiple of 16 rows (128) or 32 rows (256), the last tile shorter by less than that per tile
     for (int BM : {moe::kSkinnyBM, moe::kWideBM, moe::kTallBM})
