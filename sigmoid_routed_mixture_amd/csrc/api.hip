@@ -1,4 +1,5 @@
 // The C ABI of include/moe.h: argument checks, workspace carving, stream/event orchestration, launches.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -273,6 +274,24 @@ moe_status forward_impl(const Request& q) {
     const char* ps = std::getenv("MOE_PERSIST"); // test knob: "0" keeps one workgroup per block
     const bool persist = balanced && !(ps && std::strcmp(ps, "0") == 0);
     if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
+    // decode-sized gate/up launches: the permutation picks a K split of 1 or 2 from the live block count
+    const char* kss = std::getenv("MOE_KSPLIT"); // test knob: "1" never splits, "2" always does
+    const bool ks_off = kss && std::strcmp(kss, "1") == 0, ks_on = kss && std::strcmp(kss, "2") == 0;
+    bool ksplit = false;
+    if (path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off) {
+        int cus = 0;
+        MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
+        // the split needs two rounds of blocks: with at most one (every expert and the shared one active),
+        // no reduction is launched
+        const int ntn1 = moe::dma_ntn(true, I);
+        const int64_t most = (std::min<int64_t>(E, (int64_t)T * k) + moe::shared_tiles(T, BM)) * ntn1;
+        ksplit = ks_on || most > cus;
+        split.ks_ntn = ntn1;
+        split.cus = cus;
+        split.ks_force = ks_on ? 2 : 0;
+    }
+    int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
+    split.ksplit = ks_flag;
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
                                 static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, split,
                                 s0),
@@ -313,7 +332,14 @@ moe_status forward_impl(const Request& q) {
     // same (the work-balanced split measured 2 % slower there, 2 % faster on the down GEMM)
     add_shared(r1, q.ws1, q.ws3);
     if (persist) r1.work_ctr = reinterpret_cast<unsigned long long*>(split.ctr);
+    const int h_rows = T * k + (fold ? T : 0);
+    if (ksplit) {
+        r1.ksplit_dev = ks_flag;
+        r1.part = static_cast<float*>(at(L.ks_part));
+        r1.part_rows = h_rows;
+    }
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
+    if (ksplit) MOE_HIP(moe::launch_reduce_ksplit(r1.part, ks_flag, h_rows, I, h_perm, s0), "gate/up K-split reduction");
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
     r2.act = h_perm;

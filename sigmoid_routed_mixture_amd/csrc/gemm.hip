@@ -95,11 +95,14 @@ __device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, 
     return true;
 }
 
+// With a K split of S, S consecutive positions of the order are the K ranges of one block (`ks` is the range).
 template <int BM>
-__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, TileInfo& ti, int& ntile) {
-    const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn);
+__device__ __forceinline__ bool grouped_block(const GemmArgs& a, int ntn, int64_t bid, TileInfo& ti, int& ntile,
+                                              int S = 1, int* ks = nullptr) {
+    const int64_t L = xcd_block_order(bid, (int64_t)a.ntiles[0] * ntn * S);
     if (L < 0) return false;
-    return block_at<BM>(a, ntn, L, ti, ntile);
+    if (ks != nullptr) *ks = (int)(L % S);
+    return block_at<BM>(a, ntn, L / S, ti, ntile);
 }
 
 // The same order with the work-balanced XCD split the permutation wrote: XCD x = bid % kXcds takes the
@@ -451,7 +454,7 @@ __device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
 template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST>
 __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, int ntile, uint16_t* ws0,
                                          uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1, int wave0,
-                                         int ntn, int& got) {
+                                         int ntn, int& got, int ks = 0, int S = 1) {
     constexpr int XI = (NBW + 1) / 2; // token load instructions per wave and K step
     // persistent: the lane index comes from mbcnt, so nothing derived from the thread index has to stay in
     // registers from one tile to the next
@@ -462,7 +465,10 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     const int rl = lane & 15, kg = lane >> 4;
     const int wm = wave & 3, wn = wave >> 2;
     const int K = a.K, N = a.N;
-    const int nk = K / kBK;
+    // K steps [sb, sb + nk) of the nk_all: all of them, or half with a K split of 2
+    const int nk_all = K / kBK;
+    const int sb = ks * nk_all / S;
+    const int nk = (ks + 1) * nk_all / S - sb;
 
     // Load instruction t (8 rows = 1 KB of LDS) of an operand is issued by wave t % 8: 4 weight loads and
     // XI token loads per wave and step (token rows past the computed blocks are not loaded, but for an odd
@@ -496,14 +502,14 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
 #pragma unroll
         for (int q = 0; q < XI; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lptr_t)(xl + 8 * (wave + 8 * q) * kBK), 16, xoff[q],
-                                                     2 * st * kBK, 0, 0);
+                                                     2 * (sb + st) * kBK, 0, 0);
     };
     auto load_w = [&](uint16_t* wl, int st) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(KIND == GemmKind::GateUp && q >= 2 ? rw1 : rw0,
                                                      (lptr_t)(wl + 8 * (wave + 8 * q) * kBK), 16, woff[q],
-                                                     2 * st * kBK, 0, 0);
+                                                     2 * (sb + st) * kBK, 0, 0);
     };
 
     // fragments: block bases are multiples of 16 rows, so the swizzle depends on the lane only
@@ -640,6 +646,24 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         // gate/up: lane holds features 4 kg + r of weight blocks i (g) and i + 2 (u), token rl of token
         // block 2 jj + wn
         static_assert(KIND == GemmKind::GateUp, "the dma kernel computes gate/up and fp32 down GEMMs");
+        if (S > 1) {
+            // K split: fp32 partials of g (columns [0, N)) and u ([N, 2N)) of this K range
+            float* part = a.part + (size_t)ks * a.part_rows * 2 * N;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const int m = 16 * (2 * j + wn) + rl;
+                if (m >= ti.rows) continue;
+                float* prow = part + ((size_t)ti.off + ti.m0 + m) * 2 * N;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int col = ntile * 128 + 32 * wm + 16 * i + 4 * kg;
+                    if (col >= N) continue;
+                    *reinterpret_cast<f32x4*>(prow + col) = acc[i][j];
+                    *reinterpret_cast<f32x4*>(prow + N + col) = acc[i + 2][j];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int m = 16 * (2 * j + wn) + rl;
@@ -662,13 +686,14 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
 template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
     const int64_t bid = blockIdx.x;
-    int ntile;
+    int ntile, S = 1, ks = 0;
+    if (!DENSE && KIND == GemmKind::GateUp && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
     TileInfo ti;
     if (DENSE) {
         ntile = (int)(bid % ntn);
         if (!tile_info<true, kDRows>(a, bid / ntn, ti)) return;
     } else if (a.xcd_bounds != nullptr ? !balanced_block<kDRows>(a, ntn, bid, ti, ntile)
-                                       : !grouped_block<kDRows>(a, ntn, bid, ti, ntile)) {
+                                       : !grouped_block<kDRows>(a, ntn, bid, ti, ntile, S, &ks)) {
         return;
     }
 
@@ -682,7 +707,7 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn
     // 16-row token blocks per wave: tiles up to 256 rows, 32 per pair of token waves
     const int nb = (ti.rows + 31) >> 5;
     int got = 0;
-#define MOE_DMA_TILE(NBV) dma_tile<KIND, DENSE, NBV, false>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, 0, ntn, got)
+#define MOE_DMA_TILE(NBV) dma_tile<KIND, DENSE, NBV, false>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, 0, ntn, got, ks, S)
     switch (nb) {
     case 1: MOE_DMA_TILE(1); break;
     case 2: MOE_DMA_TILE(2); break;
@@ -887,6 +912,25 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
     *reinterpret_cast<uint2*>(h + row * N + col) = v;
 }
 
+// The same for a grouped gate/up launch whose K split the permutation chose: nothing to do when it is 1 (the
+// GEMM wrote h itself).
+__global__ __launch_bounds__(256) void reduce_swiglu_ksplit_kernel(const float* __restrict__ part,
+                                                                   const int32_t* __restrict__ ksplit, int rows,
+                                                                   int N, uint16_t* __restrict__ h) {
+    if (ksplit[0] != 2) return;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= (int64_t)rows * N) return;
+    const int64_t row = i / N, col = i % N;
+    const float* p0 = part + (size_t)row * 2 * N + col;
+    const float* p1 = p0 + (size_t)rows * 2 * N;
+    const float4 g0 = *reinterpret_cast<const float4*>(p0), u0 = *reinterpret_cast<const float4*>(p0 + N);
+    const float4 g1 = *reinterpret_cast<const float4*>(p1), u1 = *reinterpret_cast<const float4*>(p1 + N);
+    uint2 v;
+    v.x = pack_bf16x2(swiglu(g0.x + g1.x, u0.x + u1.x), swiglu(g0.y + g1.y, u0.y + u1.y));
+    v.y = pack_bf16x2(swiglu(g0.z + g1.z, u0.z + u1.z), swiglu(g0.w + g1.w, u0.w + u1.w));
+    *reinterpret_cast<uint2*>(h + row * N + col) = v;
+}
+
 __global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict__ part, int S, int64_t n,
                                                          float* __restrict__ out) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -927,6 +971,10 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     const int splits = (KIND == GemmKind::Logits || (!wide && DENSE)) && a.ksplit > 1 ? a.ksplit : 1;
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
+    if (KIND == GemmKind::GateUp && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {
+        if (a.part == nullptr || a.part_rows <= 0 || a.K < 2 * kBK) return hipErrorInvalidValue;
+        blocks *= 2; // room for a K split of 2
+    }
     if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (path == GemmPath::Dma && !DENSE && a.xcd_bounds != nullptr) {
         if (ntn != dma_ntn(KIND == GemmKind::GateUp, a.N)) return hipErrorInvalidValue;
@@ -974,6 +1022,16 @@ hipError_t launch_reduce(GemmKind kind, const float* partial, int S, int rows, i
         reduce_sum_kernel<<<blocks, 256, 0, stream>>>(partial, S, n, static_cast<float*>(out));
     return hipGetLastError();
 }
+
+hipError_t launch_reduce_ksplit(const float* partial, const int32_t* ksplit, int rows, int N, uint16_t* h,
+                                hipStream_t stream) {
+    const int64_t n = (int64_t)rows * N;
+    if (n <= 0) return hipSuccess;
+    reduce_swiglu_ksplit_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, stream>>>(partial, ksplit, rows, N, h);
+    return hipGetLastError();
+}
+
+hipError_t device_cus(int& cus) { return cu_count(cus); }
 
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     const bool dense = a.counts == nullptr;

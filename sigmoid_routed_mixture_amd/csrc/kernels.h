@@ -25,11 +25,17 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
 // at most cap[i] blocks). With `ctr` (8-byte aligned) it zeroes the 2 * kXcds 64-bit work counters of the
 // persistent DMA kernel (kXcds for each GEMM).
+// With `ksplit` it writes the gate/up K split (gate_up_ksplit of the live blocks, ks_ntn column tiles each,
+// on `cus` compute units; ks_force > 0 forces that split).
 struct XcdSplit {
     int32_t* bounds;
     int ntn[2];
     int cap[2];
     int32_t* ctr;
+    int32_t* ksplit;
+    int ks_ntn;
+    int cus;
+    int ks_force;
 };
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
@@ -63,6 +69,9 @@ struct GemmArgs {
                                   // form (one workgroup per CU claiming blocks), or null for one block each
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
+    const int32_t* ksplit_dev; // DMA kernel, grouped gate/up: the K split (1 or 2) the permutation chose, or null
+    float* part;               // its fp32 partials [2][part_rows][2N] (g, then u) when the split is 2
+    int part_rows;
 };
 enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
@@ -70,6 +79,11 @@ hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t 
 // In-order reduction of a split dense GEMM's partials (dense_splits in plan.h) into h (gate/up, bf16 after
 // the SwiGLU) or the fp32 output (down).
 hipError_t launch_reduce(GemmKind kind, const float* partial, int S, int rows, int N, void* out, hipStream_t stream);
+// The same for a grouped gate/up launch whose K split the device chose (*ksplit): nothing when it is 1.
+hipError_t launch_reduce_ksplit(const float* partial, const int32_t* ksplit, int rows, int N, uint16_t* h,
+                                hipStream_t stream);
+// Compute units of the current device.
+hipError_t device_cus(int& cus);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
 // residual (bf16) added last.

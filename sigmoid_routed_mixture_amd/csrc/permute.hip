@@ -64,9 +64,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
 
 // Appends the folded shared expert's tiles (group E, all shared_rows tokens, its rows from shared_off on)
 // after the routed ones.
-__device__ __forceinline__ void append_shared_tiles(int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                    int routed_tiles, int E, int shared_rows, int shared_off,
-                                                    int BM) {
+__device__ __forceinline__ int append_shared_tiles(int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                   int routed_tiles, int E, int shared_rows, int shared_off,
+                                                   int BM) {
     const int tid = threadIdx.x;
     int ns = 0;
     if (shared_rows > 0) {
@@ -76,6 +76,13 @@ __device__ __forceinline__ void append_shared_tiles(int4* __restrict__ tiles, in
             tiles[routed_tiles + i] = make_int4(E | (hs << 16), i * hs, shared_rows, shared_off);
     }
     if (tid == 0) ntiles[0] = routed_tiles + ns;
+    return routed_tiles + ns;
+}
+
+// The gate/up K split of a decode-sized launch (thread 0).
+__device__ __forceinline__ void write_ksplit(const XcdSplit& sp, int all_tiles) {
+    if (sp.ksplit != nullptr && threadIdx.x == 0)
+        sp.ksplit[0] = sp.ks_force > 0 ? sp.ks_force : gate_up_ksplit((int64_t)all_tiles * sp.ks_ntn, sp.cus);
 }
 
 // The work-balanced XCD split (plan.h) of the tile list just built, for both column-tile counts. Thread e
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     int tiles_total = 0;
     const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
     for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(e | (ht << 16), i * ht, n, off);
-    append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, shared_off, BM);
+    write_ksplit(split, append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, shared_off, BM));
     if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
     if (split.ctr != nullptr && e < 4 * kXcds) split.ctr[e] = 0;
 }
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         int tiles_total = 0;
         const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
         for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(tid | (ht << 16), i * ht, n, off);
-        append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, T * k, BM);
+        write_ksplit(split, append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, T * k, BM));
         if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
         if (split.ctr != nullptr && tid < 4 * kXcds) split.ctr[tid] = 0;
     }

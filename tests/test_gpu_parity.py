@@ -112,6 +112,21 @@ def test_forward_parity(moe, name):
         assert counts[0] == cfg.T and np.all(counts[59:] == 0)
 
 
+@pytest.mark.parametrize("name", ["tiny", "glm5_decode", "glm47_decode"])
+@pytest.mark.parametrize("ks", ["1", "2"])
+def test_decode_gate_up_k_split(moe, monkeypatch, name, ks):
+    # decode-sized gate/up launches with the K split forced off and on, against the oracle on every token
+    say("[K split %s] %s" % (ks, name))
+    monkeypatch.setenv("MOE_KSPLIT", ks)
+    cfg, h, d = case(name)
+    ref = route_ref(name)
+    out, ids, gates, counts = run_forward(moe, cfg, d)
+    same, nnear, ndiff = compare_routing(ids, gates, ref, name)
+    rows = np.arange(cfg.T, dtype=np.int32)[same]
+    orc = oracle_forward_rows(h, cfg.k, cfg.scale, rows)
+    compare_out(out[rows], orc["out"], "%s/ks%s" % (name, ks))
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("glm5_decode", 16), ("mid", 384)])
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
