@@ -449,8 +449,10 @@ __device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
     return -1;
 }
 
-// Persistent kernel (PERSIST): `wave0` is the wave index (a scalar); after the K loop thread 0 claims the
-// workgroup's next block, which wave 0 holds in `got` (-1: none left).
+// One tile of the DMA GEMM. Persistent kernel (PERSIST): `wave0` is the wave index (a scalar); after the K
+// loop thread 0 claims the workgroup's next block, which wave 0 holds in `got` (-1: none left). With a K
+// split S of 2 (decode-sized gate/up launches) the tile computes K range `ks` and writes fp32 partials of g
+// and u instead of h.
 template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST>
 __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, int ntile, uint16_t* ws0,
                                          uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1, int wave0,
