@@ -274,24 +274,25 @@ moe_status forward_impl(const Request& q) {
     const char* ps = std::getenv("MOE_PERSIST"); // test knob: "0" keeps one workgroup per block
     const bool persist = balanced && !(ps && std::strcmp(ps, "0") == 0);
     if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
-    // decode-sized gate/up launches: the permutation picks a K split of 1 or 2 from the live block count
+    // decode-sized grouped GEMMs: the permutation picks a K split of 1 or 2 for each from the live block count
     const char* kss = std::getenv("MOE_KSPLIT"); // test knob: "1" never splits, "2" always does
     const bool ks_off = kss && std::strcmp(kss, "1") == 0, ks_on = kss && std::strcmp(kss, "2") == 0;
-    bool ksplit = false;
-    if (path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off) {
+    const bool ksplit = path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off;
+    int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
+    bool ks_gate_up = false; // the gate/up split needs a reduction launch: skipped when it can never pay
+    if (ksplit) {
         int cus = 0;
         MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
-        // the split needs two rounds of blocks: with at most one (every expert and the shared one active),
-        // no reduction is launched
-        const int ntn1 = moe::dma_ntn(true, I);
-        const int64_t most = (std::min<int64_t>(E, (int64_t)T * k) + moe::shared_tiles(T, BM)) * ntn1;
-        ksplit = ks_on || most > cus;
-        split.ks_ntn = ntn1;
+        split.ksplit = ks_flag;
+        split.ks_ntn[0] = moe::dma_ntn(true, I);
+        split.ks_ntn[1] = moe::dma_ntn(false, H);
         split.cus = cus;
         split.ks_force = ks_on ? 2 : 0;
+        // a split needs two rounds of blocks: with at most one (every expert and the shared one active)
+        // the gate/up reduction is not launched (the down GEMM's halves are added by the combine)
+        const int64_t most = (std::min<int64_t>(E, (int64_t)T * k) + moe::shared_tiles(T, BM)) * split.ks_ntn[0];
+        ks_gate_up = ks_on || most > cus;
     }
-    int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
-    split.ksplit = ks_flag;
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
                                 static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, split,
                                 s0),
@@ -333,13 +334,14 @@ moe_status forward_impl(const Request& q) {
     add_shared(r1, q.ws1, q.ws3);
     if (persist) r1.work_ctr = reinterpret_cast<unsigned long long*>(split.ctr);
     const int h_rows = T * k + (fold ? T : 0);
-    if (ksplit) {
+    if (ks_gate_up) {
         r1.ksplit_dev = ks_flag;
         r1.part = static_cast<float*>(at(L.ks_part));
         r1.part_rows = h_rows;
     }
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
-    if (ksplit) MOE_HIP(moe::launch_reduce_ksplit(r1.part, ks_flag, h_rows, I, h_perm, s0), "gate/up K-split reduction");
+    if (ks_gate_up)
+        MOE_HIP(moe::launch_reduce_ksplit(r1.part, ks_flag, h_rows, I, h_perm, s0), "gate/up K-split reduction");
     MOE_TRY(mark(4));
     moe::GemmArgs r2{};
     r2.act = h_perm;
@@ -354,12 +356,20 @@ moe_status forward_impl(const Request& q) {
     r2.K = I;
     r2.xcd_bounds = balanced ? split.bounds + (moe::kXcds + 1) : nullptr;
     r2.work_ctr = persist ? reinterpret_cast<unsigned long long*>(split.ctr) + moe::kXcds : nullptr;
+    float* y2 = ksplit ? static_cast<float*>(at(L.ks_part_down)) : nullptr;
+    if (ksplit) {
+        r2.ksplit_dev = ks_flag + 1;
+        r2.part = y2;
+        r2.part_rows = h_rows;
+    }
     add_shared(r2, q.ws2, nullptr);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
-    MOE_HIP(moe::launch_combine(y_perm, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out, s0),
+    MOE_HIP(moe::launch_combine(y_perm, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out, s0, y2,
+                                y2 != nullptr && fold ? y2 + (size_t)T * k * H : nullptr,
+                                ksplit ? ks_flag + 1 : nullptr),
             "combine");
     MOE_TRY(mark(6));
     return MOE_OK;

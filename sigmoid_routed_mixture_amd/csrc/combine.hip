@@ -18,11 +18,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ y_shared,
                                                       const uint16_t* __restrict__ resid, int T, int H, int k,
-                                                      float* __restrict__ out) {
+                                                      float* __restrict__ out, const float* __restrict__ y2,
+                                                      const float* __restrict__ y_shared2,
+                                                      const int32_t* __restrict__ ysplit) {
     __shared__ float g[kMaxK];
     __shared__ int rr[kMaxK];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    // the down GEMM split K in two: a row of y is its first half plus the same row of y2
+    const bool two = ysplit != nullptr && ysplit[0] == 2;
     if (tid < k) {
         g[tid] = gates[(size_t)t * k + tid];
         rr[tid] = slot_row[(size_t)t * k + tid];
@@ -41,6 +45,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 if (r >= 0) {
                     v0[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8);
                     v1[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8 + 4);
+                    if (two) {
+                        const float4 a = *reinterpret_cast<const float4*>(y2 + (size_t)r * H + c * 8);
+                        const float4 b = *reinterpret_cast<const float4*>(y2 + (size_t)r * H + c * 8 + 4);
+                        v0[jj] = make_float4(v0[jj].x + a.x, v0[jj].y + a.y, v0[jj].z + a.z, v0[jj].w + a.w);
+                        v1[jj] = make_float4(v1[jj].x + b.x, v1[jj].y + b.y, v1[jj].z + b.z, v1[jj].w + b.w);
+                    }
                 }
             }
 #pragma unroll
@@ -55,8 +65,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         }
         float* o = out + (size_t)t * H + c * 8;
         if (y_shared) {
-            const float4 s0 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8);
-            const float4 s1 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8 + 4);
+            float4 s0 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8);
+            float4 s1 = *reinterpret_cast<const float4*>(y_shared + (size_t)t * H + c * 8 + 4);
+            if (two) {
+                const float4 a = *reinterpret_cast<const float4*>(y_shared2 + (size_t)t * H + c * 8);
+                const float4 b = *reinterpret_cast<const float4*>(y_shared2 + (size_t)t * H + c * 8 + 4);
+                s0 = make_float4(s0.x + a.x, s0.y + a.y, s0.z + a.z, s0.w + a.w);
+                s1 = make_float4(s1.x + b.x, s1.y + b.y, s1.z + b.z, s1.w + b.w);
+            }
             acc[0] += s0.x; acc[1] += s0.y; acc[2] += s0.z; acc[3] += s0.w;
             acc[4] += s1.x; acc[5] += s1.y; acc[6] += s1.z; acc[7] += s1.w;
         }
@@ -76,11 +92,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 } // namespace
 
 hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream) {
+                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream, const float* y2,
+                          const float* y_shared2, const int32_t* ysplit) {
+    if (ysplit != nullptr && (y2 == nullptr || (y_shared != nullptr && y_shared2 == nullptr)))
+        return hipErrorInvalidValue;
     if (T <= 0) return hipSuccess;
     // few tokens: spread each token's row over several workgroups so every thread has one chunk
-    const int ysplit = T < 1024 ? (H / 8 + 255) / 256 : 1;
-    combine_kernel<<<dim3(T, ysplit), 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out);
+    const int ycols = T < 1024 ? (H / 8 + 255) / 256 : 1;
+    combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out, y2,
+                                                      y_shared2, ysplit);
     return hipGetLastError();
 }
 

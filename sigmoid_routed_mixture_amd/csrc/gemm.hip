@@ -627,6 +627,8 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         float* stg = reinterpret_cast<float*>(wave < 4 ? ws0 : ws1) + (wave & 3) * (16 * 68);
         const int c4 = lane & 15, r4 = lane >> 4;
         const int colw = ntile * 256 + 64 * wm;
+        // K split: the second half's rows go to the partial buffer, the combine adds them
+        float* yout = ks == 0 ? static_cast<float*>(a.out) : a.part;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
 #pragma unroll
@@ -640,7 +642,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
                 const int m = 16 * (2 * j + wn) + t;
                 const int col = colw + 4 * c4;
                 if (m < ti.rows && col < N)
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
+                    *reinterpret_cast<f32x4*>(yout + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
             }
             __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next block overwrites the area
         }
@@ -689,7 +691,7 @@ template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
     const int64_t bid = blockIdx.x;
     int ntile, S = 1, ks = 0;
-    if (!DENSE && KIND == GemmKind::GateUp && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
     TileInfo ti;
     if (DENSE) {
         ntile = (int)(bid % ntn);
@@ -973,7 +975,7 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     const int splits = (KIND == GemmKind::Logits || (!wide && DENSE)) && a.ksplit > 1 ? a.ksplit : 1;
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
-    if (KIND == GemmKind::GateUp && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {
+    if (KIND != GemmKind::Logits && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {
         if (a.part == nullptr || a.part_rows <= 0 || a.K < 2 * kBK) return hipErrorInvalidValue;
         blocks *= 2; // room for a K split of 2
     }

@@ -25,15 +25,15 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
 // at most cap[i] blocks). With `ctr` (8-byte aligned) it zeroes the 2 * kXcds 64-bit work counters of the
 // persistent DMA kernel (kXcds for each GEMM).
-// With `ksplit` it writes the gate/up K split (gate_up_ksplit of the live blocks, ks_ntn column tiles each,
-// on `cus` compute units; ks_force > 0 forces that split).
+// With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit of the live
+// blocks, ks_ntn[i] column tiles each, on `cus` compute units; ks_force > 0 forces that split).
 struct XcdSplit {
     int32_t* bounds;
     int ntn[2];
     int cap[2];
     int32_t* ctr;
     int32_t* ksplit;
-    int ks_ntn;
+    int ks_ntn[2];
     int cus;
     int ks_force;
 };
@@ -69,8 +69,9 @@ struct GemmArgs {
                                   // form (one workgroup per CU claiming blocks), or null for one block each
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
-    const int32_t* ksplit_dev; // DMA kernel, grouped gate/up: the K split (1 or 2) the permutation chose, or null
-    float* part;               // its fp32 partials [2][part_rows][2N] (g, then u) when the split is 2
+    const int32_t* ksplit_dev; // DMA kernel, grouped: the K split (1 or 2) the permutation chose, or null
+    float* part;               // with a split of 2: gate/up fp32 partials [2][part_rows][2N] (g, then u); down:
+                               // the second K half's fp32 rows [part_rows][N] (the first half goes to out)
     int part_rows;
 };
 enum class GemmKind { GateUp, DownF32, Logits };
@@ -86,9 +87,12 @@ hipError_t launch_reduce_ksplit(const float* partial, const int32_t* ksplit, int
 hipError_t device_cus(int& cus);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
-// residual (bf16) added last.
+// residual (bf16) added last. With `ysplit` (a device int) equal to 2 the down GEMM split K: each row of y
+// and y_shared is its first half plus the same row of y2 / y_shared2.
 hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream);
+                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream,
+                          const float* y2 = nullptr, const float* y_shared2 = nullptr,
+                          const int32_t* ysplit = nullptr);
 
 // out[t] = bf16(gamma * x[t] / sqrt(mean(x[t]^2) + eps)), computed in fp64.
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps, int T, int H, uint16_t* out,

@@ -79,10 +79,12 @@ __device__ __forceinline__ int append_shared_tiles(int4* __restrict__ tiles, int
     return routed_tiles + ns;
 }
 
-// The gate/up K split of a decode-sized launch (thread 0).
+// The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0).
 __device__ __forceinline__ void write_ksplit(const XcdSplit& sp, int all_tiles) {
     if (sp.ksplit != nullptr && threadIdx.x == 0)
-        sp.ksplit[0] = sp.ks_force > 0 ? sp.ks_force : gate_up_ksplit((int64_t)all_tiles * sp.ks_ntn, sp.cus);
+        for (int i = 0; i < 2; ++i)
+            sp.ksplit[i] =
+                sp.ks_force > 0 ? sp.ks_force : decode_ksplit((int64_t)all_tiles * sp.ks_ntn[i], sp.cus);
 }
 
 // The work-balanced XCD split (plan.h) of the tile list just built, for both column-tile counts. Thread e

@@ -97,8 +97,9 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     const size_t shp = dense_shared ? dense_partial_bytes(T, H, Is) : 0;
     L.sh_partial = shp > 0 ? take(shp) : size_t(-1);
     const bool ks = ksplit_possible(T, H, E, k, I, Is);
-    L.ks_flag = ks ? take(4) : size_t(-1);
+    L.ks_flag = ks ? take(8) : size_t(-1);
     L.ks_part = ks ? take(2 * rows * (size_t)I * 2 * 4) : size_t(-1);
+    L.ks_part_down = ks ? take(rows * (size_t)H * 4) : size_t(-1);
     L.x_norm = with_norm ? take((size_t)T * (size_t)H * 2) : size_t(-1); // last: the block layout extends the plain one
     L.total = off;
     return L;

@@ -124,13 +124,13 @@ constexpr bool shared_fold(int T, int E, int k, int I, int Is) {
     return Is > 0 && Is == I && (int64_t)T * k <= (int64_t)kSkinnyBM * E;
 }
 constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
-// Decode-sized gate/up GEMMs (the shared expert folded in, at most kKSplitMaxT tokens, K of at least two
+// Decode-sized grouped GEMMs (the shared expert folded in, at most kKSplitMaxT tokens, K of at least two
 // steps) may split K in two. Every CU runs one DMA block at a time, so a launch of b blocks takes
 // ceil(b / cus) rounds; from two rounds on, two half-length blocks per block pay when they round better,
 // counting about 5 % for the extra prologues and the fp32 partials (in one round the fixed costs win). The permutation picks the split from the live block
 // count, so the GEMM and the reduction that follows agree on it.
 constexpr int kKSplitMaxT = 64;
-constexpr int gate_up_ksplit(int64_t blocks, int cus) {
+constexpr int decode_ksplit(int64_t blocks, int cus) {
     if (blocks <= 0 || cus <= 0) return 1;
     const int64_t r1 = (blocks + cus - 1) / cus, r2 = (2 * blocks + cus - 1) / cus;
     return r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1; // one round already: no split; else 0.525 r2 < r1
@@ -143,15 +143,16 @@ constexpr int kTileEntryBytes = 16;
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present
     size_t ids, gates, counts, offsets, row_token, slot_row, chunk_base, tiles, ntiles, xcd_bounds, partial,
-        h_perm, y_perm, h_sh, y_sh, sh_partial, x_norm, ks_flag, ks_part;
+        h_perm, y_perm, h_sh, y_sh, sh_partial, x_norm, ks_flag, ks_part, ks_part_down;
     size_t total;
 };
 // with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.
-// ks_flag / ks_part: the device's K-split choice (one int) and the gate/up partials [2][T·k + T][2I] fp32
-// of a decode-sized launch (ksplit_possible), else not present.
+// ks_flag / ks_part / ks_part_down: the device's K-split choices (gate/up, down: two ints), the gate/up
+// partials [2][T·k + T][2I] fp32 and the down GEMM's second-half rows [T·k + T][H] fp32 of a decode-sized
+// launch (ksplit_possible), else not present.
 Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm = false);
 constexpr bool ksplit_possible(int T, int H, int E, int k, int I, int Is) {
-    return shared_fold(T, E, k, I, Is) && T <= kKSplitMaxT && H >= 128;
+    return shared_fold(T, E, k, I, Is) && T <= kKSplitMaxT && H >= 128 && I >= 128; // a K step per half
 }
 size_t permute_scratch_bytes(int T, int E);
 

@@ -72,9 +72,11 @@ int main() {
                             CHECK((L.ks_flag != size_t(-1)) == moe::ksplit_possible(T, H, E, k, I, Is) &&
                                       (L.ks_part != size_t(-1)) == (L.ks_flag != size_t(-1)),
                                   "K-split regions (T=%d E=%d k=%d I=%d Is=%d)", T, E, k, I, Is);
+                            CHECK((L.ks_part_down != size_t(-1)) == (L.ks_flag != size_t(-1)), "K-split down rows");
                             if (L.ks_flag != size_t(-1)) {
-                                rs.push_back({L.ks_flag, 4, "ks_flag"});
+                                rs.push_back({L.ks_flag, 8, "ks_flag"});
                                 rs.push_back({L.ks_part, 2 * rows * I * 2 * 4, "ks_part"});
+                                rs.push_back({L.ks_part_down, rows * H * 4, "ks_part_down"});
                             }
                             rs.push_back({L.x_norm, (size_t)T * H * 2, "x_norm"});
                             for (size_t i = 0; i < rs.size(); ++i) {
@@ -148,15 +150,15 @@ int main() {
     std::printf("%d block orders checked\n", orders);
 
     // K split of decode-sized gate/up launches: split when two half-length rounds beat one (5 % margin)
-    CHECK(moe::gate_up_ksplit(1312, 256) == 2 && moe::gate_up_ksplit(1536, 256) == 1 &&
-              moe::gate_up_ksplit(272, 256) == 2 && moe::gate_up_ksplit(144, 256) == 1 &&
-              moe::gate_up_ksplit(17, 256) == 1 && moe::gate_up_ksplit(0, 256) == 1 &&
-              moe::gate_up_ksplit(100, 0) == 1,
-          "gate_up_ksplit");
+    CHECK(moe::decode_ksplit(1312, 256) == 2 && moe::decode_ksplit(1536, 256) == 1 &&
+              moe::decode_ksplit(272, 256) == 2 && moe::decode_ksplit(144, 256) == 1 &&
+              moe::decode_ksplit(17, 256) == 1 && moe::decode_ksplit(0, 256) == 1 &&
+              moe::decode_ksplit(100, 0) == 1,
+          "decode_ksplit");
     for (int64_t b = 1; b < 5000; b += 7)
         for (int cus : {80, 256, 304}) {
             const int64_t r1 = (b + cus - 1) / cus, r2 = (2 * b + cus - 1) / cus;
-            CHECK(moe::gate_up_ksplit(b, cus) == (r1 >= 2 && 0.525 * (double)r2 < (double)r1 ? 2 : 1),
+            CHECK(moe::decode_ksplit(b, cus) == (r1 >= 2 && 0.525 * (double)r2 < (double)r1 ? 2 : 1),
                   "split b=%lld cus=%d", (long long)b, cus);
         }
     // block claims of the persistent kernel: any interleaving of front (home) and back (other XCDs) claims

@@ -114,8 +114,9 @@ def test_forward_parity(moe, name):
 
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "glm47_decode"])
 @pytest.mark.parametrize("ks", ["1", "2"])
-def test_decode_gate_up_k_split(moe, monkeypatch, name, ks):
-    # decode-sized gate/up launches with the K split forced off and on, against the oracle on every token
+def test_decode_k_split(moe, monkeypatch, name, ks):
+    # decode-sized grouped GEMMs (gate/up with its reduction, down with the combine adding the halves) with
+    # the K split forced off and on, against the oracle on every token
     say("[K split %s] %s" % (ks, name))
     monkeypatch.setenv("MOE_KSPLIT", ks)
     cfg, h, d = case(name)
