@@ -26,12 +26,17 @@
  *  - `stream` is a hipStream_t (NULL: the default stream). All work is enqueued on it and the call
  *    returns without synchronising; results are ready when the stream's work completes.
  *  - The caller owns every buffer and stream. The library never allocates or frees device memory and
- *    never copies to the host. Its only state is one pair of HIP events per device, made on first use.
+ *    never copies to the host. Its only state, made on first use per device, is one pair of HIP events
+ *    (for stream_shared) and the device's compute-unit count (it sizes the persistent GEMM grids).
  *  - Arguments are checked before anything is enqueued: a call that returns an error has no effect.
  *    T == 0 returns MOE_OK once the sizes pass their checks, without looking at any pointer, and
  *    enqueues nothing. Non-finite inputs are outside the contract.
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H, I and Is multiples of 64, T * k < 2^31.
  *  - Calls on one stream run in order; overlapping calls that share output or workspace buffers race.
+ *  - Environment variables read on every call, for tests only: MOE_GEMM_PATH (wide | tall | dma | skinny)
+ *    forces one GEMM kernel; MOE_XCD_SPLIT=count, MOE_PERSIST=0 and MOE_KSPLIT (1 | 2) change how GEMM
+ *    blocks are spread over the chip or split along K. Unset, the library picks by size. Every choice
+ *    computes the same layer; only a K split or a different kernel changes the fp32 summation order.
  */
 #ifndef SIGMOID_ROUTED_MIXTURE_MOE_H
 #define SIGMOID_ROUTED_MIXTURE_MOE_H
