@@ -117,8 +117,10 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
  *                                routed experts; it waits for work already on `stream` and `stream` waits
  *                                for it before the combine. NULL runs the shared expert on `stream`.
  * Expert GEMMs take bf16 operands with fp32 accumulation; the SwiGLU activation h is stored as bf16
- * between the two GEMMs (it is the down GEMM's bf16 MFMA operand); per-slot expert outputs are fp32;
- * the combine sums the k gated slots in slot order plus the shared expert in fp32.
+ * between the two GEMMs (it is the down GEMM's bf16 MFMA operand); per-slot expert outputs are stored as
+ * bf16 when k >= 8 (their roundings then partly cancel in the gated sum) unless the shared expert runs as
+ * one more group of the routed GEMMs (when 0 < Is == I and T * k <= 16 * E), else as fp32; the combine sums
+ * the k gated slots in slot order plus the shared expert in fp32.
  * Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (g = x W1, u = x W3,
  * a = g sigma(g), h = a * u, E_i = h W2, y_routed = sum G_i E_i, the shared expert, delta_ffn =
  * y_routed + y_shared); nnterp glm_moe_dsa "The mixture" (routed + shared == mlp_output).

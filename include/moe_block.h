@@ -34,8 +34,8 @@ extern "C" {
  *                                        per expert however many of its slots name it)
  *   workspace           at least moe_workspace_bytes(T, H, E, k, I, Is) bytes
  *   stream, stream_shared                as for moe_forward
- * Numerics as moe_forward: bf16 operands, fp32 accumulation, bf16 h between the GEMMs, fp32 per-slot rows
- * and fp32 combine in slot order.
+ * Numerics as moe_forward: bf16 operands, fp32 accumulation, bf16 h between the GEMMs, per-slot rows bf16
+ * or fp32 by the same rule, and fp32 combine in slot order.
  */
 moe_status moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_gates,
                               const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1,

@@ -222,7 +222,7 @@ moe_status forward_impl(const Request& q) {
     int4* tiles = static_cast<int4*>(at(L.tiles));
     int32_t* ntiles = static_cast<int32_t*>(at(L.ntiles));
     uint16_t* h_perm = static_cast<uint16_t*>(at(L.h_perm));
-    float* y_perm = static_cast<float*>(at(L.y_perm));
+    float* y_perm = static_cast<float*>(at(L.y_perm)); // per-slot rows, fp32 or bf16 (slot_rows_bf16)
     // The shared expert: one more group of the routed GEMMs (rows T * k onwards of h_perm and y_perm) when
     // it has the routed width, else a dense MLP of its own.
     const bool fold = moe::shared_fold(T, E, k, I, Is);
@@ -363,12 +363,14 @@ moe_status forward_impl(const Request& q) {
         r2.part_rows = h_rows;
     }
     add_shared(r2, q.ws2, nullptr);
+    const bool ybf = moe::slot_rows_bf16(T, E, k, I, Is) && !ksplit;
+    r2.out_bf16 = ybf ? 1 : 0;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
-    MOE_HIP(moe::launch_combine(y_perm, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out, s0, y2,
-                                y2 != nullptr && fold ? y2 + (size_t)T * k * H : nullptr,
+    MOE_HIP(moe::launch_combine(y_perm, ybf, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out,
+                                s0, y2, y2 != nullptr && fold ? y2 + (size_t)T * k * H : nullptr,
                                 ksplit ? ks_flag + 1 : nullptr),
             "combine");
     MOE_TRY(mark(6));

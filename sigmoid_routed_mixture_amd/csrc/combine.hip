@@ -1,6 +1,6 @@
 // Gate-weighted combine on gfx950: out[t] = sum_j G[t, j] * y[slot_row[t, j]] + y_shared[t] (+ x'[t]), in
 // fp32 with the k slots added in slot order, then the shared expert, then (block entry point) the residual
-// stream. The per-slot expert outputs y are fp32 rows.
+// stream. The per-slot expert outputs y are fp32 or bf16 rows (widened to fp32 exactly), y_shared fp32.
 // Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (y_routed = sum_i G_i E_i,
 // delta_ffn = y_routed + y_shared, x_{n+1} = x'_n + delta_ffn); nnterp encyclopedia glm_moe_dsa, "The
 // mixture" (routed + shared == out).
@@ -11,10 +11,24 @@
 namespace moe {
 namespace {
 
+// 8 consecutive values of a per-slot row as fp32.
+__device__ __forceinline__ void load_row8(const float* y, size_t i, float4& a, float4& b) {
+    a = *reinterpret_cast<const float4*>(y + i);
+    b = *reinterpret_cast<const float4*>(y + i + 4);
+}
+__device__ __forceinline__ void load_row8(const uint16_t* y, size_t i, float4& a, float4& b) {
+    const Pack16 q = load16(y + i);
+    a = make_float4(bf16_to_f32((uint16_t)(q.w[0] & 0xFFFFu)), bf16_to_f32((uint16_t)(q.w[0] >> 16)),
+                    bf16_to_f32((uint16_t)(q.w[1] & 0xFFFFu)), bf16_to_f32((uint16_t)(q.w[1] >> 16)));
+    b = make_float4(bf16_to_f32((uint16_t)(q.w[2] & 0xFFFFu)), bf16_to_f32((uint16_t)(q.w[2] >> 16)),
+                    bf16_to_f32((uint16_t)(q.w[3] & 0xFFFFu)), bf16_to_f32((uint16_t)(q.w[3] >> 16)));
+}
+
 // One workgroup per (token, column range); each thread owns 8-column chunks (16-byte loads and stores).
 // The k slot rows of a chunk are loaded eight at a time before any is added, so their latencies overlap;
 // they are added in slot order.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ gates,
+template <typename Y>
+__global__ __launch_bounds__(256) void combine_kernel(const Y* __restrict__ y, const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ y_shared,
                                                       const uint16_t* __restrict__ resid, int T, int H, int k,
@@ -43,8 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 const int j = j0 + jj;
                 const int r = j < k ? rr[j] : -1;
                 if (r >= 0) {
-                    v0[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8);
-                    v1[jj] = *reinterpret_cast<const float4*>(y + (size_t)r * H + c * 8 + 4);
+                    load_row8(y, (size_t)r * H + c * 8, v0[jj], v1[jj]);
                     if (two) {
                         const float4 a = *reinterpret_cast<const float4*>(y2 + (size_t)r * H + c * 8);
                         const float4 b = *reinterpret_cast<const float4*>(y2 + (size_t)r * H + c * 8 + 4);
@@ -91,16 +104,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 } // namespace
 
-hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream, const float* y2,
-                          const float* y_shared2, const int32_t* ysplit) {
-    if (ysplit != nullptr && (y2 == nullptr || (y_shared != nullptr && y_shared2 == nullptr)))
+hipError_t launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* slot_row,
+                          const float* y_shared, const uint16_t* resid, int T, int H, int k, float* out,
+                          hipStream_t stream, const float* y2, const float* y_shared2, const int32_t* ysplit) {
+    if (ysplit != nullptr && (y_bf16 || y2 == nullptr || (y_shared != nullptr && y_shared2 == nullptr)))
         return hipErrorInvalidValue;
     if (T <= 0) return hipSuccess;
     // few tokens: spread each token's row over several workgroups so every thread has one chunk
     const int ycols = T < 1024 ? (H / 8 + 255) / 256 : 1;
-    combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(y, gates, slot_row, y_shared, resid, T, H, k, out, y2,
-                                                      y_shared2, ysplit);
+    if (y_bf16)
+        combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(static_cast<const uint16_t*>(y), gates, slot_row, y_shared,
+                                                          resid, T, H, k, out, y2, y_shared2, ysplit);
+    else
+        combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(static_cast<const float*>(y), gates, slot_row, y_shared,
+                                                          resid, T, H, k, out, y2, y_shared2, ysplit);
     return hipGetLastError();
 }
 

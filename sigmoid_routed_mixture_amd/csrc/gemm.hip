@@ -291,6 +291,13 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const TileInfo& ti,
                 const int col = col0 + i * 16 + 4 * kg;
                 if (col >= N) continue;
                 const f32x4 y = acc[i][j];
+                if (KIND == GemmKind::DownF32 && !DENSE && a.out_bf16) { // per-slot rows as bf16 (N % 64 == 0)
+                    uint2 v;
+                    v.x = pack_bf16x2(y[0], y[1]);
+                    v.y = pack_bf16x2(y[2], y[3]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                    continue;
+                }
                 float* o = static_cast<float*>(a.out) + (size_t)split * a.dense_rows * N + row * N + col;
                 if (col + 3 < N) {
                     *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
@@ -620,9 +627,9 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     }
 
     if constexpr (KIND == GemmKind::DownF32) {
-        // fp32 rows leave through LDS: each wave turns one 16-token block at a time into 16 rows of its 64
-        // features (256 contiguous bytes per row) in a private 4.25 KB area of ws0 / ws1 (row stride 68
-        // floats), then stores whole rows
+        // rows leave through LDS: each wave turns one 16-token block at a time into 16 rows of its 64
+        // features in a private 4.25 KB area of ws0 / ws1 (fp32, row stride 68 floats), then stores whole
+        // row segments (256 contiguous bytes per fp32 row, 128 per bf16 row)
         __syncthreads(); // every wave is done reading the operand buffers
         float* stg = reinterpret_cast<float*>(wave < 4 ? ws0 : ws1) + (wave & 3) * (16 * 68);
         const int c4 = lane & 15, r4 = lane >> 4;
@@ -635,14 +642,35 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<f32x4*>(stg + rl * 68 + 16 * i + 4 * kg) = acc[i][j];
             __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the block is in LDS
+            if (!DENSE && a.out_bf16) {
+                // bf16 rows (N % 64 == 0, no K split): 8 lanes of 16 bytes per row segment, 8 rows per store
+                const int c8 = lane & 7, r8 = lane >> 3;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int t = 4 * p + r4;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 68 + 4 * c4);
-                const int m = 16 * (2 * j + wn) + t;
-                const int col = colw + 4 * c4;
-                if (m < ti.rows && col < N)
-                    *reinterpret_cast<f32x4*>(yout + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
+                for (int p = 0; p < 2; ++p) {
+                    const int t = 8 * p + r8;
+                    const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg + t * 68 + 8 * c8);
+                    const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg + t * 68 + 8 * c8 + 4);
+                    const int m = 16 * (2 * j + wn) + t;
+                    const int col = colw + 8 * c8;
+                    if (m < ti.rows && col < N) {
+                        Pack16 q;
+                        q.w[0] = pack_bf16x2(v0[0], v0[1]);
+                        q.w[1] = pack_bf16x2(v0[2], v0[3]);
+                        q.w[2] = pack_bf16x2(v1[0], v1[1]);
+                        q.w[3] = pack_bf16x2(v1[2], v1[3]);
+                        store16(static_cast<uint16_t*>(a.out) + ((size_t)ti.off + ti.m0 + m) * N + col, q);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int t = 4 * p + r4;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 68 + 4 * c4);
+                    const int m = 16 * (2 * j + wn) + t;
+                    const int col = colw + 4 * c4;
+                    if (m < ti.rows && col < N)
+                        *reinterpret_cast<f32x4*>(yout + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
+                }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next block overwrites the area
         }
@@ -891,6 +919,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int ntn, i
             const int col = col0 + b * 16 + 4 * kg;
             if (col >= N) continue;
             const f32x4 y = acc[b];
+            if (KIND == GemmKind::DownF32 && !DENSE && a.out_bf16) { // per-slot rows as bf16
+                uint2 v;
+                v.x = pack_bf16x2(y[0], y[1]);
+                v.y = pack_bf16x2(y[2], y[3]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                continue;
+            }
             *reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * N + col) = make_float4(y[0], y[1], y[2], y[3]);
         }
     }
@@ -966,6 +1001,9 @@ hipError_t cu_count(int& cus) {
 
 template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
+    // bf16 output rows: grouped down GEMMs only, whole 64-column chunks, no K split
+    if (a.out_bf16 && (KIND != GemmKind::DownF32 || DENSE || a.N % 64 != 0 || a.ksplit_dev != nullptr))
+        return hipErrorInvalidValue;
     const bool wide = path != GemmPath::Skinny;
     int ntn;
     if (wide)

@@ -51,7 +51,7 @@ struct GemmArgs {
     const int32_t* row_token;  // gather map row -> activation row (gate/up GEMM of routed experts), or null
     const uint16_t* w_a;       // weights [groups][N][K] (down: W2; gate/up: W1)
     const uint16_t* w_b;       // gate/up only: W3 [groups][N][K]
-    void* out;                 // [rows, N]: bf16 (h or per-slot outputs) or fp32
+    void* out;                 // [rows, N]: bf16 (h; grouped down with out_bf16) or fp32
     const int32_t* counts;     // rows per group, or null for one dense group
     const int32_t* offsets;    // first row of each group
     const int4* tiles;         // per tile {group | tile height << 16, first row in the group, rows of the group,
@@ -73,6 +73,7 @@ struct GemmArgs {
     float* part;               // with a split of 2: gate/up fp32 partials [2][part_rows][2N] (g, then u); down:
                                // the second K half's fp32 rows [part_rows][N] (the first half goes to out)
     int part_rows;
+    int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32
 };
 enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);
@@ -87,11 +88,12 @@ hipError_t launch_reduce_ksplit(const float* partial, const int32_t* ksplit, int
 hipError_t device_cus(int& cus);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
-// residual (bf16) added last. With `ysplit` (a device int) equal to 2 the down GEMM split K: each row of y
-// and y_shared is its first half plus the same row of y2 / y_shared2.
-hipError_t launch_combine(const float* y, const float* gates, const int32_t* slot_row, const float* y_shared,
-                          const uint16_t* resid, int T, int H, int k, float* out, hipStream_t stream,
-                          const float* y2 = nullptr, const float* y_shared2 = nullptr,
+// residual (bf16) added last. The rows of y are bf16 when y_bf16, else fp32; y_shared is fp32. With
+// `ysplit` (a device int) equal to 2 the down GEMM split K: each row of y and y_shared is its first half
+// plus the same row of y2 / y_shared2 (fp32 rows only).
+hipError_t launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* slot_row,
+                          const float* y_shared, const uint16_t* resid, int T, int H, int k, float* out,
+                          hipStream_t stream, const float* y2 = nullptr, const float* y_shared2 = nullptr,
                           const int32_t* ysplit = nullptr);
 
 // out[t] = bf16(gamma * x[t] / sqrt(mean(x[t]^2) + eps)), computed in fp64.

@@ -124,6 +124,12 @@ constexpr bool shared_fold(int T, int E, int k, int I, int Is) {
     return Is > 0 && Is == I && (int64_t)T * k <= (int64_t)kSkinnyBM * E;
 }
 constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
+// The down GEMM's per-slot rows (read back once by the combine) are stored as bf16 when every token has at
+// least 8 gated slots and the shared expert is not folded in (so neither a K split nor shared rows are among
+// them), else as fp32. A bf16 row adds one rounding of each slot's output before the fp32 weighted sum; over
+// 8 or more slots these roundings partly cancel (simulated worst case about 0.010 x the output RMS at k = 8,
+// 0.013-0.015 at k = 4 and up to 0.020 at k = 1, where h's own bf16 rounding alone gives 0.008-0.012).
+constexpr bool slot_rows_bf16(int T, int E, int k, int I, int Is) { return k >= 8 && !shared_fold(T, E, k, I, Is); }
 // Decode-sized grouped GEMMs (the shared expert folded in, at most kKSplitMaxT tokens, K of at least two
 // steps) may split K in two. Every CU runs one DMA block at a time, so a launch of b blocks takes
 // ceil(b / cus) rounds; from two rounds on, two half-length blocks per block pay when they round better,

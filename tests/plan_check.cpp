@@ -73,6 +73,10 @@ int main() {
                                       (L.ks_part != size_t(-1)) == (L.ks_flag != size_t(-1)),
                                   "K-split regions (T=%d E=%d k=%d I=%d Is=%d)", T, E, k, I, Is);
                             CHECK((L.ks_part_down != size_t(-1)) == (L.ks_flag != size_t(-1)), "K-split down rows");
+                            // bf16 per-slot rows never meet a K split or folded shared rows, and need 8 slots
+                            CHECK(!moe::slot_rows_bf16(T, E, k, I, Is) ||
+                                      (!fold && k >= 8 && !moe::ksplit_possible(T, H, E, k, I, Is)),
+                                  "bf16 per-slot rows (T=%d E=%d k=%d)", T, E, k);
                             if (L.ks_flag != size_t(-1)) {
                                 rs.push_back({L.ks_flag, 8, "ks_flag"});
                                 rs.push_back({L.ks_part, 2 * rows * I * 2 * 4, "ks_part"});
