@@ -456,8 +456,8 @@ __device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
     return -1;
 }
 
-// One tile of the DMA GEMM. Persistent kernel (PERSIST): `wave0` is the wave index (a scalar); after the K
-// loop thread 0 claims the workgroup's next block, which wave 0 holds in `got` (-1: none left). With a K
+// One tile of the DMA GEMM. Persistent kernel (PERSIST): `wave0` is the wave index (a scalar); after the
+// tile's stores thread 0 claims the workgroup's next block, which wave 0 holds in `got` (-1: none left). With a K
 // split S of 2 (decode-sized gate/up launches) the tile computes K range `ks` and writes fp32 partials of g
 // and u instead of h.
 template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST>
@@ -620,11 +620,15 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     if (s + 3 < nk) step(ws0, xs1, ws1, xs0, s + 3);
     if (s + 4 < nk) step(ws1, xs0, ws2, xs1, s + 4);
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
-    if constexpr (PERSIST) {
-        int claim = -1;
-        if (tid == 0) claim = grab_block(a, ntn, (int)(blockIdx.x % kXcds));
-        if (wave == 0) got = __builtin_amdgcn_readfirstlane(claim);
-    }
+    // persistent form: thread 0 claims the next block once the tile's stores are issued, so the claim's round
+    // trip overlaps their drain
+    auto claim_next = [&]() {
+        if constexpr (PERSIST) {
+            int claim = -1;
+            if (tid == 0) claim = grab_block(a, ntn, (int)(blockIdx.x % kXcds));
+            if (wave == 0) got = __builtin_amdgcn_readfirstlane(claim);
+        }
+    };
 
     if constexpr (KIND == GemmKind::DownF32) {
         // rows leave through LDS: each wave turns one 16-token block at a time into 16 rows of its 64
@@ -694,6 +698,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
                     *reinterpret_cast<f32x4*>(prow + N + col) = acc[i + 2][j];
                 }
             }
+            claim_next();
             return;
         }
 #pragma unroll
@@ -713,6 +718,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
             }
         }
     }
+    claim_next();
 }
 
 template <GemmKind KIND, bool DENSE>
