@@ -51,7 +51,7 @@ def forward_routed(m, cfg, d, ids, gates, x=None, stream_shared=None):
 # ---------------------------------------------------------------------------------------------------
 # routing given by the caller
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "glm5_decode", "glm47_decode"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "glm5_decode", "glm47_decode", "glm5_prefill"])
 def test_routed_with_own_routing_is_forward_bitwise(moe, name):
     """moe_forward_routed fed moe_forward's own ids and gates runs the same kernels on the same bytes."""
     say("[routed = forward] %s" % name)
