@@ -55,13 +55,16 @@ typedef enum moe_status {
     MOE_ERR_INVALID_ARG = 1, /* null required pointer, T < 0, H/E/I <= 0, k < 1, k > E, Is < 0 */
     MOE_ERR_UNSUPPORTED = 2, /* E > 256, k > 32, H/I/Is not a multiple of 64, T * k >= 2^31 */
     MOE_ERR_MISALIGNED = 3,  /* a tensor not 16-byte aligned, or the workspace not 256-byte aligned */
-    MOE_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than moe_workspace_bytes(...) */
+    MOE_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than this call's sizes need (never more than the
+                                matching *_workspace_bytes query returns) */
     MOE_ERR_HIP = 5          /* a HIP launch or event call failed; moe_last_error() has the text */
 } moe_status;
 
 /*
- * Bytes of workspace moe_forward needs for these sizes (an upper bound that does not depend on the
- * routing). Pure host arithmetic: no device access. Returns 0 when the sizes are invalid or unsupported.
+ * Bytes of workspace moe_forward needs for up to T tokens at these sizes: an upper bound that does not
+ * depend on the routing and covers every token count from 0 to T (the layout is not monotone in T, so the
+ * query returns the largest one), so one workspace sized for the largest batch serves every smaller one.
+ * Pure host arithmetic: no device access. Returns 0 when the sizes are invalid or unsupported.
  */
 size_t moe_workspace_bytes(int T, int H, int E, int k, int I, int Is);
 

@@ -45,7 +45,7 @@ moe_status moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const 
 
 /*
  * Workspace bytes of moe_block_forward (moe_workspace_bytes plus a [T, H] bf16 region for the normalised
- * stream). 0 when the sizes are invalid or unsupported.
+ * stream), for up to T tokens like moe_workspace_bytes. 0 when the sizes are invalid or unsupported.
  */
 size_t moe_block_workspace_bytes(int T, int H, int E, int k, int I, int Is);
 
@@ -75,7 +75,8 @@ moe_status moe_block_forward(const moe_bf16* resid, const moe_bf16* gamma, doubl
                              float* topk_gates, int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                              void* stream, void* stream_shared);
 
-/* Workspace bytes of moe_dense_mlp: h [T, I] bf16. 0 when the sizes are invalid or unsupported. */
+/* Workspace bytes of moe_dense_mlp for up to T tokens: h [T, I] bf16 and, at few tokens, the fp32 partials
+ * of the split-K GEMMs. 0 when the sizes are invalid or unsupported. */
 size_t moe_dense_mlp_workspace_bytes(int T, int H, int I);
 
 /*

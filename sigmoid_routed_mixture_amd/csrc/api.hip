@@ -430,7 +430,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_workspace_bytes(int T, int H, int E, int k, int I, int Is) {
     if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) return 0;
-    return moe::forward_layout(T, H, E, k, I, Is).total;
+    return moe::forward_workspace_bound(T, H, E, k, I, Is);
 }
 
 size_t moe_permute_workspace_bytes(int T, int E) {
@@ -510,7 +510,7 @@ moe_status moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const 
 
 size_t moe_block_workspace_bytes(int T, int H, int E, int k, int I, int Is) {
     if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) return 0;
-    return moe::forward_layout(T, H, E, k, I, Is, true).total;
+    return moe::forward_workspace_bound(T, H, E, k, I, Is, true);
 }
 
 moe_status moe_block_forward(const moe_bf16* resid, const moe_bf16* gamma, double eps, const moe_bf16* w_router,
@@ -534,7 +534,7 @@ moe_status moe_block_forward(const moe_bf16* resid, const moe_bf16* gamma, doubl
 
 size_t moe_dense_mlp_workspace_bytes(int T, int H, int I) {
     if (!moe::check_dense_sizes(T, H, I).ok()) return 0;
-    return moe::dense_workspace_bytes(T, H, I);
+    return moe::dense_workspace_bound(T, H, I);
 }
 
 moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* w3, const moe_bf16* w2, int T,

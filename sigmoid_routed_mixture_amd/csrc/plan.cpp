@@ -137,6 +137,35 @@ size_t dense_workspace_bytes(int T, int H, int Id) {
     return hb + align_up(dense_partial_bytes(T, H, Id), 256);
 }
 
+namespace {
+// Workspace sizes are not monotone in T: regions appear and vanish with the regimes (the shared-expert fold,
+// the decode K split, the dense shared expert), and the router's and the dense GEMMs' K splits step down as
+// T grows. Between consecutive candidates below every region grows with T, so the largest size over
+// T' <= T is the largest over T and the candidates: the multiples of 16 (the 16- and 128-row tile
+// boundaries where the splits step down; past 32768 rows no split is left) and the last T of the fold and
+// K-split regimes.
+template <typename F>
+size_t max_over_smaller(int T, int fold_end, F size_at) {
+    size_t best = size_at(T);
+    const int lim = std::min(T - 1, 32768);
+    for (int t = 16; t <= lim; t += 16) best = std::max(best, size_at(t));
+    for (int t : {fold_end, std::min(fold_end, kKSplitMaxT)})
+        if (t >= 0 && t < T) best = std::max(best, size_at(t));
+    return best;
+}
+} // namespace
+
+size_t forward_workspace_bound(int T, int H, int E, int k, int I, int Is, bool with_norm) {
+    // last T with the shared expert folded in (T * k <= kSkinnyBM * E), when it can fold at all
+    const int fold_end = Is > 0 && Is == I ? (int)std::min<int64_t>((int64_t)kSkinnyBM * E / k, INT32_MAX) : -1;
+    return max_over_smaller(T, fold_end,
+                            [&](int t) { return forward_layout(t, H, E, k, I, Is, with_norm).total; });
+}
+
+size_t dense_workspace_bound(int T, int H, int Id) {
+    return max_over_smaller(T, -1, [&](int t) { return dense_workspace_bytes(t, H, Id); });
+}
+
 size_t permute_scratch_bytes(int T, int E) {
     const size_t chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
     return align_up(std::max<size_t>(chunks * (size_t)E * 4, 1), 256);

@@ -160,6 +160,9 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm 
 constexpr bool ksplit_possible(int T, int H, int E, int k, int I, int Is) {
     return shared_fold(T, E, k, I, Is) && T <= kKSplitMaxT && H >= 128 && I >= 128; // a K step per half
 }
+// What a caller allocates for up to T tokens: the largest forward_layout(T', ...).total over T' <= T (the
+// layouts are not monotone in T), so one workspace sized for the largest batch serves every smaller one.
+size_t forward_workspace_bound(int T, int H, int E, int k, int I, int Is, bool with_norm = false);
 size_t permute_scratch_bytes(int T, int E);
 
 // K ranges of a dense GEMM (rows x N outputs, reduction K) on the weight-streaming kernel: enough for
@@ -172,5 +175,7 @@ size_t dense_partial_bytes(int T, int H, int Id);
 // split partials.
 Check check_dense_sizes(int T, int H, int Id);
 size_t dense_workspace_bytes(int T, int H, int Id);
+// The largest dense_workspace_bytes(T', H, Id) over T' <= T.
+size_t dense_workspace_bound(int T, int H, int Id);
 
 } // namespace moe

@@ -153,6 +153,34 @@ int main() {
     }
     std::printf("%d block orders checked\n", orders);
 
+    // workspace queries: the largest layout over every T' <= T, so a workspace sized for the largest batch
+    // serves every smaller one (brute force over T' for small T, sampled T up to past the split ranges)
+    {
+        struct Shape { int H, E, k, I, Is; };
+        const Shape shapes[] = {{6144, 256, 8, 2048, 2048}, {2048, 64, 4, 1536, 1536}, {256, 16, 4, 128, 128},
+                                {192, 8, 8, 64, 0}, {256, 32, 1, 128, 192}, {64, 1, 1, 64, 64},
+                                {6144, 256, 8, 2048, 0}, {128, 4, 2, 128, 128}};
+        for (const Shape& q : shapes) {
+            for (int norm = 0; norm < 2; ++norm) {
+                size_t run = 0, prev = 0;
+                for (int T = 0; T <= 40000; ++T) {
+                    run = std::max(run, moe::forward_layout(T, q.H, q.E, q.k, q.I, q.Is, norm).total);
+                    if (T > 1500 && T % 97 != 0 && T != 32768 && T != 32769) continue;
+                    const size_t b = moe::forward_workspace_bound(T, q.H, q.E, q.k, q.I, q.Is, norm);
+                    CHECK(b == run && b >= prev, "forward bound T=%d H=%d E=%d k=%d I=%d Is=%d norm=%d: %zu vs %zu",
+                          T, q.H, q.E, q.k, q.I, q.Is, norm, b, run);
+                    prev = b;
+                }
+            }
+            size_t run = 0;
+            for (int T = 0; T <= 20000; ++T) {
+                run = std::max(run, moe::dense_workspace_bytes(T, q.H, q.I));
+                if (T > 1500 && T % 97 != 0) continue;
+                CHECK(moe::dense_workspace_bound(T, q.H, q.I) == run, "dense bound T=%d H=%d I=%d", T, q.H, q.I);
+            }
+        }
+    }
+
     // K split of decode-sized gate/up launches: split when two half-length rounds beat one (5 % margin)
     CHECK(moe::decode_ksplit(1312, 256) == 2 && moe::decode_ksplit(1536, 256) == 1 &&
               moe::decode_ksplit(272, 256) == 2 && moe::decode_ksplit(144, 256) == 1 &&

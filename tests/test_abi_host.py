@@ -103,6 +103,17 @@ def test_workspace_bytes(lib):
     assert lib.moe_permute_workspace_bytes(1000, 64) >= 4 * 64 * 4
 
 
+@pytest.mark.parametrize("shape", [(6144, 256, 8, 2048, 2048), (2048, 64, 4, 1536, 1536), (256, 16, 4, 128, 128)])
+def test_workspace_queries_never_shrink_with_T(lib, shape):
+    # a workspace sized for the largest batch must serve every smaller one: the layout loses regions as T
+    # grows (the decode K split past 64 tokens, the folded shared expert), so the queries take the largest
+    H, E, k, I, Is = shape
+    for q, args in ((lib.moe_workspace_bytes, (H, E, k, I, Is)), (lib.moe_block_workspace_bytes, (H, E, k, I, Is)),
+                    (lib.moe_dense_mlp_workspace_bytes, (H, I))):
+        sizes = [q(T, *args) for T in range(0, 1200)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:])), q.__name__
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), INVALID), (dict(H=0), INVALID), (dict(E=0), INVALID), (dict(k=0), INVALID),
     (dict(k=17), INVALID), (dict(E=300, k=4), UNSUPPORTED), (dict(E=64, k=33), UNSUPPORTED),
