@@ -51,6 +51,22 @@ def forward_routed(m, cfg, d, ids, gates, x=None, stream_shared=None):
 # ---------------------------------------------------------------------------------------------------
 # routing given by the caller
 
+def test_layer_sized_for_a_larger_batch(moe):
+    """One workspace sized for T_max serves every smaller batch. At the GLM-5 shape the layout of 64 tokens
+    (decode K split, shared expert folded in) is larger than that of 100: MoELayer(T_max = 100) runs 16, 64
+    and 100 tokens, each equal bit for bit to moe_forward with a workspace of its own size."""
+    say("[layer sized for 100 tokens]")
+    cfg, h, d = case("glm5_prefill")
+    layer = moe.MoELayer(d["wr"], d["b"], d["w1"], d["w3"], d["w2"], d["ws1"], d["ws3"], d["ws2"], cfg.k,
+                         cfg.scale, 100)
+    for T in (16, 64, 100):
+        x = d["x"][:T]
+        out = layer(x)
+        torch.cuda.synchronize()
+        ref, _, _ = forward(moe, cfg, d, x=x)
+        assert torch.equal(out, ref), T
+
+
 @pytest.mark.parametrize("name", ["tiny", "mid", "glm5_decode", "glm47_decode", "glm5_prefill"])
 def test_routed_with_own_routing_is_forward_bitwise(moe, name):
     """moe_forward_routed fed moe_forward's own ids and gates runs the same kernels on the same bytes."""
