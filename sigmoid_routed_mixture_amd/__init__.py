@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libmoe.so is not built; run `python -m sigmoid_routed_mixture_amd._build` "
+    raise ImportError("libmoe.so is not built; run `python sigmoid_routed_mixture_amd/_build.py` "
                       "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
