@@ -33,10 +33,10 @@
  *    enqueues nothing. Non-finite inputs are outside the contract.
  *  - Supported sizes: 1 <= k <= min(E, 32), E <= 256, H, I and Is multiples of 64, T * k < 2^31.
  *  - Calls on one stream run in order; overlapping calls that share output or workspace buffers race.
- *  - Environment variables read on every call, for tests only: MOE_GEMM_PATH (wide | tall | dma | skinny)
- *    forces one GEMM kernel; MOE_XCD_SPLIT=count, MOE_PERSIST=0 and MOE_KSPLIT (1 | 2) change how GEMM
- *    blocks are spread over the chip or split along K. Unset, the library picks by size. Every choice
- *    computes the same layer; only a K split or a different kernel changes the fp32 summation order.
+ *  - Kernels, the spread of GEMM blocks over the chip and any K split are picked from the sizes alone; the
+ *    library reads no environment variable. Tests and benchmarks may override those choices through the
+ *    process-wide knobs of moe_tuning.h. Every choice computes the same layer; only a K split or a
+ *    different kernel changes the fp32 summation order.
  */
 #ifndef SIGMOID_ROUTED_MIXTURE_MOE_H
 #define SIGMOID_ROUTED_MIXTURE_MOE_H

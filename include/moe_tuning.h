@@ -1,0 +1,51 @@
+/*
+ * moe_tuning.h -- process-wide overrides of the MoE layer's kernel-selection rules, for tests and
+ * benchmarks.
+ *
+ * By default every entry point of moe.h and moe_block.h picks its GEMM kernel, the spread of GEMM blocks
+ * over the chip and any split of the reduction dimension from the sizes alone. A test that wants to run
+ * every kernel on the same inputs, or compare two block orders bit for bit, sets a knob here first. Every
+ * setting computes the same layer: block orders and grids give bitwise identical results; another GEMM
+ * kernel or a K split changes only the fp32 summation order.
+ *
+ * Knobs are plain process-wide integers (atomic: reading or setting one from any thread is safe). A value
+ * applies to every call that starts after it is set, from any thread and on any device, until it is set
+ * again; 0 restores the size-based rule. Production callers leave them at 0. Nothing else in the library
+ * reads the environment or any other global setting.
+ */
+#ifndef SIGMOID_ROUTED_MIXTURE_MOE_TUNING_H
+#define SIGMOID_ROUTED_MIXTURE_MOE_TUNING_H
+
+#include "moe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_tune_knob {
+    /* GEMM kernel of every grouped and dense GEMM: 0 by size; 1 the 128-token register-streaming kernel,
+       2 its 256-token form, 3 the LDS-copy kernel (where every operand fits its 32-bit offsets; else the
+       size rule's fallback), 4 the 16-token weight-streaming kernel. */
+    MOE_TUNE_GEMM_PATH = 0,
+    /* Split of the LDS-copy kernel's grouped blocks over the 8 XCDs: 0 by size (the work-balanced split for
+       the down GEMM), 1 equal block counts for both GEMMs. */
+    MOE_TUNE_XCD_SPLIT = 1,
+    /* 0 by size (persistent routed GEMMs above the decode sizes), 1 one workgroup per block everywhere. */
+    MOE_TUNE_PERSIST = 2,
+    /* K split of decode-sized grouped GEMMs: 0 by the live block count, 1 never split, 2 always split. */
+    MOE_TUNE_KSPLIT = 3,
+    MOE_TUNE_KNOBS = 4 /* number of knobs */
+} moe_tune_knob;
+
+/* Sets a knob. MOE_ERR_INVALID_ARG for an unknown knob or a value outside the knob's range (nothing
+   changes then). */
+moe_status moe_set_tuning(int knob, int value);
+
+/* The knob's current value, or -1 for an unknown knob. */
+int moe_get_tuning(int knob);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGMOID_ROUTED_MIXTURE_MOE_TUNING_H */

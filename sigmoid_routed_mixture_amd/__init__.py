@@ -10,6 +10,10 @@ include/moe.h. PyTorch supplies device memory and streams. The functions keep th
     moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids=None,
                 topk_gates=None, expert_counts=None, stream=None, stream_shared=None)
 
+the knobs of include/moe_tuning.h (tests and benchmarks only):
+
+    moe_set_tuning(knob, value), moe_get_tuning(knob), and the context manager tuned(MOE_TUNE_...=value)
+
 and those of include/moe_block.h:
 
     moe_forward_routed(x, topk_ids, topk_gates, w1, w3, w2, ws1, ws3, ws2, out, workspace, expert_counts=None,
@@ -64,6 +68,10 @@ _lib.moe_dense_mlp_workspace_bytes.argtypes = [_i] * 3
 _lib.moe_dense_mlp_workspace_bytes.restype = _sz
 _lib.moe_dense_mlp.argtypes = [_p] * 4 + [_i] * 3 + [_p, _p, _sz, _p]
 _lib.moe_dense_mlp.restype = _i
+_lib.moe_set_tuning.argtypes = [_i, _i]
+_lib.moe_set_tuning.restype = _i
+_lib.moe_get_tuning.argtypes = [_i]
+_lib.moe_get_tuning.restype = _i
 _lib.moe_status_string.argtypes = [_i]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_last_error.argtypes = []
@@ -73,7 +81,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WO
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_route", "moe_permute",
                     "moe_forward", "moe_forward_profiled", "moe_status_string", "moe_last_error",
                     "moe_forward_routed", "moe_block_workspace_bytes", "moe_block_forward",
-                    "moe_dense_mlp_workspace_bytes", "moe_dense_mlp")
+                    "moe_dense_mlp_workspace_bytes", "moe_dense_mlp", "moe_set_tuning", "moe_get_tuning")
+# Knobs of include/moe_tuning.h (tests and benchmarks only; 0 = the size rules).
+MOE_TUNE_GEMM_PATH, MOE_TUNE_XCD_SPLIT, MOE_TUNE_PERSIST, MOE_TUNE_KSPLIT = range(4)
+GEMM_PATHS = {"auto": 0, "wide": 1, "tall": 2, "dma": 3, "skinny": 4}
 
 
 class MoEError(RuntimeError):
@@ -113,6 +124,36 @@ def _stream(s, device):
     if isinstance(s, torch.cuda.Stream):
         return s.cuda_stream
     return int(s)
+
+
+def moe_set_tuning(knob: int, value: int) -> None:
+    _check(_lib.moe_set_tuning(knob, value))
+
+
+def moe_get_tuning(knob: int) -> int:
+    return _lib.moe_get_tuning(knob)
+
+
+class tuned:
+    """Context manager that sets tuning knobs (include/moe_tuning.h) and restores them on exit:
+    `with tuned(MOE_TUNE_GEMM_PATH=3): ...`."""
+
+    _names = {"MOE_TUNE_GEMM_PATH": 0, "MOE_TUNE_XCD_SPLIT": 1, "MOE_TUNE_PERSIST": 2, "MOE_TUNE_KSPLIT": 3}
+
+    def __init__(self, **knobs):
+        self.knobs = {self._names[k]: v for k, v in knobs.items()}
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            self.saved[k] = moe_get_tuning(k)
+            moe_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            moe_set_tuning(k, v)
+        return False
 
 
 def moe_workspace_bytes(T: int, H: int, E: int, k: int, I: int, Is: int) -> int:

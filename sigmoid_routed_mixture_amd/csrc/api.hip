@@ -1,6 +1,6 @@
 // The C ABI of include/moe.h: argument checks, workspace carving, stream/event orchestration, launches.
 #include <algorithm>
-#include <cstdlib>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -9,6 +9,7 @@
 #include "moe.h"
 #include "moe_block.h"
 #include "moe_profile.h"
+#include "moe_tuning.h"
 #include "plan.h"
 
 namespace {
@@ -76,19 +77,27 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
     return MOE_OK;
 }
 
-// Test knob: MOE_GEMM_PATH=wide|tall|dma|skinny forces one GEMM kernel for every size (all are exact
-// implementations of the same GEMMs; the default is gemm_path for the grouped GEMMs, dense_path for a
-// dense MLP of T rows). The Dma kernel is used only when every operand fits its 32-bit offsets: x [T, H],
-// h [T k + T, I] and [T, Is], the weights.
+// Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
+// benchmark set one.
+std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2};
+
+int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
+
+// The GEMM kernel: gemm_path for the grouped GEMMs, dense_path for a dense MLP of T rows, unless the
+// MOE_TUNE_GEMM_PATH knob forces one (all are exact implementations of the same GEMMs). The Dma kernel is
+// used only when every operand fits its 32-bit offsets: x [T, H], h [T k + T, I] and [T, Is], the weights.
 moe::GemmPath pick_path(int T, int E, int k, int H, int I, int Is, bool dense = false) {
     const bool fits = moe::dma_fits(T, H) && moe::dma_fits((int64_t)T * k + T, I) && moe::dma_fits(T, Is) &&
                       moe::dma_fits(I, H) && moe::dma_fits(H, I) && moe::dma_fits(Is, H) && moe::dma_fits(H, Is);
-    const char* f = std::getenv("MOE_GEMM_PATH");
     moe::GemmPath p = dense ? moe::dense_path(T) : moe::gemm_path(T, E, k);
-    if (f && std::strcmp(f, "wide") == 0) p = moe::GemmPath::Wide;
-    if (f && std::strcmp(f, "tall") == 0) p = moe::GemmPath::Tall;
-    if (f && std::strcmp(f, "dma") == 0) p = moe::GemmPath::Dma;
-    if (f && std::strcmp(f, "skinny") == 0) p = moe::GemmPath::Skinny;
+    switch (tuning(MOE_TUNE_GEMM_PATH)) {
+    case 1: p = moe::GemmPath::Wide; break;
+    case 2: p = moe::GemmPath::Tall; break;
+    case 3: p = moe::GemmPath::Dma; break;
+    case 4: p = moe::GemmPath::Skinny; break;
+    default: break;
+    }
     return p == moe::GemmPath::Dma && !fits ? moe::fallback_path(T, E, k) : p;
 }
 
@@ -261,8 +270,7 @@ moe_status forward_impl(const Request& q) {
     MOE_TRY(mark(1));
     // the DMA kernel's work-balanced XCD split (computed for both grouped GEMMs, used by the down GEMM)
     const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (fold ? moe::shared_tiles(T, BM) : 0);
-    const char* xs = std::getenv("MOE_XCD_SPLIT"); // test knob: "count" keeps the block-count split
-    const bool balanced = path == moe::GemmPath::Dma && !fold && !(xs && std::strcmp(xs, "count") == 0);
+    const bool balanced = path == moe::GemmPath::Dma && !fold && tuning(MOE_TUNE_XCD_SPLIT) == 0;
     moe::XcdSplit split{};
     if (balanced) {
         split.bounds = static_cast<int32_t*>(at(L.xcd_bounds));
@@ -271,12 +279,11 @@ moe_status forward_impl(const Request& q) {
         for (int v = 0; v < 2; ++v) split.cap[v] = (int)moe::dma_xcd_cap(grid_tiles, split.ntn[v]);
     }
     // the grouped DMA GEMMs run persistent (one workgroup per CU claiming blocks from per-XCD counters)
-    const char* ps = std::getenv("MOE_PERSIST"); // test knob: "0" keeps one workgroup per block
-    const bool persist = balanced && !(ps && std::strcmp(ps, "0") == 0);
+    const bool persist = balanced && tuning(MOE_TUNE_PERSIST) == 0;
     if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
     // decode-sized grouped GEMMs: the permutation picks a K split of 1 or 2 for each from the live block count
-    const char* kss = std::getenv("MOE_KSPLIT"); // test knob: "1" never splits, "2" always does
-    const bool ks_off = kss && std::strcmp(kss, "1") == 0, ks_on = kss && std::strcmp(kss, "2") == 0;
+    const int ks_knob = tuning(MOE_TUNE_KSPLIT);
+    const bool ks_off = ks_knob == 1, ks_on = ks_knob == 2;
     const bool ksplit = path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off;
     int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
     bool ks_gate_up = false; // the gate/up split needs a reduction launch: skipped when it can never pay
@@ -427,6 +434,19 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_set_tuning(int knob, int value) {
+    g_last_error.clear();
+    if (knob < 0 || knob >= MOE_TUNE_KNOBS) return fail(MOE_ERR_INVALID_ARG, "unknown tuning knob");
+    if (value < 0 || value > kTuneMax[knob]) return fail(MOE_ERR_INVALID_ARG, "tuning value out of range");
+    g_tuning[knob].store(value, std::memory_order_relaxed);
+    return MOE_OK;
+}
+
+int moe_get_tuning(int knob) {
+    if (knob < 0 || knob >= MOE_TUNE_KNOBS) return -1;
+    return g_tuning[knob].load(std::memory_order_relaxed);
+}
 
 size_t moe_workspace_bytes(int T, int H, int E, int k, int I, int Is) {
     if (!moe::check_sizes(T, H, E, k, I, Is, true).ok()) return 0;

@@ -211,3 +211,27 @@ def test_dense_mlp_argument_checks(lib):
     assert L.moe_dense_mlp(A, A, A, A, -1, 256, 384, A, ws, nb, None) == INVALID
     assert L.moe_dense_mlp(A, A, A, A, 64, 256, 96, A, ws, nb, None) == UNSUPPORTED
     assert L.moe_dense_mlp(None, None, None, None, 0, 256, 384, None, None, 0, None) == OK
+
+
+def test_tuning_knobs_set_get_and_reject_out_of_range(lib):
+    # include/moe_tuning.h: process-wide knobs, 0 = the size rules; bad knobs or values change nothing
+    lib.moe_set_tuning.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.moe_get_tuning.argtypes = [ctypes.c_int]
+    maxima = {0: 4, 1: 1, 2: 1, 3: 2}
+    for knob, top in maxima.items():
+        assert lib.moe_get_tuning(knob) == 0
+        for v in range(top + 1):
+            assert lib.moe_set_tuning(knob, v) == OK
+            assert lib.moe_get_tuning(knob) == v
+        assert lib.moe_set_tuning(knob, top + 1) == INVALID
+        assert lib.moe_set_tuning(knob, -1) == INVALID
+        assert lib.moe_get_tuning(knob) == top
+        assert lib.moe_set_tuning(knob, 0) == OK
+    assert lib.moe_set_tuning(4, 0) == INVALID
+    assert lib.moe_get_tuning(4) == -1 and lib.moe_get_tuning(-1) == -1
+
+
+def test_library_reads_no_environment():
+    # every kernel choice comes from the sizes and the tuning knobs, never from the process environment
+    out = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True, check=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", out)

@@ -22,6 +22,19 @@ def moe():
     return m
 
 
+@pytest.fixture
+def tune(moe):
+    """Sets tuning knobs of include/moe_tuning.h by name; every knob is back at 0 after the test."""
+
+    def set_knobs(**knobs):
+        for name, value in knobs.items():
+            moe.moe_set_tuning(getattr(moe, name), value)
+
+    yield set_knobs
+    for knob in range(4):
+        moe.moe_set_tuning(knob, 0)
+
+
 def forward(m, cfg, d, x=None, b=None):
     x = d["x"] if x is None else x
     T = x.shape[0]
@@ -273,8 +286,8 @@ def test_dense_mlp_parity(moe, name):
 
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 @pytest.mark.parametrize("T", [1, 16, 100])
-def test_dense_mlp_both_kernels_and_ragged(moe, monkeypatch, path, T):
-    monkeypatch.setenv("MOE_GEMM_PATH", path)
+def test_dense_mlp_both_kernels_and_ragged(moe, tune, path, T):
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS[path])
     cfg, h, d = dense_case("dense_tiny")
     out = dense(moe, cfg, d, T=min(T, cfg.T))
     rows = np.arange(min(T, cfg.T), dtype=np.int32)

@@ -26,6 +26,19 @@ def moe():
     return m
 
 
+@pytest.fixture
+def tune(moe):
+    """Sets tuning knobs of include/moe_tuning.h by name; every knob is back at 0 after the test."""
+
+    def set_knobs(**knobs):
+        for name, value in knobs.items():
+            moe.moe_set_tuning(getattr(moe, name), value)
+
+    yield set_knobs
+    for knob in range(4):
+        moe.moe_set_tuning(knob, 0)
+
+
 def run_forward(m, cfg, d, stream_shared=None, T=None):
     T = cfg.T if T is None else T
     out = torch.empty(T, cfg.H, dtype=torch.float32, device="cuda")
@@ -114,11 +127,11 @@ def test_forward_parity(moe, name):
 
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "glm47_decode"])
 @pytest.mark.parametrize("ks", ["1", "2"])
-def test_decode_k_split(moe, monkeypatch, name, ks):
+def test_decode_k_split(moe, tune, name, ks):
     # decode-sized grouped GEMMs (gate/up with its reduction, down with the combine adding the halves) with
     # the K split forced off and on, against the oracle on every token
     say("[K split %s] %s" % (ks, name))
-    monkeypatch.setenv("MOE_KSPLIT", ks)
+    tune(MOE_TUNE_KSPLIT=int(ks))
     cfg, h, d = case(name)
     ref = route_ref(name)
     out, ids, gates, counts = run_forward(moe, cfg, d)
@@ -130,9 +143,9 @@ def test_decode_k_split(moe, monkeypatch, name, ks):
 
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("glm5_decode", 16), ("mid", 384)])
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
-def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
+def test_both_gemm_kernels(moe, tune, name, T, path):
     say("[gemm path %s] %s T=%d" % (path, name, T))
-    monkeypatch.setenv("MOE_GEMM_PATH", path)
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS[path])
     cfg, h, d = case(name)
     out, ids, gates, counts = run_forward(moe, cfg, d, T=T)
     ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(T))
@@ -141,37 +154,37 @@ def test_both_gemm_kernels(moe, monkeypatch, name, T, path):
 
 
 @pytest.mark.parametrize("name,T", [("mid", 700), ("glm47_prefill", 2048)])
-def test_dma_kernel_matches_register_kernel_bitwise(moe, monkeypatch, name, T):
+def test_dma_kernel_matches_register_kernel_bitwise(moe, tune, name, T):
     # the LDS-copy kernel sums every accumulator in the register-streaming kernel's order
     say("[dma vs tall] %s T=%d" % (name, T))
     cfg, h, d = case(name)
-    monkeypatch.setenv("MOE_GEMM_PATH", "tall")
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS["tall"])
     a = run_forward(moe, cfg, d, T=T)
-    monkeypatch.setenv("MOE_GEMM_PATH", "dma")
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS["dma"])
     b = run_forward(moe, cfg, d, T=T)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
-def test_xcd_split_does_not_change_results(moe, monkeypatch):
+def test_xcd_split_does_not_change_results(moe, tune):
     # the work-balanced and the block-count XCD split only reorder the same blocks
     say("[xcd split] mid")
     cfg, h, d = case("mid")
     a = run_forward(moe, cfg, d)
-    monkeypatch.setenv("MOE_XCD_SPLIT", "count")
+    tune(MOE_TUNE_XCD_SPLIT=1)
     b = run_forward(moe, cfg, d)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
-def test_persistent_grid_does_not_change_results(moe, monkeypatch, name):
+def test_persistent_grid_does_not_change_results(moe, tune, name):
     # one workgroup per CU claiming blocks from the XCD counters (and from the back of other XCDs' ranges
     # once its own is used up) computes every block exactly as one workgroup per block does
     say("[persistent] %s" % name)
     cfg, h, d = case(name)
     a = run_forward(moe, cfg, d)
-    monkeypatch.setenv("MOE_PERSIST", "0")
+    tune(MOE_TUNE_PERSIST=1)
     b = run_forward(moe, cfg, d)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
@@ -235,10 +248,10 @@ EDGE = [
 
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 @pytest.mark.parametrize("shape", EDGE, ids=[e[-1] for e in EDGE])
-def test_edge_shapes(moe, monkeypatch, shape, path):
+def test_edge_shapes(moe, tune, shape, path):
     T, H, E, k, I, Is, what = shape
     say("[edge %s] %s T=%d H=%d E=%d k=%d I=%d Is=%d" % (path, what, T, H, E, k, I, Is))
-    monkeypatch.setenv("MOE_GEMM_PATH", path)
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS[path])
     cfg = wl.MoEConfig(50, "edge", T=T, H=H, E=E, k=k, I=I, Is=Is, scale=2.5)
     h = config_host(cfg)
     if Is == 0:
@@ -253,9 +266,9 @@ def test_edge_shapes(moe, monkeypatch, shape, path):
 
 
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
-def test_identical_tokens_one_giant_group(moe, monkeypatch, path):
+def test_identical_tokens_one_giant_group(moe, tune, path):
     say("[giant group %s]" % path)
-    monkeypatch.setenv("MOE_GEMM_PATH", path)
+    tune(MOE_TUNE_GEMM_PATH=moe.GEMM_PATHS[path])
     cfg = wl.MoEConfig(51, "same", T=700, H=256, E=16, k=4, I=128, Is=128, scale=1.8)
     h = config_host(cfg)
     h["x"] = np.ascontiguousarray(np.repeat(h["x"][:1], cfg.T, axis=0))
