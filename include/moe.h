@@ -78,6 +78,10 @@ size_t moe_workspace_bytes(int T, int H, int E, int k, int I, int Is);
  *   topk_gates [T, k] fp32      out: G = scale * s / (sum of the chosen s), same slot order
  *   logits     [T, E] fp32      out, nullable: z = x W_r (fp32-accumulated), before sigmoid and bias
  * Logits accumulate in fp32 (exact bf16 products); s = 1 / (1 + exp(-z)) in fp32; s + b in fp32.
+ * Here each logit is one fp32 sum over h; inside moe_forward the same logits are summed over K ranges in
+ * another fp32 order, so the two may differ in the last bits of z. A token whose k-th and (k+1)-th values
+ * of s + b lie that close may then choose differently here than inside moe_forward (so moe_route followed
+ * by moe_forward_routed is not bit-identical to moe_forward for such tokens).
  * Pages: open-model-atlas GLM-5 "MoE transformer block", "All 43 steps" (z = x W_r, s = sigma(z),
  * top-8 of s + b, G_i); nnterp glm_moe_dsa "The mixture" (router_logits, expert_weights, expert_indices).
  */
@@ -88,14 +92,17 @@ moe_status moe_route(const moe_bf16* x, const moe_bf16* w_router, const float* b
  * Permutation of the T * k routing slots into expert-contiguous rows (a stable counting sort by expert).
  *   x          [T, H] bf16       tokens (read only when x_perm is non-null; may then be null otherwise)
  *   topk_ids   [T, k] int32      experts chosen per token, each in [0, E) and distinct within a token
- *   counts     [E] int32         out: slots routed to each expert
- *   offsets    [E + 1] int32     out: exclusive prefix sum of counts; offsets[E] = T * k
+ *   counts     [E] int32         out: rows given to each expert, one per token whose ids name it
+ *   offsets    [E + 1] int32     out: exclusive prefix sum of counts; offsets[E] = T * k when every id is
+ *                                in [0, E) and distinct within its token (as moe_route writes them),
+ *                                else the number of rows actually given out
  *   row_token  [T * k] int32     out: token of each expert-contiguous row; the rows of expert e are
  *                                offsets[e] .. offsets[e+1]-1, in ascending token order
  *   slot_row   [T * k] int32     out: row that slot j of token t went to, at index t * k + j
  *   x_perm     [T * k, H] bf16   out, nullable: x_perm[r] = x[row_token[r]]
  *   workspace                    device scratch of at least moe_permute_workspace_bytes(T, E) bytes
- * Ids outside [0, E) are skipped (their slots get no row); repeated ids within one token share a row.
+ * Ids outside [0, E) are skipped (their slots get no row and slot_row -1); repeated ids within one token
+ * share a row (the token counts once for that expert).
  * Neither is produced by moe_route. The pages pass (hidden, indices, weights) to the routed experts
  * (nnterp glm_moe_dsa, expert_indices = "experts's inputs, element 1"); this grouping is how the experts
  * here receive their tokens.

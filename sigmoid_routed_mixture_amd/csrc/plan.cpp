@@ -90,7 +90,8 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     L.partial = take((size_t)router_splits(T, H, E) * (size_t)T * (size_t)E * 4);
     const size_t rows = Tk + (fold ? (size_t)T : 0);
     L.h_perm = take(rows * (size_t)I * 2);
-    L.y_perm = take(rows * (size_t)H * 4);
+    // per-slot rows: bf16 where slot_rows_bf16 holds (never with the shared expert folded in), else fp32
+    L.y_perm = take(rows * (size_t)H * (slot_rows_bf16(T, E, k, I, Is) ? 2 : 4));
     const bool dense_shared = Is > 0 && !fold;
     L.h_sh = dense_shared ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
     L.y_sh = dense_shared ? take((size_t)T * (size_t)H * 4) : size_t(-1);

@@ -60,7 +60,8 @@ int main() {
                                 {L.slot_row, Tk * 4, "slot_row"}, {L.chunk_base, chunks * E * 4, "chunk_base"},
                                 {L.tiles, tiles_need, "tiles"}, {L.ntiles, 4, "ntiles"},
                                 {L.partial, (size_t)moe::router_splits(T, H, E) * T * E * 4, "partial"},
-                                {L.h_perm, rows * I * 2, "h_perm"}, {L.y_perm, rows * H * 4, "y_perm"}};
+                                {L.h_perm, rows * I * 2, "h_perm"},
+                                {L.y_perm, rows * H * (moe::slot_rows_bf16(T, E, k, I, Is) ? 2 : 4), "y_perm"}};
                             CHECK(fold == (L.h_sh == size_t(-1) && L.y_sh == size_t(-1) && Is > 0),
                                   "dense shared buffers only without the fold (I=%d Is=%d)", I, Is);
                             if (Is > 0 && !fold) {
