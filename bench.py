@@ -92,6 +92,7 @@ class Runner:
         ms = start.elapsed_time(end) / steps
         stages = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                   for j, name in enumerate(STAGES)}
+        self.step_ms = [ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)]
         return ms, stages
 
 
@@ -289,24 +290,64 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
     return res
 
 
-def cpu_baseline(cfg, host, budget_s):
+def profile_workload(m, wl, name, args, device):
+    """Only the timed steps of one workload, for profiler runs: a mixture workload (prefill and decode name
+    the GLM-5 ones) through moe_forward_profiled, or a dense-MLP workload through moe_dense_mlp."""
+    import torch
+
+    name = {"prefill": "glm5_prefill", "decode": "glm5_decode"}.get(name, name)
+    if name in wl.DENSE_BY_NAME:
+        cfg = wl.DENSE_BY_NAME[name]
+        w = {k: to_dev_bf16(wl.dense_weight(cfg, k), device) for k in ("w1", "w3", "w2")}
+        x = to_dev_bf16(wl.dense_tokens(cfg), device)
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
+        ws = torch.empty(m.moe_dense_mlp_workspace_bytes(cfg.T, cfg.H, cfg.Id), dtype=torch.uint8, device=device)
+        steps = args.steps if cfg.T > 64 else args.decode_steps
+        ms = time_call(lambda: m.moe_dense_mlp(x, w["w1"], w["w3"], w["w2"], out, ws), steps, args.warmup)
+        log("%s: %.4f ms/step" % (name, ms))
+        return
+    if name not in wl.BY_NAME:
+        raise SystemExit("unknown workload %r" % name)
+    cfg = wl.BY_NAME[name]
+    log("generating the expert weights of %s" % name)
+    w = {n: to_dev_bf16(wl.weight(cfg, n), device) for n in WEIGHT_NAMES}
+    host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
+    r = Runner(m, cfg, w, host_t, device, args.two_streams)
+    ms, stages = r.time(args.steps if cfg.T > 64 else args.decode_steps, args.warmup)
+    active = int((r.counts.cpu().numpy() > 0).sum())
+    log("%s: %.4f ms/step, stages %s, active experts %d" % (name, ms, stages, active))
+
+
+def cpu_baseline(cfg, host, budget_s, rounds=5):
+    """The CPU oracle as it stands, token-sharded over the host's threads, on `rounds` equal slices of one
+    seeded sample of the workload's tokens (about budget_s seconds in all); the value is the median rate of
+    the slices."""
     import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    rows = np.arange(cfg.T, dtype=np.int32)
+    desc = oracle.host_description()
+    threads = desc["threads"]
     rng = np.random.default_rng(0)
     t0 = time.perf_counter()
-    oracle.forward(host, cfg.k, cfg.scale, rows=rows[:1])
-    t1 = time.perf_counter() - t0
-    n = max(threads, int(budget_s / max(t1, 1e-3)) * threads)
-    n = min(n, cfg.T)
-    sample = np.sort(rng.choice(cfg.T, size=n, replace=False)).astype(np.int32)
-    t0 = time.perf_counter()
-    oracle.run_sharded(lambda rows: oracle.forward(host, cfg.k, cfg.scale, rows=rows), sample, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d seeded random tokens of the %s workload (T=%d), fp64 plain C, %d threads, %.1f s"
-                      % (n, cfg.name, cfg.T, threads, dt)}
+    oracle.forward(host, cfg.k, cfg.scale, rows=np.array([0], dtype=np.int32))
+    t1 = time.perf_counter() - t0  # one token on one thread
+    per_round = max(threads, int(budget_s / rounds / max(t1, 1e-3)) * threads)
+    per_round = min(per_round, cfg.T // rounds)
+    sample = rng.choice(cfg.T, size=per_round * rounds, replace=False).astype(np.int32)
+    rates, total = [], 0.0
+    for r in range(rounds):
+        rows = np.sort(sample[r * per_round:(r + 1) * per_round])
+        t0 = time.perf_counter()
+        oracle.run_sharded(lambda rows: oracle.forward(host, cfg.k, cfg.scale, rows=rows), rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        total += dt
+        rates.append(per_round / dt)
+    return {"value": float(np.median(rates)), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d seeded random tokens of the %s workload (T=%d) in %d slices of %d, fp64 plain C, %d threads "
+                      "(host: nproc %s, affinity %s, %s), %.1f s in all; value = median slice rate"
+                      % (per_round * rounds, cfg.name, cfg.T, rounds, per_round, threads, desc["nproc"],
+                         desc["affinity"], desc["cpu_model"], total),
+            "threads": threads, "nproc": desc["nproc"], "affinity": desc["affinity"], "cpu_model": desc["cpu_model"],
+            "slice_rates": rates}
 
 
 def main():
@@ -326,8 +367,10 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=None, metavar="GIB",
                     help="time a plain device-to-device copy of this many GiB (HBM ceiling, and the known-size "
                          "reference for profiler byte counters) and exit")
-    ap.add_argument("--profile-only", choices=["prefill", "decode"], default=None,
-                    help="run only this workload's timed steps and print its timings (for profiler runs)")
+    ap.add_argument("--profile-only", default=None, metavar="WORKLOAD",
+                    help="run only this workload's timed steps and print its timings (for profiler runs): prefill, "
+                         "decode, or any mixture or dense-MLP workload name (mid, glm5_skewed, glm47_prefill, "
+                         "glm5_dense_decode, ...)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer's hot path has no multi-GPU mode (see the sharding "
@@ -359,6 +402,9 @@ def main():
     import workloads as wl
 
     device = torch.device("cuda", 0)
+    if args.profile_only:
+        profile_workload(m, wl, args.profile_only, args, device)
+        return
     cfg_p = wl.BY_NAME["glm5_prefill"]
     cfg_d = wl.BY_NAME["glm5_decode"]
     log("generating GLM-5 expert weights on the host (%d threads)" % wl.host_threads())
@@ -371,22 +417,18 @@ def main():
 
     results = {}
     plan = ((cfg_p, args.steps), (cfg_d, args.decode_steps))
-    if args.profile_only:
-        plan = tuple(p for p in plan if p[0].name.endswith(args.profile_only))
     for cfg, steps in plan:
         host_t = {"x": wl.tokens(cfg), "wr": wl.router_weight(cfg), "b": wl.selection_bias(cfg)}
         r = Runner(m, cfg, dev_w, host_t, device, two)
         ms, stages = r.time(steps, args.warmup)
         active = int((r.counts.cpu().numpy() > 0).sum())
-        results[cfg.name] = (ms, stages, active, host_t)
+        results[cfg.name] = (ms, stages, active, host_t, float(np.median(r.step_ms)))
         log("%s: %.4f ms/step, stages %s, active experts %d" % (cfg.name, ms, stages, active))
         del r
         torch.cuda.empty_cache()
 
-    if args.profile_only:
-        return
-    ms_p, st_p, act_p, host_tp = results[cfg_p.name]
-    ms_d, st_d, act_d, _ = results[cfg_d.name]
+    ms_p, st_p, act_p, host_tp, med_p = results[cfg_p.name]
+    ms_d, st_d, act_d, _, med_d = results[cfg_d.name]
     gu_ms = st_p["gate_up"]
     achieved = gate_up_flops(cfg_p) / (gu_ms * 1e-3) / 1e12
     layer_tflops = cfg_p.flops() / (ms_p * 1e-3) / 1e12
@@ -413,11 +455,12 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(), "launch_ms": gu_ms,
                      "algorithmic_bytes": gate_up_bytes(cfg_p, act_p)},
-        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_BF16_TFLOPS,
+        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_BF16_TFLOPS, "median_step_ms": med_p,
                   "gbs": layer_bytes(cfg_p, act_p) / (ms_p * 1e-3) / 1e9, "active_experts": act_p,
                   "stages_ms": st_p},
         "decode": {"workload": cfg_d.name, "T": cfg_d.T, "steps": args.decode_steps, "ms_per_step": ms_d,
-                   "tokens_per_s": cfg_d.T / (ms_d * 1e-3), "gbs": dec_gbs, "hbm_frac": dec_gbs / PEAK_HBM_GBS,
+                   "tokens_per_s": cfg_d.T / (ms_d * 1e-3), "median_step_ms": med_d, "gbs": dec_gbs,
+                   "hbm_frac": dec_gbs / PEAK_HBM_GBS,
                    "active_experts": act_d, "stages_ms": st_d,
                    "gate_up_roofline": {"bound": "hbm", "achieved": dec_gu_gbs, "peak": PEAK_HBM_GBS,
                                         "unit": "GB/s", "frac": dec_gu_gbs / PEAK_HBM_GBS}},

@@ -245,11 +245,38 @@ def permute(ids, E):
     return {"counts": counts, "offsets": offsets, "row_token": row_token, "slot_row": slot_row}
 
 
+def host_threads() -> int:
+    """Host threads the oracle runs on: the job's granted CPU share when OMP_NUM_THREADS states one, else
+    every core this process may run on (its CPU affinity)."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, avail) if n > 0 else avail)
+
+
+def host_description() -> dict:
+    """What the oracle's host is: the threads it uses, the logical CPUs of the machine and of this process's
+    affinity, and the CPU model from /proc/cpuinfo."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"threads": host_threads(), "nproc": os.cpu_count(), "affinity": affinity, "cpu_model": model}
+
+
 def run_sharded(fn, rows, nthreads=None, **kw):
     """Run fn(rows=chunk, **kw) over contiguous chunks of `rows` on host threads and concatenate the dict
     results along axis 0. The per-chunk code is the plain single-threaded oracle."""
     rows = np.ascontiguousarray(rows, dtype=np.int32)
-    nthreads = nthreads or max(1, min(16, os.cpu_count() or 1))
+    nthreads = nthreads or host_threads()
     nthreads = max(1, min(nthreads, rows.size))
     chunks = [c for c in np.array_split(rows, nthreads) if c.size]
     with ThreadPoolExecutor(max_workers=len(chunks)) as ex:

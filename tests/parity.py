@@ -87,23 +87,65 @@ def compare_out(out_gpu, out_ref, label=""):
     rms = float(np.sqrt(np.mean(out_ref ** 2)))
     err = float(np.max(np.abs(out_gpu - out_ref))) if out_ref.size else 0.0
     ratio = err / rms if rms > 0 else err
-    say("  %s: max|err| = %.3e, RMS = %.3e, ratio = %.4f (limit %.3f)" % (label, err, rms, ratio, OUT_TOL))
+    say("  %s: %d tokens compared, max|err| = %.3e, RMS = %.3e, ratio = %.4f (limit %.3f)"
+        % (label, out_ref.shape[0] if out_ref.ndim > 1 else 1, err, rms, ratio, OUT_TOL))
     assert ratio <= OUT_TOL, "%s: max|err|/RMS = %.4f > %.3f" % (label, ratio, OUT_TOL)
     return ratio
 
 
+# Output comparisons on a sample take at least this many seeded random tokens (plus the boundary tokens of
+# sample_rows); smaller batches are compared on every token.
+SAMPLE_FLOOR = 1024
+
+
+def tile_height(n: int, BM: int = 256) -> int:
+    """Height of the GPU's token tiles of an expert with n rows: n split evenly over ceil(n / BM) tiles,
+    rounded up to 32 rows (the LDS-copy GEMM's tiles of up to 256 tokens). Used only to pick which tokens
+    a sample must contain."""
+    if n <= 0:
+        return BM
+    nt = (n + BM - 1) // BM
+    h = ((n + nt - 1) // nt + 31) // 32 * 32
+    return min(h, BM)
+
+
 def sample_rows(ids_ref, n_random: int, seed: int = 0):
-    """A seeded sample of tokens plus, for every expert that got any token, the first token routed to it."""
-    T = ids_ref.shape[0]
+    """A seeded sample of n_random tokens plus, for every expert that got any token, the first and the last
+    token routed to it and the two tokens on each side of every boundary between its GPU token tiles (the
+    rows of an expert are its tokens in ascending order; the last tile is the shortest, where the row masks
+    apply)."""
+    ids_ref = np.asarray(ids_ref)
+    T, k = ids_ref.shape
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
     flat = ids_ref.ravel()
-    seen = {}
-    for i, e in enumerate(flat):
-        if e not in seen:
-            seen[int(e)] = i // ids_ref.shape[1]
-    pick |= set(seen.values())
+    order = np.argsort(flat, kind="stable")  # slots by expert, ascending token within an expert
+    experts, starts, counts = np.unique(flat[order], return_index=True, return_counts=True)
+    for e, s0, n in zip(experts, starts, counts):
+        if e < 0:
+            continue
+        toks = order[s0:s0 + n] // k
+        pick.add(int(toks[0]))
+        pick.add(int(toks[-1]))
+        ht = tile_height(int(n))
+        for b in range(ht, int(n), ht):
+            pick.add(int(toks[b - 1]))
+            pick.add(int(toks[b]))
     return np.array(sorted(pick), dtype=np.int32)
+
+
+def output_rows(T: int, ids_ref, seed: int, full: bool):
+    """Tokens whose outputs a test compares: all of them when `full` or T <= SAMPLE_FLOOR, else
+    sample_rows with SAMPLE_FLOOR random tokens."""
+    if full or T <= SAMPLE_FLOOR:
+        return np.arange(T, dtype=np.int32)
+    return sample_rows(ids_ref, SAMPLE_FLOOR, seed=seed)
+
+
+def host_line() -> str:
+    d = oracle.host_description()
+    return "oracle host: %d threads (nproc %s, affinity %s, %s)" % (d["threads"], d["nproc"], d["affinity"],
+                                                                     d["cpu_model"])
 
 
 def config_host(cfg: wl.MoEConfig, weights: dict | None = None) -> dict:

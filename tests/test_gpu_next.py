@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import workloads as wl
-from parity import (case, compare_out, compare_routing, dense_case, dev, dev_bf16, oracle_forward_rows,
-                    route_ref, sample_rows, say)
+from parity import (SAMPLE_FLOOR, case, compare_out, compare_routing, dense_case, dev, dev_bf16, host_line,
+                    oracle_forward_rows, output_rows, route_ref, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,11 +177,13 @@ def block(m, cfg, d, gamma, T=None, stream_shared=None):
     return out, xn, ids, gates
 
 
-BLOCK_SAMPLE = {"tiny": None, "mid": 256, "glm5_decode": None, "glm47_decode": None, "glm5_prefill": 64,
-                "glm47_prefill": 128}
+# the block's output on every token, but at GLM-5 prefill on parity.sample_rows' sample (parity.SAMPLE_FLOOR
+# seeded tokens plus every expert's first, last and tile-boundary tokens)
+BLOCK_FULL = {"tiny": True, "mid": True, "glm5_decode": True, "glm47_decode": True, "glm5_prefill": False,
+              "glm47_prefill": True}
 
 
-@pytest.mark.parametrize("name", list(BLOCK_SAMPLE))
+@pytest.mark.parametrize("name", list(BLOCK_FULL))
 def test_block_forward_parity(moe, name):
     say("[block] %s" % name)
     cfg, h, d = case(name)
@@ -208,10 +210,10 @@ def test_block_forward_parity(moe, name):
                              np.arange(cfg.T))
     same, nnear, ndiff = compare_routing(ids.cpu().numpy(), gates.cpu().numpy(), ref, name)
     # 4. the block output against the oracle's block on (a sample of) the tokens that chose alike
-    n = BLOCK_SAMPLE[name]
-    rows = np.arange(cfg.T, dtype=np.int32) if n is None else sample_rows(ref["ids"], n, seed=cfg.index)
+    rows = output_rows(cfg.T, ref["ids"], cfg.index, BLOCK_FULL[name])
     rows = rows[same[rows]]
-    say("  oracle block on %d tokens (near-tie %d, differing %d)" % (rows.size, nnear, ndiff))
+    say("  %s; oracle block on %d of %d tokens (near-tie %d, differing %d)" % (
+        host_line(), rows.size, cfg.T, nnear, ndiff))
     orc = oracle.run_sharded(lambda rows: oracle.block_forward(h, gamma_h, wl.NORM_EPS, cfg.k, cfg.scale, rows=rows),
                              rows)
     assert np.array_equal(orc["x_norm"], xn_ref[rows])
@@ -267,18 +269,22 @@ def dense(m, cfg, d, T=None):
     return out.cpu().numpy()
 
 
-DENSE_ROWS = {"dense_tiny": None, "glm5_dense_decode": None, "glm5_dense_prefill": 48, "glm47_dense_prefill": 96}
+# dense MLP outputs on every token up to parity.SAMPLE_FLOOR tokens, else on that many seeded tokens plus
+# the first and the last
+DENSE_FULL = {"dense_tiny": True, "glm5_dense_decode": True, "glm5_dense_prefill": False,
+              "glm47_dense_prefill": False}
 
 
-@pytest.mark.parametrize("name", list(DENSE_ROWS))
+@pytest.mark.parametrize("name", list(DENSE_FULL))
 def test_dense_mlp_parity(moe, name):
     say("[dense mlp] %s" % name)
     cfg, h, d = dense_case(name)
     out = dense(moe, cfg, d)
-    n = DENSE_ROWS[name]
     rng = np.random.default_rng(cfg.index)
-    rows = np.arange(cfg.T, dtype=np.int32) if n is None else np.sort(
+    n = SAMPLE_FLOOR
+    rows = np.arange(cfg.T, dtype=np.int32) if DENSE_FULL[name] or cfg.T <= n else np.sort(
         np.concatenate([[0, cfg.T - 1], rng.choice(np.arange(1, cfg.T - 1), n, replace=False)])).astype(np.int32)
+    say("  %s; oracle dense MLP on %d of %d tokens" % (host_line(), rows.size, cfg.T))
     ref = oracle.run_sharded(lambda rows: {"o": oracle.dense_mlp(h["x"], h["w1"], h["w3"], h["w2"], rows=rows)},
                              rows)["o"]
     compare_out(out[rows], ref, name)

@@ -15,7 +15,8 @@ import torch
 import oracle
 import workloads as wl
 from parity import (NEAR_TIE, case, compare_out, compare_routing, config_host, dev, dev_bf16,
-                    oracle_forward_rows, oracle_route_all, route_ref, sample_rows, say, to_device)
+                    host_line, oracle_forward_rows, oracle_route_all, output_rows, route_ref, sample_rows, say,
+                    to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +102,11 @@ def test_permute_parity(moe, name):
         (ref["counts"] > 0).sum(), ref["counts"].max(), (ref["counts"] == 0).sum()))
 
 
-SAMPLE = {"tiny": None, "mid": 512, "glm5_decode": None, "glm5_prefill": 96, "glm5_skewed": 64,
-          "glm47_decode": None, "glm47_prefill": 256}
+# Outputs on every token where the oracle takes well under a minute on the host's threads; on the two
+# largest GLM-5 batches a seeded sample of parity.SAMPLE_FLOOR tokens plus every expert's first and last
+# token and the tokens on both sides of each of its tile boundaries.
+FULL_OUTPUT = {"tiny": True, "mid": True, "glm5_decode": True, "glm5_prefill": False, "glm5_skewed": False,
+               "glm47_decode": True, "glm47_prefill": True}
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -115,10 +119,10 @@ def test_forward_parity(moe, name):
     assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=cfg.E))
     if ndiff == 0:
         assert np.array_equal(counts, np.bincount(ref["ids"].ravel(), minlength=cfg.E))
-    n = SAMPLE[name]
-    rows = np.arange(cfg.T, dtype=np.int32) if n is None else sample_rows(ref["ids"], n, seed=cfg.index)
+    rows = output_rows(cfg.T, ref["ids"], cfg.index, FULL_OUTPUT[name])
     rows = rows[same[rows]]
-    say("  oracle forward on %d tokens (near-tie %d, differing %d)" % (rows.size, nnear, ndiff))
+    say("  %s; oracle forward on %d of %d tokens (near-tie %d, differing %d)" % (
+        host_line(), rows.size, cfg.T, nnear, ndiff))
     orc = oracle_forward_rows(h, cfg.k, cfg.scale, rows)
     compare_out(out[rows], orc["out"], name)
     if name == "glm5_skewed":

@@ -78,8 +78,14 @@ def lib():
 
 
 def host_threads() -> int:
-    n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    """Generator threads: the job's granted CPU share when OMP_NUM_THREADS states one, else every core this
+    process may run on."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, avail) if n > 0 else avail)
 
 
 @dataclass(frozen=True)
