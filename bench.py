@@ -371,6 +371,9 @@ def main():
                     help="run only this workload's timed steps and print its timings (for profiler runs): prefill, "
                          "decode, or any mixture or dense-MLP workload name (mid, glm5_skewed, glm47_prefill, "
                          "glm5_dense_decode, ...)")
+    ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
+                    help="set a knob of include/moe_tuning.h before measuring (e.g. MOE_TUNE_ORDER=1); the default "
+                         "run sets none")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer's hot path has no multi-GPU mode (see the sharding "
@@ -401,6 +404,10 @@ def main():
     import sigmoid_routed_mixture_amd as m
     import workloads as wl
 
+    for item in args.tune:
+        knob, _, value = item.partition("=")
+        m.moe_set_tuning(getattr(m, knob), int(value))
+        log("tuning %s = %s" % (knob, value))
     device = torch.device("cuda", 0)
     if args.profile_only:
         profile_workload(m, wl, args.profile_only, args, device)
@@ -449,7 +456,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg_p.name, "T": cfg_p.T, "H": cfg_p.H, "E": cfg_p.E, "k": cfg_p.k, "I": cfg_p.I,
-                   "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none"},
+                   "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none",
+                   "tuning": args.tune},
         "roofline": {"bound": "mfma", "kernel": "gate/up SwiGLU grouped GEMM (routed experts%s)"
                      % (" + shared expert" if shared_folded(cfg_p) else ""), "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
