@@ -34,7 +34,12 @@ typedef enum moe_tune_knob {
     MOE_TUNE_PERSIST = 2,
     /* K split of decode-sized grouped GEMMs: 0 by the live block count, 1 never split, 2 always split. */
     MOE_TUNE_KSPLIT = 3,
-    MOE_TUNE_KNOBS = 4 /* number of knobs */
+    /* Block order of the persistent routed GEMMs: 0 by size (experts in index order, each cut into chunks
+       of up to 16 token tiles, contiguous XCD ranges); 1 the same with chunks of up to 128 tiles; dealt
+       orders, the chunks dealt over the XCDs in turn: 2 largest experts first, 3 in index order, 4 largest
+       first alternating with the smallest within each XCD. */
+    MOE_TUNE_ORDER = 4,
+    MOE_TUNE_KNOBS = 5 /* number of knobs */
 } moe_tune_knob;
 
 /* Sets a knob. MOE_ERR_INVALID_ARG for an unknown knob or a value outside the knob's range (nothing

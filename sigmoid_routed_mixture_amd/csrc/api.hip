@@ -80,7 +80,7 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -281,6 +281,12 @@ moe_status forward_impl(const Request& q) {
     // the grouped DMA GEMMs run persistent (one workgroup per CU claiming blocks from per-XCD counters)
     const bool persist = balanced && tuning(MOE_TUNE_PERSIST) == 0;
     if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
+    // block order of the persistent GEMMs: experts in index order, each cut into chunks of at most
+    // kPlainChunkTiles tiles (the MOE_TUNE_ORDER knob picks the longer chunks or one of the dealt orders)
+    const int order = tuning(MOE_TUNE_ORDER);
+    const bool dealt = persist && order >= 2;
+    split.dealt = dealt ? order - 1 : 0;
+    split.plain_cap = order == 1 ? moe::kMaxChunkTiles : moe::kPlainChunkTiles;
     // decode-sized grouped GEMMs: the permutation picks a K split of 1 or 2 for each from the live block count
     const int ks_knob = tuning(MOE_TUNE_KSPLIT);
     const bool ks_off = ks_knob == 1, ks_on = ks_knob == 2;
@@ -340,6 +346,7 @@ moe_status forward_impl(const Request& q) {
     // same (the work-balanced split measured 2 % slower there, 2 % faster on the down GEMM)
     add_shared(r1, q.ws1, q.ws3);
     if (persist) r1.work_ctr = reinterpret_cast<unsigned long long*>(split.ctr);
+    if (dealt) r1.xcd_bounds = split.bounds;
     const int h_rows = T * k + (fold ? T : 0);
     if (ks_gate_up) {
         r1.ksplit_dev = ks_flag;

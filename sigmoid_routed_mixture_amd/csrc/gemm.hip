@@ -45,13 +45,13 @@ __device__ __forceinline__ const uint16_t* weight_row(const uint16_t* w, const u
     return ti.shared ? ws + (size_t)n * K : w + ((size_t)ti.g * N + n) * K;
 }
 
-// A tile of the list: {group | tile height << 16, first row in the group, rows of the group, first permuted
-// row of the group}; the folded shared expert is group `groups`.
+// A tile of the list: {tile_word (group, tile height, place in its chunk), first row in the group, rows of
+// the group, first permuted row of the group} (plan.h); the folded shared expert is group `groups`.
 template <int BM>
 __device__ __forceinline__ bool entry_ok(const GemmArgs& a, const int4& e) {
-    const int g = e.x & 0xFFFF, ht = e.x >> 16;
+    const int g = tile_group(e.x), ht = tile_ht(e.x);
     const int ngroups = a.groups + (a.shared_rows > 0 ? 1 : 0);
-    return g < ngroups && ht > 0 && ht <= BM && e.y >= 0 && e.y < e.z && e.w >= 0;
+    return g < ngroups && ht > 0 && ht <= BM && tile_ci(e.x) < tile_cm(e.x) && e.y >= 0 && e.y < e.z && e.w >= 0;
 }
 
 template <bool DENSE, int BM>
@@ -67,32 +67,33 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
     if (mtile >= a.ntiles[0]) return false;
     const int4 t = a.tiles[mtile];
     if (!entry_ok<BM>(a, t)) return false;
-    ti.g = t.x & 0xFFFF;
+    ti.g = tile_group(t.x);
     ti.m0 = t.y;
     ti.shared = ti.g == a.groups;
     ti.off = t.w;
-    ti.rows = min(t.x >> 16, t.z - t.y);
+    ti.rows = min(tile_ht(t.x), t.z - t.y);
     return true;
 }
 
-// Workgroup -> (token tile, output-column tile) of the grouped wide GEMM. The live blocks go in
-// expert-major order and each XCD takes one contiguous eighth of it: the token tiles that share a slice
-// of an expert's weights run side by side on one XCD, and so do the column tiles that share a token
-// tile, so both come from HBM about once instead of once per XCD.
-// Block L of the order, decoded from the one entry at L / ntn (a tile of the same group): every tile of a
-// group starts at a multiple of its height, so the block's tile is known without reading its own entry.
+// Workgroup -> (token tile, output-column tile) of the grouped GEMMs. The live blocks go in chunk-major
+// order (plan.h) and each XCD takes one range of it: the token tiles of a chunk that share a slice of an
+// expert's weights run side by side on one XCD, and so do the column tiles that share a token tile, so
+// both come from HBM about once instead of once per XCD.
+// Block L of the order, decoded from the one entry at L / ntn (a tile of the same chunk): the tiles of a
+// chunk are consecutive tiles of one group, so the block's tile is known without reading its own entry.
 template <int BM>
 __device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, TileInfo& ti, int& ntile) {
-    const int4 e = a.tiles[L / ntn];
+    const int64_t at = L / ntn;
+    const int4 e = a.tiles[at];
     if (!entry_ok<BM>(a, e)) return false;
-    const int ht = e.x >> 16, m = (e.z + ht - 1) / ht;
-    const int64_t mtile = expert_major_tile(L, ntn, e.y / ht, m, ntile);
-    ti.g = e.x & 0xFFFF;
-    ti.m0 = (int)(mtile - (L / ntn - e.y / ht)) * ht;
+    const int ht = tile_ht(e.x);
+    const int64_t t = chunk_major_tile(L, ntn, tile_ci(e.x), tile_cm(e.x), ntile);
+    ti.g = tile_group(e.x);
+    ti.m0 = e.y + (int)(t - at) * ht;
     ti.shared = ti.g == a.groups;
     ti.off = e.w;
     ti.rows = min(ht, e.z - ti.m0);
-    return true;
+    return ti.rows > 0;
 }
 
 // With a K split of S, S consecutive positions of the order are the K ranges of one block (`ks` is the range).

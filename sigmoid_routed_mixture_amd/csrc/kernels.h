@@ -27,6 +27,9 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // persistent DMA kernel (kXcds for each GEMM).
 // With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit of the live
 // blocks, ks_ntn[i] column tiles each, on `cus` compute units; ks_force > 0 forces that split).
+// With `dealt` (and `bounds`) the tile list takes a dealt order of plan.h (DealtOrder) and `bounds` the exact
+// XCD ranges of that order for both GEMMs (when the chunks fit kMaxDealtChunks; else the plain order and
+// split). The plain order cuts groups into chunks of at most plain_cap tiles.
 struct XcdSplit {
     int32_t* bounds;
     int ntn[2];
@@ -36,6 +39,8 @@ struct XcdSplit {
     int ks_ntn[2];
     int cus;
     int ks_force;
+    int dealt;
+    int plain_cap;
 };
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
@@ -54,8 +59,8 @@ struct GemmArgs {
     void* out;                 // [rows, N]: bf16 (h; grouped down with out_bf16) or fp32
     const int32_t* counts;     // rows per group, or null for one dense group
     const int32_t* offsets;    // first row of each group
-    const int4* tiles;         // per tile {group | tile height << 16, first row in the group, rows of the group,
-                               // first permuted row of the group}
+    const int4* tiles;         // per tile {tile_word (group, height, place in its chunk), first row in the
+                               // group, rows of the group, first permuted row of the group} (plan.h)
     const int32_t* ntiles;     // number of valid tiles
     int dense_rows;            // rows of the dense group (also the row count of each logits split)
     int groups;                // number of groups (routed experts); tiles naming another group are skipped

@@ -2,8 +2,8 @@
 // within each expert (a stable counting sort). Work is split in chunks of 256 tokens: each chunk builds
 // an LDS bit matrix (expert x token-in-chunk), whose popcounts give the chunk's per-expert histogram and,
 // below a token's bit, that token's rank inside the chunk. One workgroup then turns the histograms into
-// per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles
-// ({expert | tile height << 16, first row}).
+// per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles (plan.h's
+// tile words, in the plain or the dealt order).
 // Pages: the routed experts receive (hidden, indices, weights) (nnterp encyclopedia glm_moe_dsa, support():
 // expert_indices and expert_weights are the experts' inputs); grouping rows by expert is how this build
 // hands each expert its tokens.
@@ -62,21 +62,112 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
     return incl - v;
 }
 
+// Writes the nt tiles of group g (n rows of height ht, its rows from `off` on in the permuted buffers) at
+// tiles[t0 ...] in the plain order: chunks of up to kMaxChunkTiles consecutive tiles.
+__device__ __forceinline__ void write_plain_tiles(int4* __restrict__ tiles, int t0, int g, int n, int ht, int nt,
+                                                  int off, int cap) {
+    const int nc = plain_chunks(nt, cap);
+    for (int c = 0; c < nc; ++c) {
+        const int f = chunk_first(c, nc, nt), cm = chunk_first(c + 1, nc, nt) - f;
+        for (int ci = 0; ci < cm; ++ci)
+            tiles[t0 + f + ci] = make_int4(tile_word(g, ht, ci, cm), (f + ci) * ht, n, off);
+    }
+}
+
 // Appends the folded shared expert's tiles (group E, all shared_rows tokens, its rows from shared_off on)
 // after the routed ones.
 __device__ __forceinline__ int append_shared_tiles(int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
                                                    int routed_tiles, int E, int shared_rows, int shared_off,
-                                                   int BM) {
+                                                   int BM, int cap) {
     const int tid = threadIdx.x;
     int ns = 0;
     if (shared_rows > 0) {
         const int hs = tile_height(shared_rows, BM);
         ns = (shared_rows + hs - 1) / hs;
-        for (int i = tid; i < ns; i += 256)
-            tiles[routed_tiles + i] = make_int4(E | (hs << 16), i * hs, shared_rows, shared_off);
+        if (tid == 0) write_plain_tiles(tiles, routed_tiles, E, shared_rows, hs, ns, shared_off, cap);
     }
     if (tid == 0) ntiles[0] = routed_tiles + ns;
     return routed_tiles + ns;
+}
+
+// The dealt order of plan.h, built by the 256 threads of the scan workgroup: thread e holds routed expert
+// e's row count n, tile height ht, tile count nt and first permuted row off (e < E); the folded shared
+// expert (shared_rows > 0: group E, its rows from shared_off on) comes before every expert. Writes the tile
+// list, its length and, for both GEMMs (ntn[v] column tiles), the XCD ranges of the blocks. Returns the
+// number of tiles, or -1 (nothing written) when the chunks exceed kMaxDealtChunks.
+__device__ int write_dealt_tiles(const XcdSplit& sp, int4* __restrict__ tiles, int32_t* __restrict__ ntiles, int E,
+                                 int n, int ht, int nt, int off, int shared_rows, int shared_off, int BM, int* sh) {
+    __shared__ int rows_of[kMaxE];
+    __shared__ int by_rank[kMaxE];
+    __shared__ int slots[kXcds * kDealtSlots];
+    const int e = threadIdx.x;
+    rows_of[e] = e < E ? n : 0;
+    for (int i = e; i < kXcds * kDealtSlots; i += 256) slots[i] = 0;
+    __syncthreads();
+    // rank among the experts: rows descending, then index (a permutation of 0 .. 255, empty experts last),
+    // or the index itself
+    int rank = e;
+    if (sp.dealt != kDealtIndex) {
+        rank = 0;
+        for (int j = 0; j < kMaxE; ++j) {
+            const int nj = rows_of[j];
+            rank += (nj > rows_of[e] || (nj == rows_of[e] && j < e)) ? 1 : 0;
+        }
+    }
+    const int nc = e < E ? dealt_chunks(nt) : 0;
+    const int hs = shared_rows > 0 ? tile_height(shared_rows, BM) : 0;
+    const int ns = shared_rows > 0 ? (shared_rows + hs - 1) / hs : 0;
+    const int ncs = dealt_chunks(ns);
+    by_rank[rank] = nc;
+    __syncthreads();
+    int routed_chunks = 0;
+    const int before = block_exclusive_scan(by_rank[e], sh, &routed_chunks); // chunks ahead of rank e
+    __syncthreads();
+    by_rank[e] = before;
+    __syncthreads();
+    const int all = ncs + routed_chunks;
+    if (all > kMaxDealtChunks) return -1; // uniform: every thread sees the same totals
+    const int c0 = ncs + by_rank[rank];  // this expert's first chunk in dealing order
+    // the (XCD, slot) place of chunk c in the list
+    auto place = [&](int c) {
+        const int x = deal_xcd(c);
+        const int sl = sp.dealt == kDealtAlternating ? alternate_slot(deal_slot(c), deal_count(x, all)) : deal_slot(c);
+        return x * kDealtSlots + sl;
+    };
+    for (int c = 0; c < nc; ++c) slots[place(c0 + c)] = chunk_first(c + 1, nc, nt) - chunk_first(c, nc, nt);
+    if (e == 0)
+        for (int c = 0; c < ncs; ++c) slots[place(c)] = chunk_first(c + 1, ncs, ns) - chunk_first(c, ncs, ns);
+    __syncthreads();
+    // first tile of every (XCD, slot): an exclusive scan of the XCD-major slot array, 8 slots per thread
+    constexpr int per = kXcds * kDealtSlots / 256;
+    int part = 0;
+    for (int i = 0; i < per; ++i) part += slots[e * per + i];
+    int total = 0;
+    int run = block_exclusive_scan(part, sh, &total);
+    for (int i = 0; i < per; ++i) {
+        const int v = slots[e * per + i];
+        slots[e * per + i] = run;
+        run += v;
+    }
+    __syncthreads();
+    for (int c = 0; c < nc; ++c) {
+        const int f = chunk_first(c, nc, nt), cm = chunk_first(c + 1, nc, nt) - f;
+        const int t0 = slots[place(c0 + c)];
+        for (int ci = 0; ci < cm; ++ci) tiles[t0 + ci] = make_int4(tile_word(e, ht, ci, cm), (f + ci) * ht, n, off);
+    }
+    if (e == 0)
+        for (int c = 0; c < ncs; ++c) {
+            const int f = chunk_first(c, ncs, ns), cm = chunk_first(c + 1, ncs, ns) - f;
+            const int t0 = slots[place(c)];
+            for (int ci = 0; ci < cm; ++ci)
+                tiles[t0 + ci] = make_int4(tile_word(E, hs, ci, cm), (f + ci) * hs, shared_rows, shared_off);
+        }
+    if (e < 2 * (kXcds + 1)) {
+        const int v = e / (kXcds + 1), x = e % (kXcds + 1);
+        sp.bounds[e] = sp.ntn[v] * (x < kXcds ? slots[x * kDealtSlots] : total);
+    }
+    if (e == 0) ntiles[0] = total;
+    return total;
 }
 
 // The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0).
@@ -126,6 +217,30 @@ __device__ void xcd_split(const XcdSplit& sp, int E, int n, int ht, int nt, int 
         }
 }
 
+// The grouped-GEMM tile list of every expert (thread e: expert e with n rows, its rows from `off` on) and
+// of the folded shared expert, in the dealt order when asked and possible, else the plain order (experts in
+// index order, the shared expert last); then the K splits, the plain order's work-balanced XCD split and the
+// zeroed block counters.
+__device__ void write_tiles(const XcdSplit& split, int4* __restrict__ tiles, int32_t* __restrict__ ntiles, int E,
+                            int n, int off, int BM, int shared_rows, int shared_off, int* sh) {
+    const int e = threadIdx.x;
+    const int ht = tile_height(n, BM);
+    const int nt = (e < E && BM > 0) ? (n + ht - 1) / ht : 0;
+    int all_tiles = -1;
+    if (split.dealt && split.bounds != nullptr)
+        all_tiles = write_dealt_tiles(split, tiles, ntiles, E, n, ht, nt, off, shared_rows, shared_off, BM, sh);
+    if (all_tiles < 0) {
+        const int cap = split.plain_cap > 0 ? split.plain_cap : kMaxChunkTiles;
+        int tiles_total = 0;
+        const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
+        if (nt > 0) write_plain_tiles(tiles, t0, e, n, ht, nt, off, cap);
+        all_tiles = append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, shared_off, BM, cap);
+        if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
+    }
+    write_ksplit(split, all_tiles);
+    if (split.ctr != nullptr && e < 4 * kXcds) split.ctr[e] = 0;
+}
+
 __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int chunks, int E,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
@@ -147,14 +262,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     if (e < E) offsets[e] = off;
     if (e == 0) offsets[E] = total;
     if (tiles == nullptr) return;
-    const int ht = tile_height(n, BM);
-    const int nt = (e < E && BM > 0) ? (n + ht - 1) / ht : 0;
-    int tiles_total = 0;
-    const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-    for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(e | (ht << 16), i * ht, n, off);
-    write_ksplit(split, append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, shared_off, BM));
-    if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
-    if (split.ctr != nullptr && e < 4 * kXcds) split.ctr[e] = 0;
+    write_tiles(split, tiles, ntiles, E, n, off, BM, shared_rows, shared_off, sh);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -209,16 +317,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         offs[tid] = off;
     }
     if (tid == 0) offsets[E] = total;
-    if (tiles != nullptr) {
-        const int ht = tile_height(n, BM);
-        const int nt = (tid < E && BM > 0) ? (n + ht - 1) / ht : 0;
-        int tiles_total = 0;
-        const int t0 = block_exclusive_scan(nt, sh, &tiles_total);
-        for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int4(tid | (ht << 16), i * ht, n, off);
-        write_ksplit(split, append_shared_tiles(tiles, ntiles, tiles_total, E, shared_rows, T * k, BM));
-        if (split.bounds != nullptr) xcd_split(split, E, n, ht, nt, t0, tiles_total, sh);
-        if (split.ctr != nullptr && tid < 4 * kXcds) split.ctr[tid] = 0;
-    }
+    if (tiles != nullptr) write_tiles(split, tiles, ntiles, E, n, off, BM, shared_rows, T * k, sh);
     __syncthreads();
     const int t = tid;
     if (t >= T) return;

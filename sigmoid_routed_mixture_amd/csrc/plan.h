@@ -84,15 +84,71 @@ constexpr int64_t xcd_block_order(int64_t bid, int64_t live) {
     const int64_t L = (bid % kXcds) * chunk + local;
     return (local < chunk && L < live) ? L : -1;
 }
-// Expert-major order: position L lies in the range of an expert whose tiles are [first, first + m) of
-// the tile list (L / ntn is tile i of the expert); inside the range, output-column tile 0 of every token
-// tile comes first, then column tile 1, and so on. Returns the tile-list index, sets the column tile.
-constexpr int64_t expert_major_tile(int64_t L, int ntn, int i, int m, int& ntile) {
-    const int64_t first = L / ntn - i;
+// Chunk-major order: the tile list is a sequence of chunks, each a run of consecutive tiles of one group
+// (expert); the blocks of a chunk whose tiles are [first, first + cm) of the list are positions
+// [first * ntn, (first + cm) * ntn) of the order, output-column tile 0 of every tile of the chunk first, then
+// column tile 1, and so on (the chunk's tiles share each weight slice side by side). Position L lies in the
+// chunk of the tile at L / ntn, which is tile ci of its chunk. Returns the block's tile-list index, sets its
+// column tile.
+constexpr int64_t chunk_major_tile(int64_t L, int ntn, int ci, int cm, int& ntile) {
+    const int64_t first = L / ntn - ci;
     const int64_t r = L - first * ntn;
-    ntile = (int)(r / m);
-    return first + r % m;
+    ntile = (int)(r / cm);
+    return first + r % cm;
 }
+
+// A tile of the device-side list is an int4 {word, first row of the tile in its group, rows of the group,
+// first permuted row of the group}; the word packs the group (9 bits), the tile height (9 bits), the
+// tile's index in its chunk (7 bits) and the chunk's tile count minus one (7 bits).
+constexpr int kTileEntryBytes = 16;
+constexpr int kMaxChunkTiles = 128;
+constexpr int tile_word(int g, int ht, int ci, int cm) {
+    return (int)((uint32_t)g | (uint32_t)ht << 9 | (uint32_t)ci << 18 | (uint32_t)(cm - 1) << 25);
+}
+constexpr int tile_group(int w) { return (int)((uint32_t)w & 511u); }
+constexpr int tile_ht(int w) { return (int)(((uint32_t)w >> 9) & 511u); }
+constexpr int tile_ci(int w) { return (int)(((uint32_t)w >> 18) & 127u); }
+constexpr int tile_cm(int w) { return (int)(((uint32_t)w >> 25) & 127u) + 1; }
+// Chunks of a group of nt tiles, chunk c of nc holding tiles [c nt / nc, (c + 1) nt / nc): in the plain order
+// one chunk per kMaxChunkTiles tiles; in the dealt order (below) one per 4 tiles up to one per XCD (a big group
+// spreads over every XCD, and each chunk's tiles share its weight slices), beyond 1024 tiles one per
+// kMaxChunkTiles.
+constexpr int plain_chunks(int nt, int cap = kMaxChunkTiles) { return nt <= 0 ? 0 : (nt + cap - 1) / cap; }
+// Tiles per chunk of the plain order by default. A chunk's blocks run side by side on one XCD, its tiles
+// sharing each weight slice and its column tiles each token tile; past ~16 tiles the blocks that share a
+// token tile run too far apart to find it in L2 (a 32768-row expert in one chunk re-read its tokens from
+// HBM for every column tile: the skewed GLM-5 workload 20.0 ms against 18.2 ms with chunks of 16).
+constexpr int kPlainChunkTiles = 16;
+constexpr int dealt_chunks(int nt) {
+    if (nt <= 0) return 0;
+    if (nt > kXcds * kMaxChunkTiles) return (nt + kMaxChunkTiles - 1) / kMaxChunkTiles;
+    const int nc = (nt + 3) / 4;
+    return nc < kXcds ? nc : kXcds;
+}
+constexpr int chunk_first(int c, int nc, int nt) { return (int)((int64_t)c * nt / nc); }
+
+// Dealt order of the persistent routed GEMMs (prefill): the chunks of every group, the largest groups first
+// (rows descending, then index; a folded shared expert before all), are dealt to the XCDs in snake order
+// (0, 1, ..., 7, 7, 6, ..., 0, 0, 1, ...); XCD x's blocks are its chunks in dealing order. Each XCD thus gets
+// a like share of big and small experts, the blocks that run side by side on an XCD have like heights, and
+// its last blocks are its smallest. Up to kMaxDealtChunks chunks (else the plain order).
+// Three forms: groups by size (rows descending) or by index; within an XCD the dealing order, or (by size)
+// its chunks alternately from the largest and the smallest end.
+enum DealtOrder { kDealtSorted = 1, kDealtIndex = 2, kDealtAlternating = 3 };
+constexpr int kMaxDealtChunks = 2048;
+constexpr int kDealtSlots = kMaxDealtChunks / kXcds; // chunks per XCD at most
+constexpr int deal_xcd(int c) {
+    const int j = c % (2 * kXcds);
+    return j < kXcds ? j : 2 * kXcds - 1 - j;
+}
+constexpr int deal_slot(int c) { return 2 * (c / (2 * kXcds)) + (c % (2 * kXcds) >= kXcds ? 1 : 0); }
+// Chunks XCD x receives when `total` chunks are dealt.
+constexpr int deal_count(int x, int total) {
+    const int q = total / (2 * kXcds), r = total % (2 * kXcds);
+    return 2 * q + (x < r ? 1 : 0) + (2 * kXcds - 1 - x < r ? 1 : 0);
+}
+// Alternating form: slot s of the m slots of an XCD moves to place 2 s (its larger half) or 2 (m - 1 - s) + 1.
+constexpr int alternate_slot(int s, int m) { return 2 * s < m ? 2 * s : 2 * (m - 1 - s) + 1; }
 
 // Work-balanced split of the DMA kernel's grouped blocks over the XCDs: XCD x takes blocks
 // [bounds[x], bounds[x + 1]) of the expert-major order, at most dma_xcd_cap(...) of them (the grid gives
@@ -142,9 +198,6 @@ constexpr int decode_ksplit(int64_t blocks, int cus) {
     return r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1; // one round already: no split; else 0.525 r2 < r1
 }
 
-// A tile of the device-side list: {group | tile height << 16, first row in the group, rows of the group,
-// first permuted row of the group} (int4), so a workgroup decodes its block with one load.
-constexpr int kTileEntryBytes = 16;
 
 struct Layout {
     // byte offsets inside the workspace (each 256-byte aligned); size_t(-1) = not present

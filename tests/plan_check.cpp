@@ -118,11 +118,26 @@ int main() {
         const bool skew = trial % 3 == 0;
         for (int t = 0; t < T * k; ++t) counts[skew ? (int)(next() % 4) % E : (int)(next() % E)]++;
         counts[E] = shared ? T : 0;
+        // tiles in chunks (plain: up to kMaxChunkTiles per chunk; every third trial the dealt sizes), each
+        // entry packed as the device writes it: {tile_word, first row}
         std::vector<std::pair<int, int>> tiles; // {expert, first row}
+        std::vector<int> words;
         std::vector<int> height(E + 1);
         for (int e = 0; e <= E; ++e) {
             height[e] = moe::tile_height(counts[e], BM);
-            for (int r = 0; r < counts[e]; r += height[e]) tiles.push_back({e, r});
+            const int nt = counts[e] > 0 ? (counts[e] + height[e] - 1) / height[e] : 0;
+            const int nc = trial % 3 == 1 ? moe::dealt_chunks(nt) : moe::plain_chunks(nt);
+            for (int c = 0; c < nc; ++c) {
+                const int f = moe::chunk_first(c, nc, nt), cm = moe::chunk_first(c + 1, nc, nt) - f;
+                CHECK(cm >= 1 && cm <= moe::kMaxChunkTiles, "chunk of %d tiles", cm);
+                for (int ci = 0; ci < cm; ++ci) {
+                    tiles.push_back({e, (f + ci) * height[e]});
+                    const int w = moe::tile_word(e, height[e], ci, cm);
+                    CHECK(moe::tile_group(w) == e && moe::tile_ht(w) == height[e] && moe::tile_ci(w) == ci &&
+                              moe::tile_cm(w) == cm, "tile word e=%d ht=%d ci=%d cm=%d", e, height[e], ci, cm);
+                    words.push_back(w);
+                }
+            }
         }
         const int64_t live = (int64_t)tiles.size() * ntn;
         int64_t grid = (moe::max_tiles(T, E, k, BM) + (shared ? moe::shared_tiles(T, BM) : 0)) * ntn;
@@ -138,12 +153,15 @@ int main() {
             hi[x] = std::max(hi[x], L);
             ++cnt[x];
             const auto entry = tiles[L / ntn];
-            const int ht = height[entry.first];
-            const int m = (counts[entry.first] + ht - 1) / ht;
+            const int w = words[L / ntn];
             int nt = -1;
-            const int64_t mt = moe::expert_major_tile(L, ntn, entry.second / ht, m, nt);
+            const int64_t mt = moe::chunk_major_tile(L, ntn, moe::tile_ci(w), moe::tile_cm(w), nt);
             CHECK(mt >= 0 && mt < (int64_t)tiles.size() && tiles[mt].first == entry.first,
                   "block %lld: tile %lld outside expert %d", (long long)b, (long long)mt, entry.first);
+            // the device derives the block's first row from the entry it read and the tile distance
+            if (mt >= 0 && mt < (int64_t)tiles.size())
+                CHECK(entry.second + (mt - L / ntn) * moe::tile_ht(w) == tiles[mt].second, "first row of tile %lld",
+                      (long long)mt);
             CHECK(nt >= 0 && nt < ntn, "block %lld: column tile %d of %d", (long long)b, nt, ntn);
             if (mt >= 0 && mt < (int64_t)tiles.size() && nt >= 0 && nt < ntn) seen[mt * ntn + nt]++;
         }
@@ -153,6 +171,31 @@ int main() {
         ++orders;
     }
     std::printf("%d block orders checked\n", orders);
+
+    // the dealt order: chunk c goes to slot deal_slot(c) of XCD deal_xcd(c); every (XCD, slot) is taken once,
+    // in dealing order within an XCD, and the XCDs take turns in snake order
+    {
+        std::vector<int> owner(moe::kXcds * moe::kDealtSlots, -1);
+        std::vector<int> last(moe::kXcds, -1);
+        for (int c = 0; c < moe::kMaxDealtChunks; ++c) {
+            const int x = moe::deal_xcd(c), sl = moe::deal_slot(c);
+            CHECK(x >= 0 && x < moe::kXcds && sl >= 0 && sl < moe::kDealtSlots, "chunk %d -> (%d, %d)", c, x, sl);
+            if (x < 0 || x >= moe::kXcds || sl < 0 || sl >= moe::kDealtSlots) continue;
+            CHECK(owner[x * moe::kDealtSlots + sl] == -1, "slot (%d, %d) taken twice", x, sl);
+            owner[x * moe::kDealtSlots + sl] = c;
+            CHECK(sl == last[x] + 1, "XCD %d slots out of order at chunk %d", x, c);
+            last[x] = sl;
+        }
+        CHECK(moe::deal_xcd(7) == 7 && moe::deal_xcd(8) == 7 && moe::deal_xcd(15) == 0 && moe::deal_xcd(16) == 0,
+              "snake dealing");
+        // chunks per group: at least one per 128 tiles, at most 8 for groups up to 1024 tiles
+        for (int nt = 1; nt <= 5000; ++nt) {
+            const int nc = moe::dealt_chunks(nt), pc = moe::plain_chunks(nt);
+            CHECK(nc >= 1 && (nt > 1024 || nc <= 8) && (nt + nc - 1) / nc <= moe::kMaxChunkTiles &&
+                      (nt < 32 || nc >= 8 || nt > 1024) && pc == (nt + 127) / 128,
+                  "chunks of %d tiles: dealt %d, plain %d", nt, nc, pc);
+        }
+    }
 
     // workspace queries: the largest layout over every T' <= T, so a workspace sized for the largest batch
     // serves every smaller one (brute force over T' for small T, sampled T up to past the split ranges)

@@ -31,7 +31,7 @@ def tune(moe):
             moe.moe_set_tuning(getattr(moe, name), value)
 
     yield set_knobs
-    for knob in range(4):
+    for knob in range(moe.MOE_TUNE_KNOBS):
         moe.moe_set_tuning(knob, 0)
 
 

@@ -36,7 +36,7 @@ def tune(moe):
             moe.moe_set_tuning(getattr(moe, name), value)
 
     yield set_knobs
-    for knob in range(4):
+    for knob in range(moe.MOE_TUNE_KNOBS):
         moe.moe_set_tuning(knob, 0)
 
 
@@ -179,6 +179,20 @@ def test_xcd_split_does_not_change_results(moe, tune):
     b = run_forward(moe, cfg, d)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["mid", "glm47_prefill", "glm5_prefill", "glm5_skewed"])
+def test_block_order_does_not_change_results(moe, tune, name):
+    # every block order of the persistent GEMMs (index order in long or short chunks, the dealt orders) runs
+    # the same blocks, each computing exactly what it computes in the others
+    say("[block order] %s" % name)
+    cfg, h, d = case(name)
+    a = run_forward(moe, cfg, d)
+    for order in range(1, 5):
+        tune(MOE_TUNE_ORDER=order)
+        b = run_forward(moe, cfg, d)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), "order %d" % order
 
 
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
