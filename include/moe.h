@@ -141,6 +141,29 @@ moe_status moe_forward(const moe_bf16* x, const moe_bf16* w_router, const float*
                        int32_t* topk_ids, float* topk_gates, int32_t* expert_counts, void* workspace,
                        size_t workspace_bytes, void* stream, void* stream_shared);
 
+/*
+ * moe_forward without a caller workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same arguments, computation and
+ * results as moe_forward (bit for bit), minus workspace, workspace_bytes and stream_shared (the shared expert
+ * runs on `stream`). The workspace is a file-scope device array of moe_forward_noalloc_max_bytes() bytes
+ * (64 MiB) inside the library, one per device, held until the process ends; the call allocates nothing.
+ *   Sizes whose workspace (the layout moe_forward uses for exactly these sizes) exceeds that maximum return
+ *   MOE_ERR_WORKSPACE with the byte counts in moe_last_error(), and enqueue nothing. GLM-5 shapes fit up to
+ *   T = 64 tokens, GLM-4.7-Flash shapes up to T = 512.
+ *   Every call on a device uses that device's one array and leaves its contents there; each call writes
+ *   everything it reads (its block counters included) before reading it, so nothing carries over. Calls
+ *   that overlap on one device (two streams, two host threads) race on the array: order them on one
+ *   stream. Calls on different devices do not share it.
+ *   The first call on each device looks up that device's array (hipGetSymbolAddress), a query that
+ *   allocates nothing; capture a graph only after one call on the device has returned.
+ */
+size_t moe_forward_noalloc_max_bytes(void);
+moe_status moe_forward_noalloc(const moe_bf16* x, const moe_bf16* w_router, const float* bias, const moe_bf16* w1,
+                               const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1, const moe_bf16* ws3,
+                               const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is, float scale,
+                               float* out, int32_t* topk_ids, float* topk_gates, int32_t* expert_counts,
+                               void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

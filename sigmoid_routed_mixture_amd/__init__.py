@@ -9,6 +9,9 @@ include/moe.h. PyTorch supplies device memory and streams. The functions keep th
     moe_permute(topk_ids, E, counts, offsets, row_token, slot_row, workspace, x=None, x_perm=None, stream=None)
     moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids=None,
                 topk_gates=None, expert_counts=None, stream=None, stream_shared=None)
+    moe_forward_noalloc_max_bytes()
+    moe_forward_noalloc(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, topk_ids=None,
+                        topk_gates=None, expert_counts=None, stream=None)
 
 the knobs of include/moe_tuning.h (tests and benchmarks only):
 
@@ -68,6 +71,10 @@ _lib.moe_dense_mlp_workspace_bytes.argtypes = [_i] * 3
 _lib.moe_dense_mlp_workspace_bytes.restype = _sz
 _lib.moe_dense_mlp.argtypes = [_p] * 4 + [_i] * 3 + [_p, _p, _sz, _p]
 _lib.moe_dense_mlp.restype = _i
+_lib.moe_forward_noalloc_max_bytes.argtypes = []
+_lib.moe_forward_noalloc_max_bytes.restype = _sz
+_lib.moe_forward_noalloc.argtypes = [_p] * 9 + [_i] * 6 + [_f] + [_p] * 4 + [_p]
+_lib.moe_forward_noalloc.restype = _i
 _lib.moe_set_tuning.argtypes = [_i, _i]
 _lib.moe_set_tuning.restype = _i
 _lib.moe_get_tuning.argtypes = [_i]
@@ -81,7 +88,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WO
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_route", "moe_permute",
                     "moe_forward", "moe_forward_profiled", "moe_status_string", "moe_last_error",
                     "moe_forward_routed", "moe_block_workspace_bytes", "moe_block_forward",
-                    "moe_dense_mlp_workspace_bytes", "moe_dense_mlp", "moe_set_tuning", "moe_get_tuning")
+                    "moe_dense_mlp_workspace_bytes", "moe_dense_mlp", "moe_set_tuning", "moe_get_tuning",
+                    "moe_forward_noalloc", "moe_forward_noalloc_max_bytes")
 # Knobs of include/moe_tuning.h (tests and benchmarks only; 0 = the size rules).
 MOE_TUNE_GEMM_PATH, MOE_TUNE_XCD_SPLIT, MOE_TUNE_PERSIST, MOE_TUNE_KSPLIT, MOE_TUNE_ORDER = range(5)
 MOE_TUNE_KNOBS = 5
@@ -205,6 +213,26 @@ def moe_forward(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, wor
                 topk_gates=None, expert_counts=None, stream=None, stream_shared=None):
     _forward(_lib.moe_forward, (), x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, topk_ids,
              topk_gates, expert_counts, stream, stream_shared)
+
+
+def moe_forward_noalloc_max_bytes() -> int:
+    return _lib.moe_forward_noalloc_max_bytes()
+
+
+def moe_forward_noalloc(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, topk_ids=None,
+                        topk_gates=None, expert_counts=None, stream=None):
+    """moe_forward on the library's own per-device scratch (include/moe.h): no workspace argument, nothing
+    allocated; sizes whose workspace exceeds moe_forward_noalloc_max_bytes() raise MoEError."""
+    T, H = x.shape
+    E, I, _ = w1.shape
+    Is = 0 if ws1 is None else ws1.shape[0]
+    bf = torch.bfloat16
+    _check(_lib.moe_forward_noalloc(
+        _ptr(x, bf, "x"), _ptr(w_router, bf, "w_router"), _ptr(bias, torch.float32, "bias"), _ptr(w1, bf, "w1"),
+        _ptr(w3, bf, "w3"), _ptr(w2, bf, "w2"), _ptr(ws1, bf, "ws1"), _ptr(ws3, bf, "ws3"), _ptr(ws2, bf, "ws2"),
+        T, H, E, k, I, Is, float(scale), _ptr(out, torch.float32, "out"), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_gates, torch.float32, "topk_gates"), _ptr(expert_counts, torch.int32, "expert_counts"),
+        _stream(stream, x.device)))
 
 
 def moe_forward_profiled(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, events,

@@ -77,6 +77,32 @@ moe_status order_after(hipStream_t waiter, hipStream_t signaller, hipEvent_t ev)
     return MOE_OK;
 }
 
+// Scratch of moe_forward_noalloc: the forward pass's workspace as file-scope device memory, one copy per
+// device, held until the process ends. Host code never uses the array's name as an address (on the host it
+// is only a stand-in): each device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct DeviceScratch {
+    std::once_flag once;
+    hipError_t status = hipSuccess;
+    void* ptr = nullptr;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+moe_status device_scratch(void** out) {
+    int dev = 0;
+    MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index >= 64");
+    DeviceScratch& d = g_scratch[dev];
+    std::call_once(d.once, [&d]() { d.status = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch)); });
+    MOE_HIP(d.status, "hipGetSymbolAddress (scratch)");
+    if (d.ptr == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress (scratch) returned null");
+    *out = d.ptr;
+    return MOE_OK;
+}
+
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
@@ -585,6 +611,30 @@ moe_status moe_dense_mlp(const moe_bf16* x, const moe_bf16* w1, const moe_bf16* 
     float* part = moe::dense_partial_bytes(T, H, I) > 0 ? reinterpret_cast<float*>(ws + hbytes) : nullptr;
     MOE_TRY(dense_mlp(path, x, w1, w3, w2, T, H, I, reinterpret_cast<uint16_t*>(ws), out, part, s, "dense"));
     return MOE_OK;
+}
+
+size_t moe_forward_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_forward_noalloc(const moe_bf16* x, const moe_bf16* w_router, const float* bias, const moe_bf16* w1,
+                               const moe_bf16* w3, const moe_bf16* w2, const moe_bf16* ws1, const moe_bf16* ws3,
+                               const moe_bf16* ws2, int T, int H, int E, int k, int I, int Is, float scale,
+                               float* out, int32_t* topk_ids, float* topk_gates, int32_t* expert_counts,
+                               void* stream) {
+    g_last_error.clear();
+    MOE_TRY(from_check(moe::check_sizes(T, H, E, k, I, Is, true)));
+    if (T == 0) return MOE_OK;
+    const size_t need = moe::forward_layout(T, H, E, k, I, Is).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "moe_forward_noalloc: these sizes need " + std::to_string(need) +
+                                           " bytes of scratch, above its " + std::to_string(kNoAllocScratchBytes) +
+                                           "-byte maximum (use moe_forward with a caller workspace)");
+    void* ws = nullptr;
+    MOE_TRY(device_scratch(&ws));
+    // the same pass as moe_forward on the device's scratch (the shared expert on `stream`); every buffer
+    // of that pass that must start at zero (the persistent GEMMs' block counters) is cleared by its kernels
+    return forward_impl(plain_request(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, T, H, E, k, I, Is, scale, out,
+                                      topk_ids, topk_gates, expert_counts, ws, kNoAllocScratchBytes, stream,
+                                      nullptr));
 }
 
 moe_status moe_forward_profiled(const moe_bf16* x, const moe_bf16* w_router, const float* bias,
