@@ -39,7 +39,10 @@ typedef enum moe_tune_knob {
        orders, the chunks dealt over the XCDs in turn: 2 largest experts first, 3 in index order, 4 largest
        first alternating with the smallest within each XCD. */
     MOE_TUNE_ORDER = 4,
-    MOE_TUNE_KNOBS = 5 /* number of knobs */
+    /* Shared expert above the decode sizes, when it has the routed width and no stream of its own: 0 by size
+       (one more group of the persistent routed GEMMs), 1 a dense MLP on the main stream before them. */
+    MOE_TUNE_SHARED = 5,
+    MOE_TUNE_KNOBS = 6 /* number of knobs */
 } moe_tune_knob;
 
 /* Sets a knob. MOE_ERR_INVALID_ARG for an unknown knob or a value outside the knob's range (nothing

@@ -106,7 +106,7 @@ moe_status device_scratch(void** out) {
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -258,22 +258,32 @@ moe_status forward_impl(const Request& q) {
     int32_t* ntiles = static_cast<int32_t*>(at(L.ntiles));
     uint16_t* h_perm = static_cast<uint16_t*>(at(L.h_perm));
     float* y_perm = static_cast<float*>(at(L.y_perm)); // per-slot rows, fp32 or bf16 (slot_rows_bf16)
-    // The shared expert: one more group of the routed GEMMs (rows T * k onwards of h_perm and y_perm) when
-    // it has the routed width, else a dense MLP of its own.
-    const bool fold = moe::shared_fold(T, E, k, I, Is);
-    const bool dense_shared = Is > 0 && !fold;
-    uint16_t* h_sh = dense_shared ? static_cast<uint16_t*>(at(L.h_sh)) : nullptr;
-    float* y_sh = dense_shared ? static_cast<float*>(at(L.y_sh)) : nullptr;
-    if (fold) y_sh = y_perm + (size_t)T * k * H;
-
-    hipStream_t s0 = static_cast<hipStream_t>(q.stream);
-    hipStream_t s1 = static_cast<hipStream_t>(q.stream_shared);
-    const bool two_streams = dense_shared && s1 != nullptr && s1 != s0;
-    DeviceEvents* ev = nullptr;
-    if (two_streams) MOE_TRY(device_events(&ev));
-
     const moe::GemmPath path = pick_path(T, E, k, H, I, Is);
     const int BM = moe::path_bm(path);
+    hipStream_t s0 = static_cast<hipStream_t>(q.stream);
+    hipStream_t s1 = static_cast<hipStream_t>(q.stream_shared);
+    const bool own_stream = s1 != nullptr && s1 != s0;
+    // the shared expert at decode sizes: one more group of the routed GEMMs (rows T * k onwards of h_perm and
+    // y_perm) when it has the routed width
+    const bool fold = moe::shared_fold(T, E, k, I, Is);
+    // the DMA kernel's work-balanced XCD split (computed for both grouped GEMMs, used by the down GEMM)
+    const bool balanced = path == moe::GemmPath::Dma && !fold && tuning(MOE_TUNE_XCD_SPLIT) == 0;
+    // the grouped DMA GEMMs run persistent (one workgroup per CU claiming blocks from per-XCD counters)
+    const bool persist = balanced && tuning(MOE_TUNE_PERSIST) == 0;
+    // above the decode sizes, with the routed width and no stream of its own: one more group of the persistent
+    // routed GEMMs, its tiles spread over the XCDs, its fp32 rows in y_shared; else a dense MLP
+    const bool fold_pre = persist && moe::shared_fold_prefill(T, E, k, I, Is) && !own_stream &&
+                          tuning(MOE_TUNE_SHARED) == 0;
+    const bool grouped_shared = fold || fold_pre;
+    const bool dense_shared = Is > 0 && !grouped_shared;
+    uint16_t* h_sh = nullptr;
+    if (dense_shared) // its h: the rows after the routed ones when it has their width
+        h_sh = Is == I ? h_perm + (size_t)T * k * I : static_cast<uint16_t*>(at(L.h_sh));
+    float* y_sh = Is > 0 && !fold ? static_cast<float*>(at(L.y_sh)) : nullptr;
+    if (fold) y_sh = y_perm + (size_t)T * k * H;
+    const bool two_streams = dense_shared && own_stream;
+    DeviceEvents* ev = nullptr;
+    if (two_streams) MOE_TRY(device_events(&ev));
 
     auto mark = [&](int i) -> moe_status {
         if (q.events == nullptr) return MOE_OK;
@@ -294,9 +304,7 @@ moe_status forward_impl(const Request& q) {
                 "router");
     }
     MOE_TRY(mark(1));
-    // the DMA kernel's work-balanced XCD split (computed for both grouped GEMMs, used by the down GEMM)
-    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (fold ? moe::shared_tiles(T, BM) : 0);
-    const bool balanced = path == moe::GemmPath::Dma && !fold && tuning(MOE_TUNE_XCD_SPLIT) == 0;
+    const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (grouped_shared ? moe::shared_tiles(T, BM) : 0);
     moe::XcdSplit split{};
     if (balanced) {
         split.bounds = static_cast<int32_t*>(at(L.xcd_bounds));
@@ -304,8 +312,6 @@ moe_status forward_impl(const Request& q) {
         split.ntn[1] = moe::dma_ntn(false, H);
         for (int v = 0; v < 2; ++v) split.cap[v] = (int)moe::dma_xcd_cap(grid_tiles, split.ntn[v]);
     }
-    // the grouped DMA GEMMs run persistent (one workgroup per CU claiming blocks from per-XCD counters)
-    const bool persist = balanced && tuning(MOE_TUNE_PERSIST) == 0;
     if (persist) split.ctr = static_cast<int32_t*>(at(L.xcd_bounds)) + 2 * (moe::kXcds + 1);
     // block order of the persistent GEMMs: experts in index order, each cut into chunks of at most
     // kPlainChunkTiles tiles (the MOE_TUNE_ORDER knob picks the longer chunks or one of the dealt orders)
@@ -313,6 +319,7 @@ moe_status forward_impl(const Request& q) {
     const bool dealt = persist && order >= 2;
     split.dealt = dealt ? order - 1 : 0;
     split.plain_cap = order == 1 ? moe::kMaxChunkTiles : moe::kPlainChunkTiles;
+    split.spread_shared = fold_pre ? 1 : 0;
     // decode-sized grouped GEMMs: the permutation picks a K split of 1 or 2 for each from the live block count
     const int ks_knob = tuning(MOE_TUNE_KSPLIT);
     const bool ks_off = ks_knob == 1, ks_on = ks_knob == 2;
@@ -333,7 +340,7 @@ moe_status forward_impl(const Request& q) {
         ks_gate_up = ks_on || most > cus;
     }
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, fold ? T : 0, split,
+                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, grouped_shared ? T : 0, split,
                                 s0),
             "permute");
     MOE_TRY(mark(2));
@@ -349,7 +356,7 @@ moe_status forward_impl(const Request& q) {
     MOE_TRY(mark(3));
 
     auto add_shared = [&](moe::GemmArgs& a, const moe_bf16* wa, const moe_bf16* wb) {
-        if (!fold) return;
+        if (!grouped_shared) return;
         a.ws_a = wa;
         a.ws_b = wb;
         a.shared_rows = T;
@@ -373,7 +380,7 @@ moe_status forward_impl(const Request& q) {
     add_shared(r1, q.ws1, q.ws3);
     if (persist) r1.work_ctr = reinterpret_cast<unsigned long long*>(split.ctr);
     if (dealt) r1.xcd_bounds = split.bounds;
-    const int h_rows = T * k + (fold ? T : 0);
+    const int h_rows = T * k + (grouped_shared ? T : 0);
     if (ks_gate_up) {
         r1.ksplit_dev = ks_flag;
         r1.part = static_cast<float*>(at(L.ks_part));
@@ -405,6 +412,7 @@ moe_status forward_impl(const Request& q) {
     add_shared(r2, q.ws2, nullptr);
     const bool ybf = moe::slot_rows_bf16(T, E, k, I, Is) && !ksplit;
     r2.out_bf16 = ybf ? 1 : 0;
+    if (fold_pre) r2.out_shared = y_sh;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 

@@ -639,15 +639,18 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         float* stg = reinterpret_cast<float*>(wave < 4 ? ws0 : ws1) + (wave & 3) * (16 * 68);
         const int c4 = lane & 15, r4 = lane >> 4;
         const int colw = ntile * 256 + 64 * wm;
-        // K split: the second half's rows go to the partial buffer, the combine adds them
-        float* yout = ks == 0 ? static_cast<float*>(a.out) : a.part;
+        // K split: the second half's rows go to the partial buffer, the combine adds them. A folded shared
+        // expert with rows of its own writes fp32 rows there, indexed by token.
+        const bool own = !DENSE && ti.shared && a.out_shared != nullptr;
+        float* yout = own ? a.out_shared : (ks == 0 ? static_cast<float*>(a.out) : a.part);
+        const size_t row0 = own ? (size_t)ti.m0 : (size_t)ti.off + ti.m0;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<f32x4*>(stg + rl * 68 + 16 * i + 4 * kg) = acc[i][j];
             __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the block is in LDS
-            if (!DENSE && a.out_bf16) {
+            if (!DENSE && a.out_bf16 && !own) {
                 // bf16 rows (N % 64 == 0, no K split): 8 lanes of 16 bytes per row segment, 8 rows per store
                 const int c8 = lane & 7, r8 = lane >> 3;
 #pragma unroll
@@ -673,8 +676,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
                     const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 68 + 4 * c4);
                     const int m = 16 * (2 * j + wn) + t;
                     const int col = colw + 4 * c4;
-                    if (m < ti.rows && col < N)
-                        *reinterpret_cast<f32x4*>(yout + ((size_t)ti.off + ti.m0 + m) * N + col) = v;
+                    if (m < ti.rows && col < N) *reinterpret_cast<f32x4*>(yout + (row0 + m) * N + col) = v;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next block overwrites the area
@@ -1010,6 +1012,10 @@ template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     // bf16 output rows: grouped down GEMMs only, whole 64-column chunks, no K split
     if (a.out_bf16 && (KIND != GemmKind::DownF32 || DENSE || a.N % 64 != 0 || a.ksplit_dev != nullptr))
+        return hipErrorInvalidValue;
+    // separate fp32 rows of a folded shared expert: the LDS-copy kernel's grouped down GEMM only
+    if (a.out_shared != nullptr && (KIND != GemmKind::DownF32 || DENSE || path != GemmPath::Dma ||
+                                    a.shared_rows <= 0 || a.ksplit_dev != nullptr))
         return hipErrorInvalidValue;
     const bool wide = path != GemmPath::Skinny;
     int ntn;

@@ -41,6 +41,7 @@ struct XcdSplit {
     int ks_force;
     int dealt;
     int plain_cap;
+    int spread_shared; // plain order: the shared group's tiles in kXcds chunks spread through the list
 };
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
@@ -79,6 +80,8 @@ struct GemmArgs {
                                // the second K half's fp32 rows [part_rows][N] (the first half goes to out)
     int part_rows;
     int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32
+    float* out_shared;         // grouped down GEMM (LDS-copy kernel): fp32 rows [shared_rows, N] of the folded
+                               // shared expert, row = its token, or null (its rows then follow the routed ones)
 };
 enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);

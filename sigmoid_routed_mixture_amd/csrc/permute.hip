@@ -62,16 +62,27 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
     return incl - v;
 }
 
-// Writes the nt tiles of group g (n rows of height ht, its rows from `off` on in the permuted buffers) at
-// tiles[t0 ...] in the plain order: chunks of up to kMaxChunkTiles consecutive tiles.
-__device__ __forceinline__ void write_plain_tiles(int4* __restrict__ tiles, int t0, int g, int n, int ht, int nt,
-                                                  int off, int cap) {
-    const int nc = plain_chunks(nt, cap);
+// Writes tiles [f0, f0 + cnt) of group g (n rows, tiles of height ht, its rows from `off` on in the permuted
+// buffers) at tiles[t0 ...] in the plain order: chunks of up to `cap` consecutive tiles.
+__device__ __forceinline__ void write_plain_tiles(int4* __restrict__ tiles, int t0, int g, int n, int ht, int cnt,
+                                                  int off, int cap, int f0 = 0) {
+    const int nc = plain_chunks(cnt, cap);
     for (int c = 0; c < nc; ++c) {
-        const int f = chunk_first(c, nc, nt), cm = chunk_first(c + 1, nc, nt) - f;
+        const int f = chunk_first(c, nc, cnt), cm = chunk_first(c + 1, nc, cnt) - f;
         for (int ci = 0; ci < cm; ++ci)
-            tiles[t0 + f + ci] = make_int4(tile_word(g, ht, ci, cm), (f + ci) * ht, n, off);
+            tiles[t0 + f + ci] = make_int4(tile_word(g, ht, ci, cm), (f0 + f + ci) * ht, n, off);
     }
+}
+
+// The shared group (group E, shared_rows rows) cut into kXcds pieces, piece j holding its tiles
+// [chunk_first(j, kXcds, ns), chunk_first(j + 1, kXcds, ns)), placed right before routed expert
+// shared_piece_at(j, E): with equal-count XCD ranges over the list, each XCD's range then holds about one
+// piece. Pieces before expert e's tiles: those with shared_piece_at(j, E) <= e.
+__device__ __forceinline__ int shared_piece_at(int j, int E) { return (j * E + kXcds - 1) / kXcds; }
+__device__ __forceinline__ int shared_pieces_before(int e, int E) {
+    int J = 0;
+    for (int j = 0; j < kXcds; ++j) J += shared_piece_at(j, E) <= e ? 1 : 0;
+    return J;
 }
 
 // Appends the folded shared expert's tiles (group E, all shared_rows tokens, its rows from shared_off on)
@@ -229,6 +240,33 @@ __device__ void write_tiles(const XcdSplit& split, int4* __restrict__ tiles, int
     int all_tiles = -1;
     if (split.dealt && split.bounds != nullptr)
         all_tiles = write_dealt_tiles(split, tiles, ntiles, E, n, ht, nt, off, shared_rows, shared_off, BM, sh);
+    if (all_tiles < 0 && split.spread_shared && shared_rows > 0) {
+        // plain order with the shared group's kXcds pieces spread through it
+        __shared__ int routed_start[kMaxE + 1];
+        const int cap = split.plain_cap > 0 ? split.plain_cap : kMaxChunkTiles;
+        int routed_total = 0;
+        const int t0r = block_exclusive_scan(nt, sh, &routed_total);
+        routed_start[e] = t0r;
+        if (e == 0) routed_start[kMaxE] = routed_total;
+        __syncthreads();
+        const int hs = tile_height(shared_rows, BM);
+        const int ns = (shared_rows + hs - 1) / hs;
+        if (nt > 0)
+            write_plain_tiles(tiles, t0r + chunk_first(shared_pieces_before(e, E), kXcds, ns), e, n, ht, nt, off, cap);
+        if (e < kXcds) {
+            const int p = shared_piece_at(e, E); // p <= E: before expert p, or at the end
+            const int f = chunk_first(e, kXcds, ns), cnt = chunk_first(e + 1, kXcds, ns) - f;
+            const int at = (p < E ? routed_start[p] : routed_total) + f;
+            if (cnt > 0) write_plain_tiles(tiles, at, E, shared_rows, hs, cnt, shared_off, cap, f);
+        }
+        all_tiles = routed_total + ns;
+        if (e == 0) ntiles[0] = all_tiles;
+        if (split.bounds != nullptr && e < 2 * (kXcds + 1)) { // equal block counts per XCD for both GEMMs
+            const int v = e / (kXcds + 1), x = e % (kXcds + 1);
+            const int live = all_tiles * split.ntn[v], chunk = (live + kXcds - 1) / kXcds;
+            split.bounds[e] = min(x * chunk, live);
+        }
+    }
     if (all_tiles < 0) {
         const int cap = split.plain_cap > 0 ? split.plain_cap : kMaxChunkTiles;
         int tiles_total = 0;

@@ -89,11 +89,15 @@ Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm)
     L.xcd_bounds = take((2 * (kXcds + 1) + 4 * kXcds) * 4); // two XCD splits, then 2 x kXcds 64-bit counters
     L.partial = take((size_t)router_splits(T, H, E) * (size_t)T * (size_t)E * 4);
     const size_t rows = Tk + (fold ? (size_t)T : 0);
-    L.h_perm = take(rows * (size_t)I * 2);
-    // per-slot rows: bf16 where slot_rows_bf16 holds (never with the shared expert folded in), else fp32
+    // h: the routed rows, then (shared expert of the routed width) its T rows, whether it runs as a group of
+    // the routed GEMMs or as a dense MLP
+    const bool same_width = Is > 0 && Is == I;
+    L.h_perm = take((Tk + (same_width ? (size_t)T : 0)) * (size_t)I * 2);
+    // per-slot rows: bf16 where slot_rows_bf16 holds (never with the shared expert folded in at decode), else
+    // fp32; the decode fold's shared rows follow them
     L.y_perm = take(rows * (size_t)H * (slot_rows_bf16(T, E, k, I, Is) ? 2 : 4));
     const bool dense_shared = Is > 0 && !fold;
-    L.h_sh = dense_shared ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
+    L.h_sh = dense_shared && !same_width ? take((size_t)T * (size_t)Is * 2) : size_t(-1);
     L.y_sh = dense_shared ? take((size_t)T * (size_t)H * 4) : size_t(-1);
     const size_t shp = dense_shared ? dense_partial_bytes(T, H, Is) : 0;
     L.sh_partial = shp > 0 ? take(shp) : size_t(-1);

@@ -180,6 +180,13 @@ constexpr bool shared_fold(int T, int E, int k, int I, int Is) {
     return Is > 0 && Is == I && (int64_t)T * k <= (int64_t)kSkinnyBM * E;
 }
 constexpr int64_t shared_tiles(int T, int BM) { return ((int64_t)T + BM - 1) / BM; }
+// Above the decode fold, the shared expert with the routed width can still be one more group of the
+// persistent routed GEMMs (when the caller gives it no stream of its own): its tiles, cut into one chunk per
+// XCD, are spread through the block order so that every XCD's range holds one; its h rows follow the T * k
+// routed rows, its output goes to fp32 y_shared rows of its own (the routed per-slot rows may be bf16).
+constexpr bool shared_fold_prefill(int T, int E, int k, int I, int Is) {
+    return Is > 0 && Is == I && !shared_fold(T, E, k, I, Is);
+}
 // The down GEMM's per-slot rows (read back once by the combine) are stored as bf16 when every token has at
 // least 8 gated slots and the shared expert is not folded in (so neither a K split nor shared rows are among
 // them), else as fp32. A bf16 row adds one rounding of each slot's output before the fp32 weighted sum; over

@@ -60,12 +60,15 @@ int main() {
                                 {L.slot_row, Tk * 4, "slot_row"}, {L.chunk_base, chunks * E * 4, "chunk_base"},
                                 {L.tiles, tiles_need, "tiles"}, {L.ntiles, 4, "ntiles"},
                                 {L.partial, (size_t)moe::router_splits(T, H, E) * T * E * 4, "partial"},
-                                {L.h_perm, rows * I * 2, "h_perm"},
+                                {L.h_perm, (Tk + (Is == I ? (size_t)T : 0)) * I * 2, "h_perm"},
                                 {L.y_perm, rows * H * (moe::slot_rows_bf16(T, E, k, I, Is) ? 2 : 4), "y_perm"}};
-                            CHECK(fold == (L.h_sh == size_t(-1) && L.y_sh == size_t(-1) && Is > 0),
-                                  "dense shared buffers only without the fold (I=%d Is=%d)", I, Is);
+                            // shared rows outside the decode fold: y_shared fp32 [T, H]; h in the rows after the
+                            // routed ones when Is == I, else a region of its own
+                            CHECK((L.y_sh == size_t(-1)) == (fold || Is == 0) &&
+                                      (L.h_sh == size_t(-1)) == (fold || Is == 0 || Is == I),
+                                  "shared buffers (T=%d E=%d k=%d I=%d Is=%d)", T, E, k, I, Is);
                             if (Is > 0 && !fold) {
-                                rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
+                                if (Is != I) rs.push_back({L.h_sh, (size_t)T * Is * 2, "h_sh"});
                                 rs.push_back({L.y_sh, (size_t)T * H * 4, "y_sh"});
                             }
                             if (L.sh_partial != size_t(-1))

@@ -195,6 +195,19 @@ def test_block_order_does_not_change_results(moe, tune, name):
             assert np.array_equal(x, y), "order %d" % order
 
 
+@pytest.mark.parametrize("name", ["mid", "glm47_prefill", "glm5_prefill"])
+def test_prefill_shared_fold_matches_dense_mlp_bitwise(moe, tune, name):
+    # above the decode sizes the shared expert runs as one more group of the persistent routed GEMMs (its
+    # tiles spread over the XCDs, fp32 rows of its own); its tiles compute exactly what the dense MLP's do
+    say("[shared fold] %s" % name)
+    cfg, h, d = case(name)
+    a = run_forward(moe, cfg, d)
+    tune(MOE_TUNE_SHARED=1)
+    b = run_forward(moe, cfg, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
 def test_persistent_grid_does_not_change_results(moe, tune, name):
     # one workgroup per CU claiming blocks from the XCD counters (and from the back of other XCDs' ranges
