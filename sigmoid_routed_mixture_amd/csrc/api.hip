@@ -136,28 +136,36 @@ moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, 
     const int BM = moe::path_bm(path);
     const int64_t tiles = ((int64_t)T + BM - 1) / BM;
     const bool skinny = path == moe::GemmPath::Skinny;
-    const int s1 = skinny && part ? moe::dense_splits(true, T, I, H) : 1;
-    const int s2 = skinny && part ? moe::dense_splits(false, T, H, I) : 1;
+    // few rows on the LDS-copy kernel: K split by the device's CU count (partials in `part`, then reduced)
+    const bool dma_split = path == moe::GemmPath::Dma && T <= moe::kDmaSplitMaxT && part != nullptr;
+    int cus = 0;
+    if (dma_split) MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
+    const int s1 = skinny && part ? moe::dense_splits(true, T, I, H) : dma_split ? moe::dma_dense_splits(true, T, I, H, cus) : 1;
+    const int s2 = skinny && part ? moe::dense_splits(false, T, H, I) : dma_split ? moe::dma_dense_splits(false, T, H, I, cus) : 1;
     moe::GemmArgs g1{};
     g1.act = x;
     g1.w_a = w1;
     g1.w_b = w3;
-    g1.out = s1 > 1 ? static_cast<void*>(part) : static_cast<void*>(h);
+    g1.out = s1 > 1 && skinny ? static_cast<void*>(part) : static_cast<void*>(h);
     g1.dense_rows = T;
     g1.N = I;
     g1.K = H;
     g1.ksplit = s1;
+    g1.part = part;
+    g1.part_rows = T;
     const std::string w(what);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), (w + " gate/up GEMM").c_str());
     if (s1 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::GateUp, part, s1, T, I, h, s), (w + " gate/up reduce").c_str());
     moe::GemmArgs g2{};
     g2.act = h;
     g2.w_a = w2;
-    g2.out = s2 > 1 ? static_cast<void*>(part) : static_cast<void*>(out);
+    g2.out = s2 > 1 && skinny ? static_cast<void*>(part) : static_cast<void*>(out);
     g2.dense_rows = T;
     g2.N = H;
     g2.K = I;
     g2.ksplit = s2;
+    g2.part = part;
+    g2.part_rows = T;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, tiles, s), (w + " down GEMM").c_str());
     if (s2 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::DownF32, part, s2, T, H, out, s), (w + " down reduce").c_str());
     return MOE_OK;

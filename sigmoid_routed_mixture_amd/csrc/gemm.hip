@@ -642,7 +642,9 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         // K split: the second half's rows go to the partial buffer, the combine adds them. A folded shared
         // expert with rows of its own writes fp32 rows there, indexed by token.
         const bool own = !DENSE && ti.shared && a.out_shared != nullptr;
-        float* yout = own ? a.out_shared : (ks == 0 ? static_cast<float*>(a.out) : a.part);
+        float* yout = own ? a.out_shared
+                          : DENSE && S > 1 ? a.part + (size_t)ks * a.part_rows * N // every range writes a partial
+                                           : (ks == 0 ? static_cast<float*>(a.out) : a.part);
         const size_t row0 = own ? (size_t)ti.m0 : (size_t)ti.off + ti.m0;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
@@ -726,9 +728,16 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
 
 template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
-    const int64_t bid = blockIdx.x;
+    int64_t bid = blockIdx.x;
     int ntile, S = 1, ks = 0;
     if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+    if (DENSE && a.ksplit > 1) { // dense, few rows: the grid is the K ranges times the blocks of one range
+        S = a.ksplit;
+        const int64_t per = (int64_t)((a.dense_rows + kDRows - 1) / kDRows) * ntn;
+        ks = (int)(bid / per);
+        if (ks >= S) return;
+        bid -= (int64_t)ks * per;
+    }
     TileInfo ti;
     if (DENSE) {
         ntile = (int)(bid % ntn);
@@ -1023,7 +1032,14 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         ntn = KIND == GemmKind::GateUp ? (a.N + kWBN / 2 - 1) / (kWBN / 2) : (a.N + kWBN - 1) / kWBN;
     else
         ntn = KIND == GemmKind::GateUp ? a.N / 64 : (a.N + 127) / 128;
-    const int splits = (KIND == GemmKind::Logits || (!wide && DENSE)) && a.ksplit > 1 ? a.ksplit : 1;
+    const int splits =
+        (KIND == GemmKind::Logits || (DENSE && (path == GemmPath::Skinny || path == GemmPath::Dma))) && a.ksplit > 1
+            ? a.ksplit : 1;
+    // a dense split on the LDS-copy kernel writes fp32 partials of dense_rows rows per K range
+    if constexpr (DENSE && KIND != GemmKind::Logits)
+        if (path == GemmPath::Dma && splits > 1 && (a.part == nullptr || a.part_rows < a.dense_rows ||
+                                                    a.K / kBK < splits))
+            return hipErrorInvalidValue;
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
     if (KIND != GemmKind::Logits && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {

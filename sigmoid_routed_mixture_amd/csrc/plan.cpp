@@ -50,7 +50,7 @@ int router_splits(int T, int H, int E) {
 
 GemmPath gemm_path(int, int, int) { return GemmPath::Dma; }
 
-GemmPath dense_path(int T) { return T <= kSkinnyBM ? GemmPath::Skinny : GemmPath::Dma; }
+GemmPath dense_path(int) { return GemmPath::Dma; }
 
 GemmPath fallback_path(int T, int E, int k) {
     const int64_t slots = (int64_t)T * k;
@@ -130,10 +130,30 @@ int dense_splits(bool gate_up, int rows, int N, int K) {
     return (int)std::max<int64_t>(1, std::min(want, cap));
 }
 
+int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus) {
+    if (rows <= 0 || rows > kDmaSplitMaxT || N <= 0 || K <= 0 || cus <= 0) return 1;
+    const int64_t tiles = ((int64_t)rows + kTallBM - 1) / kTallBM;
+    const int64_t B = tiles * dma_ntn(gate_up, N);
+    const int steps = K / 64;
+    const int cap = std::max(1, std::min(kMaxDenseSplits, steps / 4));
+    int best = 1;
+    double best_t = 0;
+    for (int S = 1; S <= cap; ++S) {
+        const double t = (double)((B * S + cus - 1) / cus) * ((double)steps / S + 3.0);
+        if (S == 1 || t < best_t) best = S, best_t = t;
+    }
+    return best;
+}
+
 size_t dense_partial_bytes(int T, int H, int Id) {
     const int s1 = dense_splits(true, T, Id, H), s2 = dense_splits(false, T, H, Id);
-    const size_t a = s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0;
-    const size_t b = s2 > 1 ? (size_t)s2 * T * H * 4 : 0;
+    size_t a = s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0;
+    size_t b = s2 > 1 ? (size_t)s2 * T * H * 4 : 0;
+    if (T > 0 && T <= kDmaSplitMaxT) { // the LDS-copy kernel's splits, whatever the device's CU count
+        const int m1 = std::max(1, std::min(kMaxDenseSplits, H / 256)), m2 = std::max(1, std::min(kMaxDenseSplits, Id / 256));
+        if (m1 > 1) a = std::max(a, (size_t)m1 * T * 2 * Id * 4);
+        if (m2 > 1) b = std::max(b, (size_t)m2 * T * H * 4);
+    }
     return std::max(a, b);
 }
 

@@ -50,8 +50,8 @@ int router_splits(int T, int H, int E);
 // Grouped GEMMs take the Dma kernel at every size (measured faster than the weight-streaming kernel from
 // one token to 512 at the GLM-5 and GLM-4.7-Flash shapes, decode included).
 GemmPath gemm_path(int T, int E, int k);
-// A dense GEMM of T rows (shared expert, dense MLP): the weight-streaming kernel with split K up to 16 rows
-// (one token tile cannot fill the GPU otherwise), else the Dma kernel.
+// A dense GEMM of T rows (shared expert, dense MLP): the Dma kernel, with split K up to kDmaSplitMaxT rows
+// (one token tile cannot fill the GPU otherwise; measured faster than the weight-streaming kernel's split).
 GemmPath dense_path(int T);
 // When an operand does not fit the Dma kernel: the weight-streaming kernel when experts average at most 16
 // rows, else the register-streaming one with 128-token tiles below 192 rows on average and 256-token
@@ -228,6 +228,13 @@ size_t permute_scratch_bytes(int T, int E);
 // K ranges of a dense GEMM (rows x N outputs, reduction K) on the weight-streaming kernel: enough for
 // ~1024 workgroups, at most kMaxDenseSplits, each range at least 256 wide. 1 = no split.
 int dense_splits(bool gate_up, int rows, int N, int K);
+// A dense GEMM of up to kDmaSplitMaxT rows on the LDS-copy kernel has too few blocks (one token tile times
+// the column tiles) to fill the GPU, so it splits K into S ranges of at least 4 K steps (S <= kMaxDenseSplits):
+// the S that minimises the launch's rounds of blocks, ceil(B S / cus), times a block's length in K steps plus
+// 3 steps of prologue, (K / 64) / S + 3 (B blocks unsplit). The ranges write fp32 partials, which a reduction
+// kernel adds in K order.
+constexpr int kDmaSplitMaxT = 64;
+int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus);
 // fp32 partials of a dense SwiGLU MLP (gate/up then down, one region reused) on that kernel; 0 if unsplit.
 size_t dense_partial_bytes(int T, int H, int Id);
 

@@ -300,6 +300,22 @@ int main() {
                 const size_t need = std::max(s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0,
                                              s2 > 1 ? (size_t)s2 * T * H * 4 : 0);
                 CHECK(moe::dense_partial_bytes(T, H, Id) >= need, "partials T=%d H=%d I=%d", T, H, Id);
+                // the LDS-copy kernel's splits at few rows, on any CU count: 4 K steps per range at least, and
+                // partials within the same region
+                for (int cus : {1, 80, 256, 304, 1024}) {
+                    const int d1 = moe::dma_dense_splits(true, T, Id, H, cus), d2 = moe::dma_dense_splits(false, T, H, Id, cus);
+                    CHECK(d1 >= 1 && d1 <= moe::kMaxDenseSplits && (d1 == 1 || (H / 64) / d1 >= 4) &&
+                              (T <= moe::kDmaSplitMaxT || d1 == 1),
+                          "dma gate/up splits %d (T=%d H=%d I=%d cus=%d)", d1, T, H, Id, cus);
+                    CHECK(d2 >= 1 && d2 <= moe::kMaxDenseSplits && (d2 == 1 || (Id / 64) / d2 >= 4) &&
+                              (T <= moe::kDmaSplitMaxT || d2 == 1),
+                          "dma down splits %d (T=%d H=%d I=%d cus=%d)", d2, T, H, Id, cus);
+                    const size_t nd = std::max(d1 > 1 ? (size_t)d1 * T * 2 * Id * 4 : 0, d2 > 1 ? (size_t)d2 * T * H * 4 : 0);
+                    CHECK(moe::dense_partial_bytes(T, H, Id) >= nd, "dma partials T=%d H=%d I=%d", T, H, Id);
+                }
+                // GLM-5 dense MLP at 16 tokens on 256 CUs: 96 gate/up blocks in ranges that fill whole rounds
+                CHECK(moe::dma_dense_splits(true, 16, 12288, 6144, 256) >= 5 &&
+                          moe::dma_dense_splits(false, 16, 6144, 12288, 256) >= 8, "GLM-5 dense splits");
                 CHECK(moe::dense_workspace_bytes(T, H, Id) >= (size_t)T * Id * 2 + need, "dense workspace");
                 const moe::Layout L = moe::forward_layout(T, H, 8, 2, Id == 64 ? 128 : 64, Id);
                 CHECK(need == 0 || (L.sh_partial != size_t(-1) && L.x_norm == size_t(-1) &&
@@ -322,8 +338,7 @@ int main() {
                 const moe::GemmPath p = moe::gemm_path(T, E, k), f = moe::fallback_path(T, E, k);
                 const bool skinny = (int64_t)T * k <= (int64_t)moe::kSkinnyBM * E;
                 CHECK(p == moe::GemmPath::Dma, "path T=%d E=%d k=%d", T, E, k);
-                CHECK(moe::dense_path(T) == (T <= moe::kSkinnyBM ? moe::GemmPath::Skinny : moe::GemmPath::Dma),
-                      "dense path T=%d", T);
+                CHECK(moe::dense_path(T) == moe::GemmPath::Dma, "dense path T=%d", T);
                 CHECK(skinny ? f == moe::GemmPath::Skinny : (f == moe::GemmPath::Wide || f == moe::GemmPath::Tall),
                       "fallback T=%d E=%d k=%d", T, E, k);
                 CHECK(moe::path_bm(moe::GemmPath::Dma) == moe::kTallBM, "dma tile height");
