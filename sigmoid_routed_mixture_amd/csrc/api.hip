@@ -342,10 +342,10 @@ moe_status forward_impl(const Request& q) {
         split.ks_ntn[1] = moe::dma_ntn(false, H);
         split.cus = cus;
         split.ks_force = ks_on ? 2 : 0;
-        // a split needs two rounds of blocks: with at most one (every expert and the shared one active)
-        // the gate/up reduction is not launched (the down GEMM's halves are added by the combine)
-        const int64_t most = (std::min<int64_t>(E, (int64_t)T * k) + moe::shared_tiles(T, BM)) * split.ks_ntn[0];
-        ks_gate_up = ks_on || most > cus;
+        // the gate/up split needs a reduction launch: only when the experts the batch is expected to reach
+        // would split (the down GEMM's halves are added by the combine, with no launch of their own)
+        const int64_t expect = (moe::expected_active(T, E, k) + moe::shared_tiles(T, BM)) * split.ks_ntn[0];
+        ks_gate_up = ks_on || moe::decode_ksplit(expect, cus) == 2;
     }
     MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
                                 static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, grouped_shared ? T : 0, split,

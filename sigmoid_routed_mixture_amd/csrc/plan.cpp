@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cmath>
 
 namespace moe {
 
@@ -35,9 +36,11 @@ Check check_aligned(const void* p, const char* name, size_t align) {
 
 int router_splits(int T, int H, int E) {
     if (T <= kRouterSmallT) {
+        // ~256 one-wave workgroups of 16 experts, but K ranges of at least 256 (a workgroup then reads 8 KB
+        // or more of W_r; shorter ranges only multiply the partials the top-k kernel sums)
         const int64_t groups = (std::max(E, 1) + 15) / 16;
         int64_t s = (256 + groups - 1) / groups;
-        s = std::max<int64_t>(1, std::min<int64_t>(s, std::min(kRouterMaxSplits, H / 32)));
+        s = std::max<int64_t>(1, std::min<int64_t>(s, std::min(kRouterMaxSplits, H / 256)));
         return (int)s;
     }
     // enough K ranges that the logits GEMM has >= 256 workgroups of 128 tokens, at most 32 and at most one
@@ -49,6 +52,12 @@ int router_splits(int T, int H, int E) {
 }
 
 GemmPath gemm_path(int, int, int) { return GemmPath::Dma; }
+
+int expected_active(int T, int E, int k) {
+    if (T <= 0 || E <= 0 || k <= 0) return 0;
+    const double miss = std::pow(1.0 - 1.0 / E, (double)T * k);
+    return std::min(E, (int)std::ceil(E * (1.0 - miss) - 1e-9));
+}
 
 GemmPath dense_path(int) { return GemmPath::Dma; }
 

@@ -42,8 +42,9 @@ Check check_sizes(int T, int H, int E, int k, int I, int Is, bool need_I);
 Check check_aligned(const void* p, const char* name, size_t align = 16);
 
 // K-split of the router's logit GEMM: the number of K ranges. Up to kRouterSmallT tokens the logits run on
-// one-wave workgroups of 16 experts x 32-wide K chunks, split so the launch has >= 256 workgroups (at most
-// kRouterMaxSplits ranges); above, on the wide GEMM kernel with 64-wide chunks (at most 32 ranges).
+// one-wave workgroups of 16 experts x 32-wide K chunks, split so the launch has up to 256 workgroups with K
+// ranges of at least 256 (at most kRouterMaxSplits ranges); above, on the wide GEMM kernel with 64-wide chunks
+// (at most 32 ranges).
 constexpr int kRouterSmallT = 16;
 constexpr int kRouterMaxSplits = 64;
 int router_splits(int T, int H, int E);
@@ -199,6 +200,10 @@ constexpr bool slot_rows_bf16(int T, int E, int k, int I, int Is) { return k >= 
 // counting about 5 % for the extra prologues and the fp32 partials (in one round the fixed costs win). The permutation picks the split from the live block
 // count, so the GEMM and the reduction that follows agree on it.
 constexpr int kKSplitMaxT = 64;
+// Experts a decode batch of T tokens is expected to reach with k picks each among E (uniform routing:
+// E (1 - (1 - 1/E)^(T k))), rounded up. The gate/up GEMM gets room for a K split (and its reduction launch)
+// only when decode_ksplit of that many experts' blocks (plus the folded shared expert's) would split.
+int expected_active(int T, int E, int k);
 constexpr int decode_ksplit(int64_t blocks, int cus) {
     if (blocks <= 0 || cus <= 0) return 1;
     const int64_t r1 = (blocks + cus - 1) / cus, r2 = (2 * blocks + cus - 1) / cus;

@@ -240,6 +240,14 @@ int main() {
             CHECK(moe::decode_ksplit(b, cus) == (r1 >= 2 && 0.525 * (double)r2 < (double)r1 ? 2 : 1),
                   "split b=%lld cus=%d", (long long)b, cus);
         }
+    // expected experts reached at decode: GLM-5 at 16 tokens (top-8 of 256) about 101, GLM-4.7-Flash (top-4 of
+    // 64) about 41; the gate/up GEMM splits K at the first and not at the second on 256 CUs
+    CHECK(moe::expected_active(16, 256, 8) == 101 && moe::expected_active(16, 64, 4) == 41 &&
+              moe::expected_active(1, 256, 8) == 8 && moe::expected_active(100000, 64, 4) == 64 &&
+              moe::expected_active(0, 64, 4) == 0,
+          "expected_active");
+    CHECK(moe::decode_ksplit((int64_t)(101 + 1) * 16, 256) == 2 && moe::decode_ksplit((int64_t)(41 + 1) * 12, 256) == 1,
+          "decode gate/up split at GLM-5 / GLM-4.7-Flash");
     // block claims of the persistent kernel: any interleaving of front (home) and back (other XCDs) claims
     // hands every block of the range out exactly once, and later claims get none
     {
