@@ -42,7 +42,10 @@ typedef enum moe_tune_knob {
     /* Shared expert above the decode sizes, when it has the routed width and no stream of its own: 0 by size
        (one more group of the persistent routed GEMMs), 1 a dense MLP on the main stream before them. */
     MOE_TUNE_SHARED = 5,
-    MOE_TUNE_KNOBS = 6 /* number of knobs */
+    /* Copy ring of the LDS-copy kernel at up to 32 tokens: 0 by size (three K steps of weights in flight),
+       1 the two-step ring of larger batches. */
+    MOE_TUNE_RING = 6,
+    MOE_TUNE_KNOBS = 7 /* number of knobs */
 } moe_tune_knob;
 
 /* Sets a knob. MOE_ERR_INVALID_ARG for an unknown knob or a value outside the knob's range (nothing

@@ -91,8 +91,9 @@ EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_r
                     "moe_dense_mlp_workspace_bytes", "moe_dense_mlp", "moe_set_tuning", "moe_get_tuning",
                     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes")
 # Knobs of include/moe_tuning.h (tests and benchmarks only; 0 = the size rules).
-MOE_TUNE_GEMM_PATH, MOE_TUNE_XCD_SPLIT, MOE_TUNE_PERSIST, MOE_TUNE_KSPLIT, MOE_TUNE_ORDER, MOE_TUNE_SHARED = range(6)
-MOE_TUNE_KNOBS = 6
+(MOE_TUNE_GEMM_PATH, MOE_TUNE_XCD_SPLIT, MOE_TUNE_PERSIST, MOE_TUNE_KSPLIT, MOE_TUNE_ORDER, MOE_TUNE_SHARED,
+ MOE_TUNE_RING) = range(7)
+MOE_TUNE_KNOBS = 7
 GEMM_PATHS = {"auto": 0, "wide": 1, "tall": 2, "dma": 3, "skinny": 4}
 
 
@@ -148,7 +149,7 @@ class tuned:
     `with tuned(MOE_TUNE_GEMM_PATH=3): ...`."""
 
     _names = {"MOE_TUNE_GEMM_PATH": 0, "MOE_TUNE_XCD_SPLIT": 1, "MOE_TUNE_PERSIST": 2, "MOE_TUNE_KSPLIT": 3,
-              "MOE_TUNE_ORDER": 4, "MOE_TUNE_SHARED": 5}
+              "MOE_TUNE_ORDER": 4, "MOE_TUNE_SHARED": 5, "MOE_TUNE_RING": 6}
 
     def __init__(self, **knobs):
         self.knobs = {self._names[k]: v for k, v in knobs.items()}

@@ -106,7 +106,7 @@ moe_status device_scratch(void** out) {
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1, 1};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -153,6 +153,7 @@ moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, 
     g1.ksplit = s1;
     g1.part = part;
     g1.part_rows = T;
+    g1.deep = path == moe::GemmPath::Dma && T <= moe::kDeepRingMaxT && tuning(MOE_TUNE_RING) == 0 ? 1 : 0;
     const std::string w(what);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), (w + " gate/up GEMM").c_str());
     if (s1 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::GateUp, part, s1, T, I, h, s), (w + " gate/up reduce").c_str());
@@ -166,6 +167,7 @@ moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, 
     g2.ksplit = s2;
     g2.part = part;
     g2.part_rows = T;
+    g2.deep = g1.deep;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, g2, tiles, s), (w + " down GEMM").c_str());
     if (s2 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::DownF32, part, s2, T, H, out, s), (w + " down reduce").c_str());
     return MOE_OK;
@@ -394,6 +396,9 @@ moe_status forward_impl(const Request& q) {
         r1.part = static_cast<float*>(at(L.ks_part));
         r1.part_rows = h_rows;
     }
+    // decode sizes: one workgroup per block with the deeper copy ring
+    const int deep = path == moe::GemmPath::Dma && !persist && T <= moe::kDeepRingMaxT && tuning(MOE_TUNE_RING) == 0;
+    r1.deep = deep;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     if (ks_gate_up)
         MOE_HIP(moe::launch_reduce_ksplit(r1.part, ks_flag, h_rows, I, h_perm, s0), "gate/up K-split reduction");
@@ -421,6 +426,7 @@ moe_status forward_impl(const Request& q) {
     const bool ybf = moe::slot_rows_bf16(T, E, k, I, Is) && !ksplit;
     r2.out_bf16 = ybf ? 1 : 0;
     if (fold_pre) r2.out_shared = y_sh;
+    r2.deep = deep;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 

@@ -461,10 +461,15 @@ __device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
 // tile's stores thread 0 claims the workgroup's next block, which wave 0 holds in `got` (-1: none left). With a K
 // split S of 2 (decode-sized gate/up launches) the tile computes K range `ks` and writes fp32 partials of g
 // and u instead of h.
-template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST>
+// DEEP (tiles of at most 32 rows, decode): rings of four weight buffers and four token buffers of 64 rows
+// (ws3, xs3 and the small xs0..xs3), so both operands are copied three K steps ahead: half again as many
+// bytes in flight per CU as the two-ahead ring, which is what bounds a CU's weight stream at decode.
+template <GemmKind KIND, bool DENSE, int NBW, bool PERSIST, bool DEEP = false>
 __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, int ntile, uint16_t* ws0,
                                          uint16_t* ws1, uint16_t* ws2, uint16_t* xs0, uint16_t* xs1, int wave0,
-                                         int ntn, int& got, int ks = 0, int S = 1) {
+                                         int ntn, int& got, int ks = 0, int S = 1, uint16_t* ws3 = nullptr,
+                                         uint16_t* xs2 = nullptr, uint16_t* xs3 = nullptr) {
+    static_assert(!DEEP || (NBW == 1 && !PERSIST), "the deep ring holds 64 token rows, one-shot tiles only");
     constexpr int XI = (NBW + 1) / 2; // token load instructions per wave and K step
     // persistent: the lane index comes from mbcnt, so nothing derived from the thread index has to stay in
     // registers from one tile to the next
@@ -591,35 +596,87 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     // for X1 and W1 (W2 may stay in flight), as in every later step. With fewer than three K steps the
     // copies of steps past the last one repeat the last step (unread; the end of the tile waits for them):
     // one branch-free sequence lets the compiler see that the first reads need X0 and W0 only.
-    constexpr int V2 = XI + 8;
-    static_assert(V2 <= 15, "vmcnt immediates below hold 4 bits");
-    load_x(xs0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(ws0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_x(xs1, min(1, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(ws1, min(1, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(ws2, min(2, nk - 1));
-    __builtin_amdgcn_s_waitcnt(0x0070 | V2); // vmcnt(XI + 8) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    read(f0a, f0b, ws0, xs0, 0);
-    // six steps per iteration (weight buffers cycle with period 3, token buffers with 2), then up to five
-    int s = 0;
-    for (; s + 6 <= nk; s += 6) {
-        step(ws0, xs0, ws1, xs1, s);
-        step(ws1, xs1, ws2, xs0, s + 1);
-        step(ws2, xs0, ws0, xs1, s + 2);
-        step(ws0, xs1, ws1, xs0, s + 3);
-        step(ws1, xs0, ws2, xs1, s + 4);
-        step(ws2, xs1, ws0, xs0, s + 5);
+    if constexpr (!DEEP) {
+        constexpr int V2 = XI + 8;
+        static_assert(V2 <= 15, "vmcnt immediates below hold 4 bits");
+        load_x(xs0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xs1, min(1, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws1, min(1, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws2, min(2, nk - 1));
+        __builtin_amdgcn_s_waitcnt(0x0070 | V2); // vmcnt(XI + 8) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        read(f0a, f0b, ws0, xs0, 0);
+        // six steps per iteration (weight buffers cycle with period 3, token buffers with 2), then up to five
+        int s = 0;
+        for (; s + 6 <= nk; s += 6) {
+            step(ws0, xs0, ws1, xs1, s);
+            step(ws1, xs1, ws2, xs0, s + 1);
+            step(ws2, xs0, ws0, xs1, s + 2);
+            step(ws0, xs1, ws1, xs0, s + 3);
+            step(ws1, xs0, ws2, xs1, s + 4);
+            step(ws2, xs1, ws0, xs0, s + 5);
+        }
+        if (s < nk) step(ws0, xs0, ws1, xs1, s);
+        if (s + 1 < nk) step(ws1, xs1, ws2, xs0, s + 1);
+        if (s + 2 < nk) step(ws2, xs0, ws0, xs1, s + 2);
+        if (s + 3 < nk) step(ws0, xs1, ws1, xs0, s + 3);
+        if (s + 4 < nk) step(ws1, xs0, ws2, xs1, s + 4);
+    } else {
+        // Deep ring: W(s) in ws[s % 4], X(s) in xs[s % 4]. Step s, after its barrier, copies X(s + 4) and
+        // W(s + 4) into the buffers of X(s) and W(s); the barrier that opens step s + 1 waits for X(s + 1) and
+        // W(s + 1), while the copies of steps s + 2 and s + 3 may stay in flight.
+        constexpr int VD = 2 * (XI + 4), VP = 3 * (XI + 4);
+        static_assert(VP <= 15, "vmcnt immediates below hold 4 bits");
+        auto dstep = [&](uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, int s) {
+            read(f1a, f1b, wc, xc, 1);
+            mma(f0a, f0b);
+            interleave();
+            __builtin_amdgcn_s_waitcnt(0x0070 | VD); // vmcnt(2 (XI + 4)) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            load_x(xc, min(s + 4, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(wc, min(s + 4, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            read(f0a, f0b, wn1, xn1, 0);
+            mma(f1a, f1b);
+            interleave();
+        };
+        // prologue: steps 0 to 3; the first barrier waits for X0 and W0
+        load_x(xs0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xs1, min(1, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws1, min(1, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xs2, min(2, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws2, min(2, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xs3, min(3, nk - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(ws3, min(3, nk - 1));
+        __builtin_amdgcn_s_waitcnt(0x0070 | VP); // vmcnt(3 (XI + 4)) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        read(f0a, f0b, ws0, xs0, 0);
+        // four steps per iteration, then up to three (none when the K steps are a multiple of four)
+        int s = 0;
+        for (; s + 4 <= nk; s += 4) {
+            dstep(ws0, xs0, ws1, xs1, s);
+            dstep(ws1, xs1, ws2, xs2, s + 1);
+            dstep(ws2, xs2, ws3, xs3, s + 2);
+            dstep(ws3, xs3, ws0, xs0, s + 3);
+        }
+        if (s < nk) dstep(ws0, xs0, ws1, xs1, s);
+        if (s + 1 < nk) dstep(ws1, xs1, ws2, xs2, s + 1);
+        if (s + 2 < nk) dstep(ws2, xs2, ws3, xs3, s + 2);
     }
-    if (s < nk) step(ws0, xs0, ws1, xs1, s);
-    if (s + 1 < nk) step(ws1, xs1, ws2, xs0, s + 1);
-    if (s + 2 < nk) step(ws2, xs0, ws0, xs1, s + 2);
-    if (s + 3 < nk) step(ws0, xs1, ws1, xs0, s + 3);
-    if (s + 4 < nk) step(ws1, xs0, ws2, xs1, s + 4);
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
     // persistent form: thread 0 claims the next block once the tile's stores are issued, so the claim's round
     // trip overlaps their drain
@@ -771,6 +828,41 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn
 #undef MOE_DMA_TILE
 }
 
+
+// The same one-shot GEMM for launches whose tiles all hold at most 32 rows (decode sizes): the deep ring of
+// dma_tile (four 32 KB weight buffers, four 8 KB token buffers of 64 rows: 160 KB).
+template <GemmKind KIND, bool DENSE>
+__global__ __launch_bounds__(kDThreads) void gemm_dma_deep_kernel(GemmArgs a, int ntn) {
+    int64_t bid = blockIdx.x;
+    int ntile, S = 1, ks = 0;
+    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+    if (DENSE && a.ksplit > 1) {
+        S = a.ksplit;
+        const int64_t per = (int64_t)((a.dense_rows + kDRows - 1) / kDRows) * ntn;
+        ks = (int)(bid / per);
+        if (ks >= S) return;
+        bid -= (int64_t)ks * per;
+    }
+    TileInfo ti;
+    if (DENSE) {
+        ntile = (int)(bid % ntn);
+        if (!tile_info<true, kDRows>(a, bid / ntn, ti)) return;
+    } else if (a.xcd_bounds != nullptr ? !balanced_block<kDRows>(a, ntn, bid, ti, ntile)
+                                       : !grouped_block<kDRows>(a, ntn, bid, ti, ntile, S, &ks)) {
+        return;
+    }
+    if (ti.rows > 32) return; // the host launches this kernel only when no tile can exceed 32 rows
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws2[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws3[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[64 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[64 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs2[64 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs3[64 * kBK];
+    int got = 0;
+    dma_tile<KIND, DENSE, 1, false, true>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, 0, ntn, got, ks, S, ws3, xs2, xs3);
+}
 
 // Persistent form of the grouped DMA GEMM: one workgroup per CU takes blocks from its XCD's counter (then
 // from the other XCDs') until none is left; each tile runs as in the one-shot kernel.
@@ -1022,6 +1114,10 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     // bf16 output rows: grouped down GEMMs only, whole 64-column chunks, no K split
     if (a.out_bf16 && (KIND != GemmKind::DownF32 || DENSE || a.N % 64 != 0 || a.ksplit_dev != nullptr))
         return hipErrorInvalidValue;
+    // the deep-ring kernel takes tiles of at most 32 rows: dense GEMMs of up to 32 rows, grouped ones whose
+    // groups hold at most 32 rows (the caller's guarantee: no more than 32 tokens)
+    if (a.deep && (path != GemmPath::Dma || (DENSE && a.dense_rows > 32) || a.work_ctr != nullptr))
+        return hipErrorInvalidValue;
     // separate fp32 rows of a folded shared expert: the LDS-copy kernel's grouped down GEMM only
     if (a.out_shared != nullptr && (KIND != GemmKind::DownF32 || DENSE || path != GemmPath::Dma ||
                                     a.shared_rows <= 0 || a.ksplit_dev != nullptr))
@@ -1069,7 +1165,9 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         if (path != GemmPath::Wide) return hipErrorInvalidValue;
         gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);
     } else {
-        if (path == GemmPath::Dma)
+        if (path == GemmPath::Dma && a.deep)
+            gemm_dma_deep_kernel<KIND, DENSE><<<grid, kDThreads, 0, stream>>>(a, ntn);
+        else if (path == GemmPath::Dma)
             gemm_dma_kernel<KIND, DENSE><<<grid, kDThreads, 0, stream>>>(a, ntn);
         else if (path == GemmPath::Wide)
             gemm_wide_kernel<KIND, DENSE, kWideBM><<<grid, kWThreads, 0, stream>>>(a, ntn, grid_tiles);

@@ -82,6 +82,8 @@ struct GemmArgs {
     int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32
     float* out_shared;         // grouped down GEMM (LDS-copy kernel): fp32 rows [shared_rows, N] of the folded
                                // shared expert, row = its token, or null (its rows then follow the routed ones)
+    int deep;                  // LDS-copy kernel, one workgroup per block: every tile has at most 32 rows, so
+                               // the kernel with the deeper copy ring (three K steps of weights ahead) runs
 };
 enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);

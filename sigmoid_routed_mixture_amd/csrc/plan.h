@@ -239,6 +239,9 @@ int dense_splits(bool gate_up, int rows, int N, int K);
 // 3 steps of prologue, (K / 64) / S + 3 (B blocks unsplit). The ranges write fp32 partials, which a reduction
 // kernel adds in K order.
 constexpr int kDmaSplitMaxT = 64;
+// Up to this many tokens every tile of a launch has at most 32 rows (a group never holds more rows than there
+// are tokens), and the LDS-copy kernel runs with its deeper copy ring.
+constexpr int kDeepRingMaxT = 32;
 int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus);
 // fp32 partials of a dense SwiGLU MLP (gate/up then down, one region reused) on that kernel; 0 if unsplit.
 size_t dense_partial_bytes(int T, int H, int Id);

@@ -208,6 +208,19 @@ def test_prefill_shared_fold_matches_dense_mlp_bitwise(moe, tune, name):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("name,T", [("tiny", 32), ("glm5_decode", 16), ("glm47_decode", 16), ("glm5_decode", 3)])
+def test_decode_copy_ring_does_not_change_results(moe, tune, name, T):
+    # up to 32 tokens the grouped GEMMs copy three K steps ahead; every tile computes what the two-step ring
+    # computes, bit for bit
+    say("[copy ring] %s T=%d" % (name, T))
+    cfg, h, d = case(name)
+    a = run_forward(moe, cfg, d, T=T)
+    tune(MOE_TUNE_RING=1)
+    b = run_forward(moe, cfg, d, T=T)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
 def test_persistent_grid_does_not_change_results(moe, tune, name):
     # one workgroup per CU claiming blocks from the XCD counters (and from the back of other XCDs' ranges
