@@ -444,13 +444,17 @@ __device__ __forceinline__ void xcd_range(const GemmArgs& a, int ntn, int x, int
 // The block a persistent workgroup of XCD x takes next (thread 0), or -1 when none is left: the front of its
 // own XCD's range, then the back of the other XCDs' ranges (the blocks their own workgroups would reach
 // last), through the counters of claim_block.
-__device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x) {
+// With `home_old` (>= 0: what an earlier front claim on the own XCD's counter returned) the own range is
+// decided from it and only the other XCDs' counters are tried.
+__device__ __forceinline__ int grab_block(const GemmArgs& a, int ntn, int x, long long home_old = -1) {
     for (int d = 0; d < kXcds; ++d) {
         const int y = (x + d) % kXcds;
         int lo, hi;
         xcd_range(a, ntn, y, lo, hi);
         if (lo >= hi) continue;
-        const unsigned long long old = atomicAdd(a.work_ctr + y, d == 0 ? kClaimFront : kClaimBack);
+        const unsigned long long old = d == 0 && home_old >= 0
+                                           ? (unsigned long long)home_old
+                                           : atomicAdd(a.work_ctr + y, d == 0 ? kClaimFront : kClaimBack);
         const int64_t c = claim_block(lo, hi, old, d == 0);
         if (c >= 0) return (int)c;
     }
@@ -576,6 +580,15 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     // last one repeat the last step (data the workgroup has just read, so they come from L2, and nobody
     // reads them): every step runs the same branch-free code, which keeps the compiler from adding waits or
     // spills of its own around conditional copies.
+    // Persistent form: thread 0 sends the front claim on its own XCD's counter before the tile's last K
+    // steps (an unconditional add: a claim on an empty or used-up range just gets no block), so its round
+    // trip overlaps them; the tile's end decides from the value it returned. Gate/up sends it at the start
+    // of the last full six-step iteration, down (whose loop has no register to spare) after that loop.
+    long long home_old = -1;
+    auto early_claim = [&]() {
+        if constexpr (PERSIST)
+            if (tid == 0) home_old = (long long)atomicAdd(a.work_ctr + (int)(blockIdx.x % kXcds), kClaimFront);
+    };
     auto step = [&](uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, int s) {
         read(f1a, f1b, wc, xc, 1);
         mma(f0a, f0b);
@@ -614,6 +627,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         // six steps per iteration (weight buffers cycle with period 3, token buffers with 2), then up to five
         int s = 0;
         for (; s + 6 <= nk; s += 6) {
+            if (KIND == GemmKind::GateUp && s + 12 > nk) early_claim();
             step(ws0, xs0, ws1, xs1, s);
             step(ws1, xs1, ws2, xs0, s + 1);
             step(ws2, xs0, ws0, xs1, s + 2);
@@ -621,6 +635,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
             step(ws1, xs0, ws2, xs1, s + 4);
             step(ws2, xs1, ws0, xs0, s + 5);
         }
+        if (KIND != GemmKind::GateUp || nk < 6) early_claim();
         if (s < nk) step(ws0, xs0, ws1, xs1, s);
         if (s + 1 < nk) step(ws1, xs1, ws2, xs0, s + 1);
         if (s + 2 < nk) step(ws2, xs0, ws0, xs1, s + 2);
@@ -683,7 +698,7 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
     auto claim_next = [&]() {
         if constexpr (PERSIST) {
             int claim = -1;
-            if (tid == 0) claim = grab_block(a, ntn, (int)(blockIdx.x % kXcds));
+            if (tid == 0) claim = grab_block(a, ntn, (int)(blockIdx.x % kXcds), home_old);
             if (wave == 0) got = __builtin_amdgcn_readfirstlane(claim);
         }
     };
