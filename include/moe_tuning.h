@@ -42,8 +42,10 @@ typedef enum moe_tune_knob {
     /* Shared expert above the decode sizes, when it has the routed width and no stream of its own: 0 by size
        (one more group of the persistent routed GEMMs), 1 a dense MLP on the main stream before them. */
     MOE_TUNE_SHARED = 5,
-    /* Copy ring of the LDS-copy kernel at up to 32 tokens: 0 by size (three K steps of weights in flight),
-       1 the two-step ring of larger batches. */
+    /* Copy ring of the LDS-copy kernel at up to 32 tokens: 0 by size (three K steps of weights in flight; one
+       workgroup per CU running its blocks back to back where the launch allows it and few blocks per CU are
+       expected, else one workgroup per block), 1 the two-step ring of larger batches, 2 the three-step ring
+       with one workgroup per block, 3 the three-step ring streamed wherever the launch allows it. */
     MOE_TUNE_RING = 6,
     MOE_TUNE_KNOBS = 7 /* number of knobs */
 } moe_tune_knob;

@@ -106,7 +106,7 @@ moe_status device_scratch(void** out) {
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1, 1};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1, 3};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -140,8 +140,20 @@ moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, 
     const bool dma_split = path == moe::GemmPath::Dma && T <= moe::kDmaSplitMaxT && part != nullptr;
     int cus = 0;
     if (dma_split) MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
-    const int s1 = skinny && part ? moe::dense_splits(true, T, I, H) : dma_split ? moe::dma_dense_splits(true, T, I, H, cus) : 1;
-    const int s2 = skinny && part ? moe::dense_splits(false, T, H, I) : dma_split ? moe::dma_dense_splits(false, T, H, I, cus) : 1;
+    // up to 32 rows the deep copy ring: streamed (ring knobs 0 and 3) where the splits of both GEMMs can be
+    // multiples of its 4-step period, else one workgroup per block (knob 2 forces that)
+    const int ring = tuning(MOE_TUNE_RING);
+    const int deep = path == moe::GemmPath::Dma && T <= moe::kDeepRingMaxT && ring != 1 ? (ring == 2 ? 1 : 2) : 0;
+    int s1 = 1, s2 = 1;
+    if (skinny && part) {
+        s1 = moe::dense_splits(true, T, I, H);
+        s2 = moe::dense_splits(false, T, H, I);
+    } else if (dma_split) {
+        const int t1 = deep == 2 ? moe::dma_stream_splits(true, T, I, H, cus) : 0;
+        const int t2 = deep == 2 ? moe::dma_stream_splits(false, T, H, I, cus) : 0;
+        s1 = t1 > 0 ? t1 : moe::dma_dense_splits(true, T, I, H, cus);
+        s2 = t2 > 0 ? t2 : moe::dma_dense_splits(false, T, H, I, cus);
+    }
     moe::GemmArgs g1{};
     g1.act = x;
     g1.w_a = w1;
@@ -153,7 +165,7 @@ moe_status dense_mlp(moe::GemmPath path, const uint16_t* x, const uint16_t* w1, 
     g1.ksplit = s1;
     g1.part = part;
     g1.part_rows = T;
-    g1.deep = path == moe::GemmPath::Dma && T <= moe::kDeepRingMaxT && tuning(MOE_TUNE_RING) == 0 ? 1 : 0;
+    g1.deep = deep;
     const std::string w(what);
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, g1, tiles, s), (w + " gate/up GEMM").c_str());
     if (s1 > 1) MOE_HIP(moe::launch_reduce(moe::GemmKind::GateUp, part, s1, T, I, h, s), (w + " gate/up reduce").c_str());
@@ -336,9 +348,11 @@ moe_status forward_impl(const Request& q) {
     const bool ksplit = path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off;
     int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
     bool ks_gate_up = false; // the gate/up split needs a reduction launch: skipped when it can never pay
+    int cus = 0;
+    MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
+    // experts (with the folded shared expert) a batch of this size is expected to reach
+    const int64_t expect_groups = moe::expected_active(T, E, k) + (grouped_shared ? 1 : 0);
     if (ksplit) {
-        int cus = 0;
-        MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
         split.ksplit = ks_flag;
         split.ks_ntn[0] = moe::dma_ntn(true, I);
         split.ks_ntn[1] = moe::dma_ntn(false, H);
@@ -396,9 +410,17 @@ moe_status forward_impl(const Request& q) {
         r1.part = static_cast<float*>(at(L.ks_part));
         r1.part_rows = h_rows;
     }
-    // decode sizes: one workgroup per block with the deeper copy ring
-    const int deep = path == moe::GemmPath::Dma && !persist && T <= moe::kDeepRingMaxT && tuning(MOE_TUNE_RING) == 0;
-    r1.deep = deep;
+    // decode sizes: the deeper copy ring, streamed (one workgroup per CU, blocks back to back) where the launch
+    // allows it and few blocks per CU are expected, else one workgroup per block (ring knob 2 forces that,
+    // ring knob 3 the streamed form wherever the launch allows it)
+    const int ring = tuning(MOE_TUNE_RING);
+    const bool deep = path == moe::GemmPath::Dma && !persist && T <= moe::kDeepRingMaxT && ring != 1;
+    auto deep_mode = [&](int ntn) {
+        if (!deep) return 0;
+        return ring == 3 || (ring == 0 && moe::decode_streamed(expect_groups * ntn, cus)) ? 2 : 1;
+    };
+    r1.deep = deep_mode(moe::dma_ntn(true, I));
+    r1.rt_rows = T * k;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     if (ks_gate_up)
         MOE_HIP(moe::launch_reduce_ksplit(r1.part, ks_flag, h_rows, I, h_perm, s0), "gate/up K-split reduction");
@@ -426,7 +448,7 @@ moe_status forward_impl(const Request& q) {
     const bool ybf = moe::slot_rows_bf16(T, E, k, I, Is) && !ksplit;
     r2.out_bf16 = ybf ? 1 : 0;
     if (fold_pre) r2.out_shared = y_sh;
-    r2.deep = deep;
+    r2.deep = deep_mode(moe::dma_ntn(false, H));
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 

@@ -81,10 +81,11 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t mtile, Tile
 // both come from HBM about once instead of once per XCD.
 // Block L of the order, decoded from the one entry at L / ntn (a tile of the same chunk): the tiles of a
 // chunk are consecutive tiles of one group, so the block's tile is known without reading its own entry.
+// `e` is the entry at L / ntn.
 template <int BM>
-__device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, TileInfo& ti, int& ntile) {
+__device__ __forceinline__ bool block_from(const GemmArgs& a, int ntn, int64_t L, const int4& e, TileInfo& ti,
+                                           int& ntile) {
     const int64_t at = L / ntn;
-    const int4 e = a.tiles[at];
     if (!entry_ok<BM>(a, e)) return false;
     const int ht = tile_ht(e.x);
     const int64_t t = chunk_major_tile(L, ntn, tile_ci(e.x), tile_cm(e.x), ntile);
@@ -94,6 +95,10 @@ __device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, 
     ti.off = e.w;
     ti.rows = min(ht, e.z - ti.m0);
     return ti.rows > 0;
+}
+template <int BM>
+__device__ __forceinline__ bool block_at(const GemmArgs& a, int ntn, int64_t L, TileInfo& ti, int& ntile) {
+    return block_from<BM>(a, ntn, L, a.tiles[L / ntn], ti, ntile);
 }
 
 // With a K split of S, S consecutive positions of the order are the K ranges of one block (`ks` is the range).
@@ -879,6 +884,269 @@ __global__ __launch_bounds__(kDThreads) void gemm_dma_deep_kernel(GemmArgs a, in
     dma_tile<KIND, DENSE, 1, false, true>(a, ti, ntile, ws0, ws1, ws2, xs0, xs1, 0, ntn, got, ks, S, ws3, xs2, xs3);
 }
 
+// Decode-sized launches streamed: one workgroup per CU runs the blocks blockIdx.x, blockIdx.x + gridDim.x, ...
+// of the one-shot kernel's order back to back with the deep ring, and the copies its last four K steps issue
+// are the next block's first four steps (the one-shot kernel repeats its last step there), so the copy stream
+// of a CU never pauses between blocks: no block starts with an empty ring. Every block has the same number of
+// K steps, a multiple of the ring's period 4 (the host checks), so each block's step s lands in ws[s % 4]
+// as in the one-shot kernel, whose bits each block reproduces. The tile list and the gate/up gather map are
+// staged in LDS first: the next block's tile and its token rows are then read from LDS, never with a vector
+// load that would have to wait behind the copies in flight. Waves 4-7 copy the same 32 token rows as waves
+// 0-3 (a tile has at most 32 rows), which halves the token buffers and makes room for that staging; each
+// wave still issues five copies per step, so the wait counts of the deep ring hold. The epilogue stores
+// straight from the accumulators (every LDS buffer holds copies in flight by then). The loads of a wave
+// return in order, so the stores it issues among its copies only make each wait stricter.
+constexpr int kStreamMaxTiles = 320;  // tile-list entries staged (decode: one tile per group)
+constexpr int kStreamMaxRows = 1024;  // row_token entries staged (T * k at T <= 32, k <= 32)
+
+template <GemmKind KIND, bool DENSE>
+__device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t* ws0, uint16_t* ws1, uint16_t* ws2,
+                                           uint16_t* ws3, uint16_t* xs0, uint16_t* xs1, uint16_t* xs2, uint16_t* xs3,
+                                           int* tl, int* rt) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int rl = lane & 15, kg = lane >> 4;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int lr = lane >> 3, ls = lane & 7;
+    const int K = a.K, N = a.N;
+    const int nk_all = K / kBK;
+
+    int S = 1;
+    int64_t live;
+    if (DENSE) {
+        S = a.ksplit > 1 ? a.ksplit : 1;
+        live = (int64_t)ntn * S; // at most 32 rows: one token tile
+    } else {
+        if (a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+        const int nt = min(a.ntiles[0], kStreamMaxTiles);
+        for (int i = tid; i < nt; i += kDThreads) {
+            const int4 e = a.tiles[i];
+            tl[4 * i] = e.x;
+            tl[4 * i + 1] = e.y;
+            tl[4 * i + 2] = e.z;
+            tl[4 * i + 3] = e.w;
+        }
+        if (KIND == GemmKind::GateUp)
+            for (int i = tid; i < min(a.rt_rows, kStreamMaxRows); i += kDThreads) rt[i] = a.row_token[i];
+        live = (int64_t)nt * ntn * S;
+        __syncthreads();
+    }
+    const int nk = nk_all / S;
+
+    // block v of the one-shot order: its tile, output-column tile and K range
+    auto block_of = [&](int64_t v, TileInfo& ti, int& ntile, int& ks) -> bool {
+        if (DENSE) {
+            if (v >= live) return false;
+            ks = (int)(v / ntn);
+            ntile = (int)(v % ntn);
+            ti.g = 0;
+            ti.m0 = 0;
+            ti.off = 0;
+            ti.rows = min(32, a.dense_rows);
+            ti.shared = false;
+            return ti.rows > 0;
+        }
+        const int64_t L = xcd_block_order(v, live);
+        if (L < 0) return false;
+        ks = (int)(L % S);
+        const int64_t Lb = L / S;
+        const int* e = tl + 4 * (Lb / ntn);
+        return block_from<kDRows>(a, ntn, Lb, make_int4(e[0], e[1], e[2], e[3]), ti, ntile) && ti.rows <= 32;
+    };
+
+    // copy source of a block: weight resources and per-lane offsets as in dma_tile, the token rows of waves
+    // 4-7 those of waves 0-3
+    struct Src {
+        const uint16_t* w0;
+        const uint16_t* w1;
+        uint32_t woff[4];
+        uint32_t xoff;
+        int sb; // first K step of the block's range
+    };
+    auto source = [&](const TileInfo& ti, int ntile, int ks) {
+        Src c;
+        c.w0 = weight_row(a.w_a, a.ws_a, ti, N, 0, K);
+        c.w1 = KIND == GemmKind::GateUp ? weight_row(a.w_b, a.ws_b, ti, N, 0, K) : c.w0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 8 * (wave + 8 * q) + lr;
+            int n = KIND == GemmKind::GateUp ? ntile * 128 + (r & 127) : ntile * 256 + r;
+            n = n < N ? n : N - 1;
+            c.woff[q] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)(ls ^ dswz(r)) * 16u;
+        }
+        const int r = 8 * wm + lr;
+        const int m = r < ti.rows ? r : ti.rows - 1;
+        int row = ti.off + ti.m0 + m;
+        if (KIND == GemmKind::GateUp && !DENSE) row = ti.shared ? ti.m0 + m : rt[row];
+        c.xoff = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(ls ^ dswz(r)) * 16u;
+        c.sb = ks * nk;
+        return c;
+    };
+    auto copy = [&](const Src& c, uint16_t* wl, uint16_t* xl, int st) {
+        const int so = 2 * (c.sb + st) * kBK;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dma_rsrc(a.act), (lptr_t)(xl + 8 * wm * kBK), 16, c.xoff, so, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const __amdgpu_buffer_rsrc_t r0 = dma_rsrc(c.w0), r1 = dma_rsrc(c.w1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(KIND == GemmKind::GateUp && q >= 2 ? r1 : r0,
+                                                     (lptr_t)(wl + 8 * (wave + 8 * q) * kBK), 16, c.woff[q], so,
+                                                     0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto arow = [&](int i) {
+        if (KIND == GemmKind::GateUp) return (i < 2 ? 0 : 128) + 32 * wm + 16 * (i & 1);
+        return 64 * wm + 16 * i;
+    };
+    const int brow = 16 * wn;
+    const int lo0 = rl * kBK + (((2 * kg) ^ dswz(rl)) << 3), lo1 = rl * kBK + (((2 * kg + 1) ^ dswz(rl)) << 3);
+    auto frag = [&](const uint16_t* l, int row0, int h) { return load16(&l[row0 * kBK + (h ? lo1 : lo0)]); };
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Pack16 f0a[4], f0b, f1a[4], f1b;
+    auto read = [&](Pack16 (&fa)[4], Pack16& fb, const uint16_t* wl, const uint16_t* xl, int h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = frag(wl, arow(i), h);
+        fb = frag(xl, brow, h);
+    };
+    auto mma = [&](const Pack16 (&fa)[4], const Pack16& fb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(fa[i], fb, acc[i]);
+    };
+    auto interleave = [&]() { // dma_tile's order at one token block: the five fragment reads, then the MFMAs
+#pragma unroll
+        for (int r = 0; r < 5; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                               // MFMA
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // step s of the ring (buffers wc, xc), as in dma_tile's deep ring; the copy after its barrier refills
+    // them with step `st` of source c
+    constexpr int VD = 2 * 5, VP = 3 * 5;
+    auto dstep = [&](uint16_t* wc, uint16_t* xc, const uint16_t* wn1, const uint16_t* xn1, const Src& c, int st) {
+        read(f1a, f1b, wc, xc, 1);
+        mma(f0a, f0b);
+        interleave();
+        __builtin_amdgcn_s_waitcnt(0x0070 | VD); // vmcnt(10) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        copy(c, wc, xc, st);
+        read(f0a, f0b, wn1, xn1, 0);
+        mma(f1a, f1b);
+        interleave();
+    };
+    // fp32 rows (down) or bf16 h / fp32 partials (gate/up) of a finished block, straight from the accumulators:
+    // lane holds features 4 kg .. 4 kg + 3 of weight block i for token 16 wn + rl
+    auto finish = [&](const TileInfo& ti, int ntile, int ks) {
+        const int m = brow + rl;
+        if (m >= ti.rows) return;
+        const size_t row = (size_t)ti.off + ti.m0 + m;
+        if constexpr (KIND == GemmKind::DownF32) {
+            float* yout = DENSE && S > 1 ? a.part + (size_t)ks * a.part_rows * N
+                                         : (ks == 0 ? static_cast<float*>(a.out) : a.part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = ntile * 256 + 64 * wm + 16 * i + 4 * kg;
+                if (col >= N) continue;
+                if (!DENSE && a.out_bf16) {
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[i][0], acc[i][1]);
+                    v.y = pack_bf16x2(acc[i][2], acc[i][3]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                } else {
+                    *reinterpret_cast<f32x4*>(yout + row * N + col) = acc[i];
+                }
+            }
+        } else {
+            static_assert(KIND == GemmKind::GateUp, "the streamed kernel computes gate/up and fp32 down GEMMs");
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int col = ntile * 128 + 32 * wm + 16 * i + 4 * kg;
+                if (col >= N) continue;
+                if (S > 1) {
+                    float* prow = a.part + (size_t)ks * a.part_rows * 2 * N + row * 2 * N;
+                    *reinterpret_cast<f32x4*>(prow + col) = acc[i];
+                    *reinterpret_cast<f32x4*>(prow + N + col) = acc[i + 2];
+                } else {
+                    const f32x4 g = acc[i], u = acc[i + 2];
+                    uint2 v;
+                    v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+                    v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
+                }
+            }
+        }
+    };
+
+    int64_t v = blockIdx.x;
+    TileInfo ti;
+    int ntile = 0, ks = 0;
+    if (!block_of(v, ti, ntile, ks)) return;
+    Src cur = source(ti, ntile, ks);
+    // the first block's ring: steps 0 to 3 (nk >= 4); the first barrier waits for X0 and W0
+    copy(cur, ws0, xs0, 0);
+    copy(cur, ws1, xs1, 1);
+    copy(cur, ws2, xs2, 2);
+    copy(cur, ws3, xs3, 3);
+    __builtin_amdgcn_s_waitcnt(0x0070 | VP); // vmcnt(15) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    read(f0a, f0b, ws0, xs0, 0);
+    for (;;) {
+        const int64_t vn = v + gridDim.x;
+        TileInfo tn;
+        int ntn2 = 0, ksn = 0;
+        const bool has = block_of(vn, tn, ntn2, ksn);
+        // this block's steps 0 .. nk - 5, copying its steps 4 .. nk - 1
+        for (int s = 0; s + 8 <= nk; s += 4) {
+            dstep(ws0, xs0, ws1, xs1, cur, s + 4);
+            dstep(ws1, xs1, ws2, xs2, cur, s + 5);
+            dstep(ws2, xs2, ws3, xs3, cur, s + 6);
+            dstep(ws3, xs3, ws0, xs0, cur, s + 7);
+        }
+        // its last four steps copy the next block's steps 0 .. 3, or (last block) repeat its own last step
+        Src nxt = cur;
+        int z = nk - 1, dz = 0;
+        if (has) {
+            nxt = source(tn, ntn2, ksn);
+            z = 0;
+            dz = 1;
+        }
+        dstep(ws0, xs0, ws1, xs1, nxt, z);
+        dstep(ws1, xs1, ws2, xs2, nxt, z + dz);
+        dstep(ws2, xs2, ws3, xs3, nxt, z + 2 * dz);
+        dstep(ws3, xs3, ws0, xs0, nxt, z + 3 * dz);
+        // the first-half fragments of the next block's step 0 are in f0a / f0b now
+        finish(ti, ntile, ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!has) break;
+        v = vn;
+        ti = tn;
+        ntile = ntn2;
+        ks = ksn;
+        cur = nxt;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup
+}
+
+template <GemmKind KIND, bool DENSE>
+__global__ __launch_bounds__(kDThreads) void gemm_dma_stream_kernel(GemmArgs a, int ntn) {
+    // 153 KB: four weight buffers of [256][64] bf16, four token buffers of [32][64], the staged tile list and
+    // gather map
+    __shared__ __attribute__((aligned(16))) uint16_t ws0[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws1[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws2[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws3[kDRows * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[32 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[32 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs2[32 * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t xs3[32 * kBK];
+    __shared__ __attribute__((aligned(16))) int tl[4 * kStreamMaxTiles]; // tile-list entries, 4 ints each
+    __shared__ int rt[kStreamMaxRows];
+    dma_stream<KIND, DENSE>(a, ntn, ws0, ws1, ws2, ws3, xs0, xs1, xs2, xs3, tl, rt);
+}
+
 // Persistent form of the grouped DMA GEMM: one workgroup per CU takes blocks from its XCD's counter (then
 // from the other XCDs') until none is left; each tile runs as in the one-shot kernel.
 template <GemmKind KIND>
@@ -1171,6 +1439,28 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
             int64_t g = (int64_t)cus < blocks ? cus : blocks;
             g = (g + kXcds - 1) / kXcds * kXcds;
             gemm_dma_persistent_kernel<KIND><<<dim3((unsigned)g), kDThreads, 0, stream>>>(a, ntn);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (KIND != GemmKind::Logits) {
+        // the streamed deep-ring kernel: the one-shot order, one workgroup per CU (a multiple of kXcds, so each
+        // workgroup's blocks stay on one XCD's range of the order), blocks of a multiple of 4 K steps, the tile
+        // list and gather map within its LDS staging
+        const int nk = a.K / kBK;
+        bool streamed = path == GemmPath::Dma && a.deep == 2 && a.xcd_bounds == nullptr && a.out_shared == nullptr;
+        if (DENSE)
+            streamed = streamed && splits >= 1 && nk % splits == 0 && (nk / splits) % 4 == 0;
+        else
+            streamed = streamed && nk % (a.ksplit_dev != nullptr ? 8 : 4) == 0 && grid_tiles <= kStreamMaxTiles &&
+                     (KIND != GemmKind::GateUp ||
+                      (a.row_token != nullptr && a.rt_rows > 0 && a.rt_rows <= kStreamMaxRows));
+        if (streamed) {
+            int cus = 0;
+            const hipError_t e = cu_count(cus);
+            if (e != hipSuccess) return e;
+            int64_t g = (int64_t)cus < blocks ? cus : blocks;
+            g = (g + kXcds - 1) / kXcds * kXcds;
+            gemm_dma_stream_kernel<KIND, DENSE><<<dim3((unsigned)g), kDThreads, 0, stream>>>(a, ntn);
             return hipGetLastError();
         }
     }

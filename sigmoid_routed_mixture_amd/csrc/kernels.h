@@ -82,8 +82,12 @@ struct GemmArgs {
     int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32
     float* out_shared;         // grouped down GEMM (LDS-copy kernel): fp32 rows [shared_rows, N] of the folded
                                // shared expert, row = its token, or null (its rows then follow the routed ones)
-    int deep;                  // LDS-copy kernel, one workgroup per block: every tile has at most 32 rows, so
-                               // the kernel with the deeper copy ring (three K steps of weights ahead) runs
+    int deep;                  // LDS-copy kernel, not persistent: every tile has at most 32 rows, so the deeper
+                               // copy ring (three K steps of weights ahead) runs: 1 one workgroup per block,
+                               // 2 streamed (one workgroup per CU runs blocks back to back, the next block's
+                               // first copies issued during the last steps of the one before) where the shape
+                               // allows it, else as 1
+    int rt_rows;               // streamed grouped gate/up: entries of row_token (T * k, at most 1024)
 };
 enum class GemmKind { GateUp, DownF32, Logits };
 hipError_t launch_gemm(GemmKind kind, GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream);

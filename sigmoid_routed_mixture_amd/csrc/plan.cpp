@@ -154,6 +154,23 @@ int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus) {
     return best;
 }
 
+int dma_stream_splits(bool gate_up, int rows, int N, int K, int cus) {
+    const int steps = K / 64;
+    if (rows <= 0 || N <= 0 || K <= 0 || cus <= 0 || steps % 4 != 0) return 0;
+    if (rows > kDmaSplitMaxT) return 1;
+    const int64_t B = (((int64_t)rows + kTallBM - 1) / kTallBM) * dma_ntn(gate_up, N);
+    const double part_step = (double)rows * (gate_up ? 2 * N : N) * 8.0 / (32768.0 * cus);
+    int best = 1;
+    double best_t = 0;
+    for (int S = 1; S <= kMaxDenseSplits && S <= steps / 4; ++S) {
+        if ((steps / 4) % S != 0) continue;
+        double t = (double)((B * S + cus - 1) / cus) * (double)(steps / S);
+        if (S > 1) t += S * part_step + 2.0;
+        if (S == 1 || t < best_t) best = S, best_t = t;
+    }
+    return best;
+}
+
 size_t dense_partial_bytes(int T, int H, int Id) {
     const int s1 = dense_splits(true, T, Id, H), s2 = dense_splits(false, T, H, Id);
     size_t a = s1 > 1 ? (size_t)s1 * T * 2 * Id * 4 : 0;

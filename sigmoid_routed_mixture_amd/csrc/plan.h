@@ -209,6 +209,15 @@ constexpr int decode_ksplit(int64_t blocks, int cus) {
     const int64_t r1 = (blocks + cus - 1) / cus, r2 = (2 * blocks + cus - 1) / cus;
     return r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1; // one round already: no split; else 0.525 r2 < r1
 }
+// A decode-sized grouped GEMM runs streamed (one workgroup per CU, its blocks back to back, the next block's
+// first copies in flight during the current one's last steps) when the blocks it is expected to have, with
+// the K split decode_ksplit would choose, come to at most 4 per CU: there the blocks' empty-ring starts
+// weigh most (GLM-4.7-Flash decode, about 2 per CU: 2.8 % faster). With many blocks per CU the one-workgroup-
+// per-block launch balances the tail better than the streamed form's fixed share (GLM-5 decode, 8-13 per
+// CU: 1.1 % slower streamed).
+constexpr bool decode_streamed(int64_t blocks, int cus) {
+    return blocks > 0 && cus > 0 && blocks * decode_ksplit(blocks, cus) <= 4 * (int64_t)cus;
+}
 
 
 struct Layout {
@@ -243,6 +252,13 @@ constexpr int kDmaSplitMaxT = 64;
 // are tokens), and the LDS-copy kernel runs with its deeper copy ring.
 constexpr int kDeepRingMaxT = 32;
 int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus);
+// The same choice for the streamed form of that kernel (one workgroup per CU running its blocks back to back,
+// the next block's first copies in flight during the last steps of the one before): ranges of equal length, a
+// multiple of 4 K steps (the copy ring's period), so S divides (K / 64) / 4. The S that minimises the rounds
+// of blocks times a block's length, ceil(B S / cus) * (K / 64) / S, plus, when S > 1, the partials' round
+// trip ((S rows N' 8) bytes in steps of cus * 32 KB, N' = 2N for gate/up, N for down) and 2 steps for the
+// reduction launch. 0 when K / 64 is not a multiple of 4 (the kernel's one-workgroup-per-block form runs).
+int dma_stream_splits(bool gate_up, int rows, int N, int K, int cus);
 // fp32 partials of a dense SwiGLU MLP (gate/up then down, one region reused) on that kernel; 0 if unsplit.
 size_t dense_partial_bytes(int T, int H, int Id);
 

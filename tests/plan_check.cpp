@@ -234,6 +234,11 @@ int main() {
               moe::decode_ksplit(17, 256) == 1 && moe::decode_ksplit(0, 256) == 1 &&
               moe::decode_ksplit(100, 0) == 1,
           "decode_ksplit");
+    // streamed decode GEMMs: GLM-4.7-Flash decode (42 groups: 504 gate/up, 336 down blocks) yes, GLM-5 decode
+    // (102 groups: 1632 gate/up, 816 down blocks, K split in two) no
+    CHECK(moe::decode_streamed(504, 256) && moe::decode_streamed(336, 256) && !moe::decode_streamed(1632, 256) &&
+              !moe::decode_streamed(816, 256) && !moe::decode_streamed(0, 256) && !moe::decode_streamed(10, 0),
+          "decode_streamed");
     for (int64_t b = 1; b < 5000; b += 7)
         for (int cus : {80, 256, 304}) {
             const int64_t r1 = (b + cus - 1) / cus, r2 = (2 * b + cus - 1) / cus;
@@ -320,10 +325,26 @@ int main() {
                           "dma down splits %d (T=%d H=%d I=%d cus=%d)", d2, T, H, Id, cus);
                     const size_t nd = std::max(d1 > 1 ? (size_t)d1 * T * 2 * Id * 4 : 0, d2 > 1 ? (size_t)d2 * T * H * 4 : 0);
                     CHECK(moe::dense_partial_bytes(T, H, Id) >= nd, "dma partials T=%d H=%d I=%d", T, H, Id);
+                    // the streamed form: ranges of a whole number of ring periods (4 K steps), within the same
+                    // partial region; 0 exactly when K / 64 is not a multiple of 4
+                    const int e1 = moe::dma_stream_splits(true, T, Id, H, cus), e2 = moe::dma_stream_splits(false, T, H, Id, cus);
+                    CHECK((e1 == 0) == ((H / 64) % 4 != 0) && (e2 == 0) == ((Id / 64) % 4 != 0),
+                          "stream splits defined (T=%d H=%d I=%d cus=%d)", T, H, Id, cus);
+                    CHECK(e1 <= moe::kMaxDenseSplits && (e1 <= 1 || ((H / 64) / 4) % e1 == 0) &&
+                              (T <= moe::kDmaSplitMaxT || e1 <= 1),
+                          "stream gate/up splits %d (T=%d H=%d I=%d cus=%d)", e1, T, H, Id, cus);
+                    CHECK(e2 <= moe::kMaxDenseSplits && (e2 <= 1 || ((Id / 64) / 4) % e2 == 0) &&
+                              (T <= moe::kDmaSplitMaxT || e2 <= 1),
+                          "stream down splits %d (T=%d H=%d I=%d cus=%d)", e2, T, H, Id, cus);
+                    const size_t ne = std::max(e1 > 1 ? (size_t)e1 * T * 2 * Id * 4 : 0, e2 > 1 ? (size_t)e2 * T * H * 4 : 0);
+                    CHECK(moe::dense_partial_bytes(T, H, Id) >= ne, "stream partials T=%d H=%d I=%d", T, H, Id);
                 }
                 // GLM-5 dense MLP at 16 tokens on 256 CUs: 96 gate/up blocks in ranges that fill whole rounds
                 CHECK(moe::dma_dense_splits(true, 16, 12288, 6144, 256) >= 5 &&
                           moe::dma_dense_splits(false, 16, 6144, 12288, 256) >= 8, "GLM-5 dense splits");
+                // streamed: 96 gate/up blocks x 8 ranges of 12 steps = 3 per CU; 24 down blocks x 8 of 24 steps
+                CHECK(moe::dma_stream_splits(true, 16, 12288, 6144, 256) == 8 &&
+                          moe::dma_stream_splits(false, 16, 6144, 12288, 256) == 8, "GLM-5 dense stream splits");
                 CHECK(moe::dense_workspace_bytes(T, H, Id) >= (size_t)T * Id * 2 + need, "dense workspace");
                 const moe::Layout L = moe::forward_layout(T, H, 8, 2, Id == 64 ? 128 : 64, Id);
                 CHECK(need == 0 || (L.sh_partial != size_t(-1) && L.x_norm == size_t(-1) &&

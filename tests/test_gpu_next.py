@@ -292,15 +292,19 @@ def test_dense_mlp_parity(moe, name):
 
 @pytest.mark.parametrize("T", [1, 7, 16])
 def test_dense_decode_copy_ring_bitwise(moe, tune, T):
-    # the GLM-5 dense MLP at decode sizes: the K-split LDS-copy GEMMs with the three-step copy ring against
-    # the two-step ring, bit for bit, and against the oracle
+    # the GLM-5 dense MLP at decode sizes: the K-split LDS-copy GEMMs with the three-step copy ring and one
+    # workgroup per block against the two-step ring, bit for bit; the streamed form (its own K splits, so its
+    # own summation order) and both against the oracle
     cfg, h, d = dense_case("glm5_dense_decode")
+    rows = np.arange(T, dtype=np.int32)
+    ref = oracle.dense_mlp(h["x"], h["w1"], h["w3"], h["w2"], rows=rows)
+    s = dense(moe, cfg, d, T=T)
+    compare_out(s, ref, "glm5_dense_decode streamed T=%d" % T)
+    tune(MOE_TUNE_RING=2)
     a = dense(moe, cfg, d, T=T)
     tune(MOE_TUNE_RING=1)
     b = dense(moe, cfg, d, T=T)
     assert np.array_equal(a, b)
-    rows = np.arange(T, dtype=np.int32)
-    ref = oracle.dense_mlp(h["x"], h["w1"], h["w3"], h["w2"], rows=rows)
     compare_out(a, ref, "glm5_dense_decode ring T=%d" % T)
 
 

@@ -210,15 +210,36 @@ def test_prefill_shared_fold_matches_dense_mlp_bitwise(moe, tune, name):
 
 @pytest.mark.parametrize("name,T", [("tiny", 32), ("glm5_decode", 16), ("glm47_decode", 16), ("glm5_decode", 3)])
 def test_decode_copy_ring_does_not_change_results(moe, tune, name, T):
-    # up to 32 tokens the grouped GEMMs copy three K steps ahead; every tile computes what the two-step ring
-    # computes, bit for bit
+    # up to 32 tokens the grouped GEMMs copy three K steps ahead, streamed (one workgroup per CU running its
+    # blocks back to back) where the launch allows it; every tile computes what the two-step ring computes, bit
+    # for bit, and so does the three-step ring with one workgroup per block
     say("[copy ring] %s T=%d" % (name, T))
     cfg, h, d = case(name)
     a = run_forward(moe, cfg, d, T=T)
-    tune(MOE_TUNE_RING=1)
+    for ring in (1, 2, 3):
+        tune(MOE_TUNE_RING=ring)
+        b = run_forward(moe, cfg, d, T=T)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("name,T,ks", [("glm5_decode", 16, 1), ("glm5_decode", 16, 2), ("glm5_decode", 1, 0),
+                                       ("glm47_decode", 16, 1), ("glm47_decode", 16, 2), ("glm47_decode", 5, 0)])
+def test_streamed_decode_gemms(moe, tune, name, T, ks):
+    # the streamed GEMMs with the K split forced off and on (the gate/up halves then go through the reduction,
+    # the down halves through the combine), one token (fewer blocks than CUs) and the batch sizes of decode:
+    # bit for bit what one workgroup per block computes, and within the bar of the oracle
+    say("[streamed] %s T=%d ksplit knob %d" % (name, T, ks))
+    cfg, h, d = case(name)
+    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3)
+    a = run_forward(moe, cfg, d, T=T)
+    tune(MOE_TUNE_RING=2)
     b = run_forward(moe, cfg, d, T=T)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+    ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(T))
+    same, _, _ = compare_routing(a[1], a[2], ref, name)
+    compare_out(a[0][same], ref["out"][same], "%s streamed T=%d" % (name, T))
 
 
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
