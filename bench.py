@@ -135,18 +135,30 @@ def measured_traffic():
         return None
 
 
-def shared_folded(cfg):
-    """The shared expert runs as one more group of the routed GEMMs when it has the routed width and the
-    layer takes the weight-streaming path (at most 16 routed rows per expert on average)."""
-    return cfg.Is > 0 and cfg.Is == cfg.I and cfg.T * cfg.k <= 16 * cfg.E
+def shared_folded(cfg, m=None, two_streams=False):
+    """Whether the shared expert runs as one more group of the routed grouped GEMMs, so that their launches
+    hold its work too. It needs the routed width (Is = I); at decode sizes (at most 16 routed rows per expert
+    on average) it is always folded in; above them when it has no stream of its own and the persistent
+    launches run with the library's default placement (the knobs of moe_tuning.h read through `m`)."""
+    if not (cfg.Is > 0 and cfg.Is == cfg.I):
+        return False
+    if cfg.T * cfg.k <= 16 * cfg.E:
+        return True
+    if two_streams:
+        return False
+    if m is None:
+        return True
+    get = lambda n: m.moe_get_tuning(getattr(m, n))
+    return (get("MOE_TUNE_SHARED") == 0 and get("MOE_TUNE_PERSIST") == 0 and get("MOE_TUNE_XCD_SPLIT") == 0
+            and get("MOE_TUNE_GEMM_PATH") in (0, 3))
 
 
-def gate_up_rows(cfg):
-    return cfg.T * cfg.k + (cfg.T if shared_folded(cfg) else 0)
+def gate_up_rows(cfg, folded):
+    return cfg.T * cfg.k + (cfg.T if folded else 0)
 
 
-def gate_up_flops(cfg):
-    return 4 * gate_up_rows(cfg) * cfg.H * cfg.I
+def gate_up_flops(cfg, folded):
+    return 4 * gate_up_rows(cfg, folded) * cfg.H * cfg.I
 
 
 def layer_bytes(cfg, active):
@@ -156,11 +168,11 @@ def layer_bytes(cfg, active):
             + 2 * cfg.T * cfg.H + 4 * cfg.T * cfg.H + 8 * cfg.T * cfg.k)
 
 
-def gate_up_bytes(cfg, active):
+def gate_up_bytes(cfg, active, folded):
     """Algorithmic bytes of one grouped gate/up launch: W1 and W3 of the active experts (and Ws1, Ws3 when
     the shared expert is folded in), x once, h written."""
-    groups = active + (1 if shared_folded(cfg) else 0)
-    return groups * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * gate_up_rows(cfg) * cfg.I
+    groups = active + (1 if folded else 0)
+    return groups * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * gate_up_rows(cfg, folded) * cfg.I
 
 
 def time_call(fn, steps, warmup):
@@ -437,10 +449,11 @@ def main():
     ms_p, st_p, act_p, host_tp, med_p = results[cfg_p.name]
     ms_d, st_d, act_d, _, med_d = results[cfg_d.name]
     gu_ms = st_p["gate_up"]
-    achieved = gate_up_flops(cfg_p) / (gu_ms * 1e-3) / 1e12
+    fold_p, fold_d = shared_folded(cfg_p, m, two), shared_folded(cfg_d, m, two)
+    achieved = gate_up_flops(cfg_p, fold_p) / (gu_ms * 1e-3) / 1e12
     layer_tflops = cfg_p.flops() / (ms_p * 1e-3) / 1e12
     dec_gbs = layer_bytes(cfg_d, act_d) / (ms_d * 1e-3) / 1e9
-    dec_gu_gbs = gate_up_bytes(cfg_d, act_d) / (st_d["gate_up"] * 1e-3) / 1e9
+    dec_gu_gbs = gate_up_bytes(cfg_d, act_d, fold_d) / (st_d["gate_up"] * 1e-3) / 1e9
 
     line = {
         "metric": METRIC,
@@ -459,10 +472,11 @@ def main():
                    "Is": cfg_p.Is, "scale": cfg_p.scale, "shared_expert_stream": two, "parallelism": "none",
                    "tuning": args.tune},
         "roofline": {"bound": "mfma", "kernel": "gate/up SwiGLU grouped GEMM (routed experts%s)"
-                     % (" + shared expert" if shared_folded(cfg_p) else ""), "achieved": achieved,
+                     % (" + shared expert" if fold_p else ""), "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(), "launch_ms": gu_ms,
-                     "algorithmic_bytes": gate_up_bytes(cfg_p, act_p)},
+                     "algorithmic_bytes": gate_up_bytes(cfg_p, act_p, fold_p),
+                     "algorithmic_flops": gate_up_flops(cfg_p, fold_p)},
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_BF16_TFLOPS, "median_step_ms": med_p,
                   "gbs": layer_bytes(cfg_p, act_p) / (ms_p * 1e-3) / 1e9, "active_experts": act_p,
                   "stages_ms": st_p},

@@ -106,7 +106,7 @@ moe_status device_scratch(void** out) {
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 2, 4, 1, 3};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 3, 4, 1, 3};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -342,22 +342,44 @@ moe_status forward_impl(const Request& q) {
     split.dealt = dealt ? order - 1 : 0;
     split.plain_cap = order == 1 ? moe::kMaxChunkTiles : moe::kPlainChunkTiles;
     split.spread_shared = fold_pre ? 1 : 0;
-    // decode-sized grouped GEMMs: the permutation picks a K split of 1 or 2 for each from the live block count
-    const int ks_knob = tuning(MOE_TUNE_KSPLIT);
-    const bool ks_off = ks_knob == 1, ks_on = ks_knob == 2;
-    const bool ksplit = path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off;
-    int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
-    bool ks_gate_up = false; // the gate/up split needs a reduction launch: skipped when it can never pay
     int cus = 0;
     MOE_HIP(moe::device_cus(cus), "hipDeviceGetAttribute (compute units)");
     // experts (with the folded shared expert) a batch of this size is expected to reach
     const int64_t expect_groups = moe::expected_active(T, E, k) + (grouped_shared ? 1 : 0);
+    // decode sizes: the deeper copy ring, streamed (one workgroup per CU, blocks back to back) where the launch
+    // allows it and few blocks per CU are expected, else one workgroup per block (ring knob 2 forces that,
+    // ring knob 3 the streamed form wherever the launch allows it)
+    const int ring = tuning(MOE_TUNE_RING);
+    const bool deep = path == moe::GemmPath::Dma && !persist && T <= moe::kDeepRingMaxT && ring != 1;
+    auto deep_mode = [&](int ntn) {
+        if (!deep) return 0;
+        return ring == 3 || (ring == 0 && moe::decode_streamed(expect_groups * ntn, cus)) ? 2 : 1;
+    };
+    const int deep_gate_up = deep_mode(moe::dma_ntn(true, I)), deep_down = deep_mode(moe::dma_ntn(false, H));
+    // decode-sized grouped GEMMs: the permutation picks each one's K split from the live block count, gate/up
+    // 1 or 2, down 1 up to down_split_max(T), splits beyond two only into whole ring periods of 4 K steps (so
+    // the streamed kernel can take them, and every copy ring computes the same split)
+    const int ks_knob = tuning(MOE_TUNE_KSPLIT);
+    const bool ks_off = ks_knob == 1, ks_on = ks_knob >= 2;
+    const bool ksplit = path == moe::GemmPath::Dma && L.ks_flag != size_t(-1) && !ks_off;
+    int32_t* ks_flag = ksplit ? static_cast<int32_t*>(at(L.ks_flag)) : nullptr;
+    bool ks_gate_up = false; // the gate/up split needs a reduction launch: skipped when it can never pay
+    int down_allow = 0;
     if (ksplit) {
+        const int nk2 = I / 64;
+        for (int S = 2; S <= moe::down_split_max(T) && S <= nk2; ++S)
+            if (S == 2 || (nk2 % S == 0 && (nk2 / S) % 4 == 0)) down_allow |= 1 << S;
+        // splits beyond two only where the rule would take one at the expected block count (a one-workgroup-
+        // per-block launch is sized for the largest allowed split: its surplus workgroups still cost dispatches)
+        if (ks_knob != 3 && moe::decode_ksplit_n(expect_groups * moe::dma_ntn(false, H), cus, down_allow) <= 2)
+            down_allow &= 1 << 2;
         split.ksplit = ks_flag;
         split.ks_ntn[0] = moe::dma_ntn(true, I);
         split.ks_ntn[1] = moe::dma_ntn(false, H);
+        split.ks_allow[0] = 1 << 2;
+        split.ks_allow[1] = down_allow;
         split.cus = cus;
-        split.ks_force = ks_on ? 2 : 0;
+        split.ks_force = ks_on ? ks_knob : 0;
         // the gate/up split needs a reduction launch: only when the experts the batch is expected to reach
         // would split (the down GEMM's halves are added by the combine, with no launch of their own)
         const int64_t expect = (moe::expected_active(T, E, k) + moe::shared_tiles(T, BM)) * split.ks_ntn[0];
@@ -407,19 +429,11 @@ moe_status forward_impl(const Request& q) {
     const int h_rows = T * k + (grouped_shared ? T : 0);
     if (ks_gate_up) {
         r1.ksplit_dev = ks_flag;
+        r1.ks_allow = 1 << 2;
         r1.part = static_cast<float*>(at(L.ks_part));
         r1.part_rows = h_rows;
     }
-    // decode sizes: the deeper copy ring, streamed (one workgroup per CU, blocks back to back) where the launch
-    // allows it and few blocks per CU are expected, else one workgroup per block (ring knob 2 forces that,
-    // ring knob 3 the streamed form wherever the launch allows it)
-    const int ring = tuning(MOE_TUNE_RING);
-    const bool deep = path == moe::GemmPath::Dma && !persist && T <= moe::kDeepRingMaxT && ring != 1;
-    auto deep_mode = [&](int ntn) {
-        if (!deep) return 0;
-        return ring == 3 || (ring == 0 && moe::decode_streamed(expect_groups * ntn, cus)) ? 2 : 1;
-    };
-    r1.deep = deep_mode(moe::dma_ntn(true, I));
+    r1.deep = deep_gate_up;
     r1.rt_rows = T * k;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::GateUp, path, r1, grid_tiles, s0), "routed gate/up GEMM");
     if (ks_gate_up)
@@ -441,6 +455,7 @@ moe_status forward_impl(const Request& q) {
     float* y2 = ksplit ? static_cast<float*>(at(L.ks_part_down)) : nullptr;
     if (ksplit) {
         r2.ksplit_dev = ks_flag + 1;
+        r2.ks_allow = down_allow;
         r2.part = y2;
         r2.part_rows = h_rows;
     }
@@ -448,14 +463,14 @@ moe_status forward_impl(const Request& q) {
     const bool ybf = moe::slot_rows_bf16(T, E, k, I, Is) && !ksplit;
     r2.out_bf16 = ybf ? 1 : 0;
     if (fold_pre) r2.out_shared = y_sh;
-    r2.deep = deep_mode(moe::dma_ntn(false, H));
+    r2.deep = deep_down;
     MOE_HIP(moe::launch_gemm(moe::GemmKind::DownF32, path, r2, grid_tiles, s0), "routed down GEMM");
     MOE_TRY(mark(5));
 
     if (two_streams) MOE_TRY(order_after(s0, s1, ev->join));
     MOE_HIP(moe::launch_combine(y_perm, ybf, gates, slot_row, y_sh, block ? q.resid : nullptr, T, H, k, q.out,
                                 s0, y2, y2 != nullptr && fold ? y2 + (size_t)T * k * H : nullptr,
-                                ksplit ? ks_flag + 1 : nullptr),
+                                ksplit ? ks_flag + 1 : nullptr, (size_t)h_rows * H),
             "combine");
     MOE_TRY(mark(6));
     return MOE_OK;

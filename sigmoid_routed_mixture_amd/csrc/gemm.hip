@@ -34,6 +34,12 @@ namespace {
 
 constexpr int kBK = 64;
 
+// The K split the permutation chose for a decode-sized grouped launch (1 .. kMaxDownSplits).
+__device__ __forceinline__ int device_split(const int32_t* ksplit) {
+    const int S = ksplit[0];
+    return S < 1 ? 1 : S > kMaxDownSplits ? kMaxDownSplits : S;
+}
+
 struct TileInfo {
     int g, m0, rows, off;
     bool shared; // the folded shared expert (group index == groups)
@@ -716,12 +722,13 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& a, const TileInfo& ti, 
         float* stg = reinterpret_cast<float*>(wave < 4 ? ws0 : ws1) + (wave & 3) * (16 * 68);
         const int c4 = lane & 15, r4 = lane >> 4;
         const int colw = ntile * 256 + 64 * wm;
-        // K split: the second half's rows go to the partial buffer, the combine adds them. A folded shared
-        // expert with rows of its own writes fp32 rows there, indexed by token.
+        // K split: the rows of ranges 2 .. S go to the partial buffers, the combine adds them. A folded
+        // shared expert with rows of its own writes fp32 rows there, indexed by token.
         const bool own = !DENSE && ti.shared && a.out_shared != nullptr;
         float* yout = own ? a.out_shared
                           : DENSE && S > 1 ? a.part + (size_t)ks * a.part_rows * N // every range writes a partial
-                                           : (ks == 0 ? static_cast<float*>(a.out) : a.part);
+                                           : (ks == 0 ? static_cast<float*>(a.out)
+                                                      : a.part + (size_t)(ks - 1) * a.part_rows * N);
         const size_t row0 = own ? (size_t)ti.m0 : (size_t)ti.off + ti.m0;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
@@ -807,7 +814,7 @@ template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_kernel(GemmArgs a, int ntn) {
     int64_t bid = blockIdx.x;
     int ntile, S = 1, ks = 0;
-    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = device_split(a.ksplit_dev);
     if (DENSE && a.ksplit > 1) { // dense, few rows: the grid is the K ranges times the blocks of one range
         S = a.ksplit;
         const int64_t per = (int64_t)((a.dense_rows + kDRows - 1) / kDRows) * ntn;
@@ -855,7 +862,7 @@ template <GemmKind KIND, bool DENSE>
 __global__ __launch_bounds__(kDThreads) void gemm_dma_deep_kernel(GemmArgs a, int ntn) {
     int64_t bid = blockIdx.x;
     int ntile, S = 1, ks = 0;
-    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+    if (!DENSE && KIND != GemmKind::Logits && a.ksplit_dev != nullptr) S = device_split(a.ksplit_dev);
     if (DENSE && a.ksplit > 1) {
         S = a.ksplit;
         const int64_t per = (int64_t)((a.dense_rows + kDRows - 1) / kDRows) * ntn;
@@ -918,7 +925,7 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         S = a.ksplit > 1 ? a.ksplit : 1;
         live = (int64_t)ntn * S; // at most 32 rows: one token tile
     } else {
-        if (a.ksplit_dev != nullptr) S = a.ksplit_dev[0] == 2 ? 2 : 1;
+        if (a.ksplit_dev != nullptr) S = device_split(a.ksplit_dev);
         const int nt = min(a.ntiles[0], kStreamMaxTiles);
         for (int i = tid; i < nt; i += kDThreads) {
             const int4 e = a.tiles[i];
@@ -1044,7 +1051,8 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         const size_t row = (size_t)ti.off + ti.m0 + m;
         if constexpr (KIND == GemmKind::DownF32) {
             float* yout = DENSE && S > 1 ? a.part + (size_t)ks * a.part_rows * N
-                                         : (ks == 0 ? static_cast<float*>(a.out) : a.part);
+                                         : (ks == 0 ? static_cast<float*>(a.out)
+                                                    : a.part + (size_t)(ks - 1) * a.part_rows * N);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int col = ntile * 256 + 64 * wm + 16 * i + 4 * kg;
@@ -1392,6 +1400,13 @@ hipError_t cu_count(int& cus) {
     return hipSuccess;
 }
 
+// Every split S in `allow` (bit S) cuts nk K steps into ranges of a whole number of deep-ring periods.
+bool ring_periods(int nk, int allow) {
+    for (int S = 1; S <= kMaxDownSplits; ++S)
+        if (((allow >> S) & 1) && (nk % S != 0 || (nk / S) % 4 != 0)) return false;
+    return true;
+}
+
 template <GemmKind KIND, bool DENSE>
 hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipStream_t stream) {
     // bf16 output rows: grouped down GEMMs only, whole 64-column chunks, no K split
@@ -1421,9 +1436,15 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
             return hipErrorInvalidValue;
     int64_t blocks = grid_tiles * ntn * splits;
     if (blocks <= 0) return hipSuccess;
+    // the largest K split the permutation may choose (bit S of ks_allow), each range at least one K step
+    int smax = 1;
     if (KIND != GemmKind::Logits && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {
-        if (a.part == nullptr || a.part_rows <= 0 || a.K < 2 * kBK) return hipErrorInvalidValue;
-        blocks *= 2; // room for a K split of 2
+        for (int S = 2; S <= kMaxDownSplits; ++S)
+            if ((a.ks_allow >> S) & 1) smax = S;
+        if ((a.ks_allow >> (kMaxDownSplits + 1)) != 0 || (KIND == GemmKind::GateUp && smax > 2))
+            return hipErrorInvalidValue;
+        if (a.part == nullptr || a.part_rows <= 0 || a.K < smax * kBK) return hipErrorInvalidValue;
+        blocks *= smax; // room for the largest split
     }
     if (wide && !DENSE) blocks = (blocks + kXcds - 1) / kXcds * kXcds;
     if (path == GemmPath::Dma && !DENSE && a.xcd_bounds != nullptr) {
@@ -1451,7 +1472,8 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
         if (DENSE)
             streamed = streamed && splits >= 1 && nk % splits == 0 && (nk / splits) % 4 == 0;
         else
-            streamed = streamed && nk % (a.ksplit_dev != nullptr ? 8 : 4) == 0 && grid_tiles <= kStreamMaxTiles &&
+            streamed = streamed && ring_periods(nk, a.ksplit_dev != nullptr ? a.ks_allow | 2 : 2) &&
+                       grid_tiles <= kStreamMaxTiles &&
                      (KIND != GemmKind::GateUp ||
                       (a.row_token != nullptr && a.rt_rows > 0 && a.rt_rows <= kStreamMaxRows));
         if (streamed) {

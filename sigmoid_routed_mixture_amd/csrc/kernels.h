@@ -37,8 +37,9 @@ struct XcdSplit {
     int32_t* ctr;
     int32_t* ksplit;
     int ks_ntn[2];
+    int ks_allow[2]; // splits each GEMM may take: bit S set for S allowed (1 always is)
     int cus;
-    int ks_force;
+    int ks_force;    // 0 by the rule, 2 split in two, 3 the largest allowed split
     int dealt;
     int plain_cap;
     int spread_shared; // plain order: the shared group's tiles in kXcds chunks spread through the list
@@ -75,9 +76,11 @@ struct GemmArgs {
                                   // form (one workgroup per CU claiming blocks), or null for one block each
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
-    const int32_t* ksplit_dev; // DMA kernel, grouped: the K split (1 or 2) the permutation chose, or null
-    float* part;               // with a split of 2: gate/up fp32 partials [2][part_rows][2N] (g, then u); down:
-                               // the second K half's fp32 rows [part_rows][N] (the first half goes to out)
+    const int32_t* ksplit_dev; // DMA kernel, grouped: the K split S the permutation chose, or null
+    int ks_allow;              // with ksplit_dev: the splits it may hold (bit S set; gate/up at most 2, down
+                               // at most kMaxDownSplits)
+    float* part;               // with a split: gate/up fp32 partials [2][part_rows][2N] (g, then u); down: the
+                               // fp32 rows of K ranges 2 .. S, [S - 1][part_rows][N] (range 1 goes to out)
     int part_rows;
     int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32
     float* out_shared;         // grouped down GEMM (LDS-copy kernel): fp32 rows [shared_rows, N] of the folded
@@ -103,12 +106,13 @@ hipError_t device_cus(int& cus);
 
 // out[t] = sum_j gates[t, j] * y[slot_row[t, j]] (+ y_shared[t]) (+ resid[t]), fp32, slot order, the
 // residual (bf16) added last. The rows of y are bf16 when y_bf16, else fp32; y_shared is fp32. With
-// `ysplit` (a device int) equal to 2 the down GEMM split K: each row of y and y_shared is its first half
-// plus the same row of y2 / y_shared2 (fp32 rows only).
+// `ysplit` (a device int S > 1) the down GEMM split K into S ranges: each row of y and y_shared is its first
+// range plus the same row of y2 + p * part_stride / y_shared2 + p * part_stride for p = 0 .. S - 2, added
+// in that order (fp32 rows only).
 hipError_t launch_combine(const void* y, bool y_bf16, const float* gates, const int32_t* slot_row,
                           const float* y_shared, const uint16_t* resid, int T, int H, int k, float* out,
                           hipStream_t stream, const float* y2 = nullptr, const float* y_shared2 = nullptr,
-                          const int32_t* ysplit = nullptr);
+                          const int32_t* ysplit = nullptr, size_t part_stride = 0);
 
 // out[t] = bf16(gamma * x[t] / sqrt(mean(x[t]^2) + eps)), computed in fp64.
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps, int T, int H, uint16_t* out,

@@ -45,21 +45,26 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
     }
 }
 
-// Exclusive prefix sum over the 256 threads of a workgroup.
+// Exclusive prefix sum over the 256 threads of a workgroup: an inclusive scan within each wave by lane
+// shuffles, the four wave totals through LDS (sh[0..3]), two barriers in all (the second lets the caller
+// reuse sh at once).
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int a = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += a;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
     }
-    const int incl = sh[tid];
-    *total = sh[255];
+    if (lane == 63) sh[w] = x;
     __syncthreads();
-    return incl - v;
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        if (i < w) before += sh[i];
+    *total = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return before + x - v;
 }
 
 // Writes tiles [f0, f0 + cnt) of group g (n rows, tiles of height ht, its rows from `off` on in the permuted
@@ -181,12 +186,22 @@ __device__ int write_dealt_tiles(const XcdSplit& sp, int4* __restrict__ tiles, i
     return total;
 }
 
-// The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0).
+// The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0): by decode_ksplit_n among each
+// GEMM's allowed splits, or forced: ks_force 2 splits in two where that is allowed, 3 takes the largest
+// allowed split.
 __device__ __forceinline__ void write_ksplit(const XcdSplit& sp, int all_tiles) {
     if (sp.ksplit != nullptr && threadIdx.x == 0)
-        for (int i = 0; i < 2; ++i)
-            sp.ksplit[i] =
-                sp.ks_force > 0 ? sp.ks_force : decode_ksplit((int64_t)all_tiles * sp.ks_ntn[i], sp.cus);
+        for (int i = 0; i < 2; ++i) {
+            const int allow = sp.ks_allow[i] | 2;
+            int S = decode_ksplit_n((int64_t)all_tiles * sp.ks_ntn[i], sp.cus, allow);
+            if (sp.ks_force > 0) {
+                const int cap = sp.ks_force == 2 ? 2 : kMaxDownSplits;
+                S = 1;
+                for (int v = 2; v <= cap; ++v)
+                    if ((allow >> v) & 1) S = v;
+            }
+            sp.ksplit[i] = S;
+        }
 }
 
 // The work-balanced XCD split (plan.h) of the tile list just built, for both column-tile counts. Thread e

@@ -204,11 +204,30 @@ constexpr int kKSplitMaxT = 64;
 // E (1 - (1 - 1/E)^(T k))), rounded up. The gate/up GEMM gets room for a K split (and its reduction launch)
 // only when decode_ksplit of that many experts' blocks (plus the folded shared expert's) would split.
 int expected_active(int T, int E, int k);
-constexpr int decode_ksplit(int64_t blocks, int cus) {
+// The down GEMM may cut K into more ranges at the smallest batches: up to kMaxDownSplits up to
+// kDownSplit4MaxT tokens, 2 above (ranges 2 .. S write fp32 rows of their own, (S - 1) x rows x H x 4 bytes
+// of workspace, which the combine adds in range order).
+constexpr int kMaxDownSplits = 4;
+constexpr int kDownSplit4MaxT = 16;
+constexpr int down_split_max(int T) { return T <= kDownSplit4MaxT ? kMaxDownSplits : 2; }
+// The split S among `allow` (bit S set for each allowed S, 1 <= S <= kMaxDownSplits; 1 is always allowed)
+// with the fewest rounds per unit of work, ceil(S b / cus) / S, each extra range counted 5 % dearer (its
+// prologue and fp32 rows): S minimises ceil(S b / cus) (19 + S) / S. One round already: no split.
+constexpr int decode_ksplit_n(int64_t blocks, int cus, int allow) {
     if (blocks <= 0 || cus <= 0) return 1;
-    const int64_t r1 = (blocks + cus - 1) / cus, r2 = (2 * blocks + cus - 1) / cus;
-    return r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1; // one round already: no split; else 0.525 r2 < r1
+    const int64_t r1 = (blocks + cus - 1) / cus;
+    if (r1 < 2) return 1;
+    int best = 1;
+    int64_t best_r = r1;
+    for (int S = 2; S <= kMaxDownSplits; ++S) {
+        if (!((allow >> S) & 1)) continue;
+        const int64_t r = (S * blocks + cus - 1) / cus;
+        if (r * (19 + S) * best < best_r * (19 + best) * S) best = S, best_r = r;
+    }
+    return best;
 }
+// The gate/up GEMM's rule: a split of 1 or 2 (two half-length blocks pay when 0.525 r2 < r1).
+constexpr int decode_ksplit(int64_t blocks, int cus) { return decode_ksplit_n(blocks, cus, 1 << 2); }
 // A decode-sized grouped GEMM runs streamed (one workgroup per CU, its blocks back to back, the next block's
 // first copies in flight during the current one's last steps) when the blocks it is expected to have, with
 // the K split decode_ksplit would choose, come to at most 4 per CU: there the blocks' empty-ring starts
@@ -228,8 +247,8 @@ struct Layout {
 };
 // with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.
 // ks_flag / ks_part / ks_part_down: the device's K-split choices (gate/up, down: two ints), the gate/up
-// partials [2][T·k + T][2I] fp32 and the down GEMM's second-half rows [T·k + T][H] fp32 of a decode-sized
-// launch (ksplit_possible), else not present.
+// partials [2][T·k + T][2I] fp32 and the rows of the down GEMM's ranges 2 .. S, [down_split_max(T) - 1]
+// [T·k + T][H] fp32, of a decode-sized launch (ksplit_possible), else not present.
 Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm = false);
 constexpr bool ksplit_possible(int T, int H, int E, int k, int I, int Is) {
     return shared_fold(T, E, k, I, Is) && T <= kKSplitMaxT && H >= 128 && I >= 128; // a K step per half

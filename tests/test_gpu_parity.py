@@ -130,10 +130,11 @@ def test_forward_parity(moe, name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "glm5_decode", "glm47_decode"])
-@pytest.mark.parametrize("ks", ["1", "2"])
+@pytest.mark.parametrize("ks", ["1", "2", "3"])
 def test_decode_k_split(moe, tune, name, ks):
-    # decode-sized grouped GEMMs (gate/up with its reduction, down with the combine adding the halves) with
-    # the K split forced off and on, against the oracle on every token
+    # decode-sized grouped GEMMs (gate/up with its reduction, down with the combine adding the ranges) with
+    # the K split forced off, in two, and to the largest split allowed (down: up to four ranges at these
+    # batch sizes), against the oracle on every token
     say("[K split %s] %s" % (ks, name))
     tune(MOE_TUNE_KSPLIT=int(ks))
     cfg, h, d = case(name)
@@ -223,8 +224,9 @@ def test_decode_copy_ring_does_not_change_results(moe, tune, name, T):
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("name,T,ks", [("glm5_decode", 16, 1), ("glm5_decode", 16, 2), ("glm5_decode", 1, 0),
-                                       ("glm47_decode", 16, 1), ("glm47_decode", 16, 2), ("glm47_decode", 5, 0)])
+@pytest.mark.parametrize("name,T,ks", [("glm5_decode", 16, 1), ("glm5_decode", 16, 2), ("glm5_decode", 16, 3),
+                                       ("glm5_decode", 1, 0), ("glm47_decode", 16, 1), ("glm47_decode", 16, 2),
+                                       ("glm47_decode", 16, 3), ("glm47_decode", 5, 0)])
 def test_streamed_decode_gemms(moe, tune, name, T, ks):
     # the streamed GEMMs with the K split forced off and on (the gate/up halves then go through the reduction,
     # the down halves through the combine), one token (fewer blocks than CUs) and the batch sizes of decode:
