@@ -273,10 +273,11 @@ constexpr int kDeepRingMaxT = 32;
 int dma_dense_splits(bool gate_up, int rows, int N, int K, int cus);
 // The same choice for the streamed form of that kernel (one workgroup per CU running its blocks back to back,
 // the next block's first copies in flight during the last steps of the one before): ranges of equal length, a
-// multiple of 4 K steps (the copy ring's period), so S divides (K / 64) / 4. The S that minimises the rounds
-// of blocks times a block's length, ceil(B S / cus) * (K / 64) / S, plus, when S > 1, the partials' round
-// trip ((S rows N' 8) bytes in steps of cus * 32 KB, N' = 2N for gate/up, N for down) and 2 steps for the
-// reduction launch. 0 when K / 64 is not a multiple of 4 (the kernel's one-workgroup-per-block form runs).
+// multiple of 4 K steps (the copy ring's period), so S divides (K / 64) / 4. The smallest S whose B S blocks
+// make one round filling at least three quarters of the CUs; failing that, the S that minimises the rounds of
+// blocks times a block's length, ceil(B S / cus) * (K / 64) / S, plus, when S > 1, the partials' round trip
+// ((S rows N' 8) bytes in steps of cus * 32 KB, N' = 2N for gate/up, N for down) and 2 steps for the reduction
+// launch. 0 when K / 64 is not a multiple of 4 (the kernel's one-workgroup-per-block form runs).
 int dma_stream_splits(bool gate_up, int rows, int N, int K, int cus);
 // fp32 partials of a dense SwiGLU MLP (gate/up then down, one region reused) on that kernel; 0 if unsplit.
 size_t dense_partial_bytes(int T, int H, int Id);

@@ -365,8 +365,9 @@ int main() {
                 // GLM-5 dense MLP at 16 tokens on 256 CUs: 96 gate/up blocks in ranges that fill whole rounds
                 CHECK(moe::dma_dense_splits(true, 16, 12288, 6144, 256) >= 5 &&
                           moe::dma_dense_splits(false, 16, 6144, 12288, 256) >= 8, "GLM-5 dense splits");
-                // streamed: 96 gate/up blocks x 8 ranges of 12 steps = 3 per CU; 24 down blocks x 8 of 24 steps
-                CHECK(moe::dma_stream_splits(true, 16, 12288, 6144, 256) == 8 &&
+                // streamed: one round filling three quarters of the CUs: 96 gate/up blocks x 2 ranges of 48 steps,
+                // 24 down blocks x 8 ranges of 24 steps (192 blocks each)
+                CHECK(moe::dma_stream_splits(true, 16, 12288, 6144, 256) == 2 &&
                           moe::dma_stream_splits(false, 16, 6144, 12288, 256) == 8, "GLM-5 dense stream splits");
                 CHECK(moe::dense_workspace_bytes(T, H, Id) >= (size_t)T * Id * 2 + need, "dense workspace");
                 const moe::Layout L = moe::forward_layout(T, H, 8, 2, Id == 64 ? 128 : 64, Id);
