@@ -371,7 +371,7 @@ moe_status forward_impl(const Request& q) {
             if (S == 2 || (nk2 % S == 0 && (nk2 / S) % 4 == 0)) down_allow |= 1 << S;
         // splits beyond two only where the rule would take one at the expected block count (a one-workgroup-
         // per-block launch is sized for the largest allowed split: its surplus workgroups still cost dispatches)
-        if (ks_knob != 3 && moe::decode_ksplit_n(expect_groups * moe::dma_ntn(false, H), cus, down_allow) <= 2)
+        if (ks_knob != 3 && moe::decode_ksplit_down(expect_groups * moe::dma_ntn(false, H), cus, down_allow) <= 2)
             down_allow &= 1 << 2;
         split.ksplit = ks_flag;
         split.ks_ntn[0] = moe::dma_ntn(true, I);

@@ -25,8 +25,9 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
 // at most cap[i] blocks). With `ctr` (8-byte aligned) it zeroes the 2 * kXcds 64-bit work counters of the
 // persistent DMA kernel (kXcds for each GEMM).
-// With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit of the live
-// blocks, ks_ntn[i] column tiles each, on `cus` compute units; ks_force > 0 forces that split).
+// With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit and
+// decode_ksplit_down of the live blocks, ks_ntn[i] column tiles each, on `cus` compute units, among the splits
+// ks_allow[i] allows; ks_force > 0 forces one).
 // With `dealt` (and `bounds`) the tile list takes a dealt order of plan.h (DealtOrder) and `bounds` the exact
 // XCD ranges of that order for both GEMMs (when the chunks fit kMaxDealtChunks; else the plain order and
 // split). The plain order cuts groups into chunks of at most plain_cap tiles.

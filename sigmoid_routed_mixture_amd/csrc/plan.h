@@ -210,24 +210,33 @@ int expected_active(int T, int E, int k);
 constexpr int kMaxDownSplits = 4;
 constexpr int kDownSplit4MaxT = 16;
 constexpr int down_split_max(int T) { return T <= kDownSplit4MaxT ? kMaxDownSplits : 2; }
-// The split S among `allow` (bit S set for each allowed S, 1 <= S <= kMaxDownSplits; 1 is always allowed)
-// with the fewest rounds per unit of work, ceil(S b / cus) / S, each extra range counted 5 % dearer (its
-// prologue and fp32 rows): S minimises ceil(S b / cus) (19 + S) / S. One round already: no split.
-constexpr int decode_ksplit_n(int64_t blocks, int cus, int allow) {
+// The gate/up GEMM's split: 1 or 2. From two rounds on, two half-length blocks per block pay when they round
+// better, counting about 5 % for the extra prologues and the partials: 0.525 r2 < r1 (r_S the rounds of S b
+// blocks on cus CUs).
+constexpr int decode_ksplit(int64_t blocks, int cus) {
+    if (blocks <= 0 || cus <= 0) return 1;
+    const int64_t r1 = (blocks + cus - 1) / cus, r2 = (2 * blocks + cus - 1) / cus;
+    return r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1;
+}
+// The down GEMM's split among `allow` (bit S set for each allowed S, 2 <= S <= kMaxDownSplits): the fewest
+// rounds per unit of work, r_S / S, with each range beyond two counted 5 % dearer (r_S (18 + S) / (20 S));
+// two ranges are taken already when they round as well as one (its second range costs no launch: the
+// combine adds it; GLM-5 decode, 1968 blocks: 1.0735 ms whole, 1.0678 ms in two, 1.1083 ms in four). One
+// round already: no split.
+constexpr int decode_ksplit_down(int64_t blocks, int cus, int allow) {
     if (blocks <= 0 || cus <= 0) return 1;
     const int64_t r1 = (blocks + cus - 1) / cus;
     if (r1 < 2) return 1;
     int best = 1;
-    int64_t best_r = r1;
+    int64_t num = r1, den = 1; // cost of the best split so far, num / den
     for (int S = 2; S <= kMaxDownSplits; ++S) {
         if (!((allow >> S) & 1)) continue;
         const int64_t r = (S * blocks + cus - 1) / cus;
-        if (r * (19 + S) * best < best_r * (19 + best) * S) best = S, best_r = r;
+        const int64_t n = r * (18 + S), d = 20 * (int64_t)S; // r (18 + S) / (20 S)
+        if (S == 2 ? n * den <= num * d : n * den < num * d) best = S, num = n, den = d;
     }
     return best;
 }
-// The gate/up GEMM's rule: a split of 1 or 2 (two half-length blocks pay when 0.525 r2 < r1).
-constexpr int decode_ksplit(int64_t blocks, int cus) { return decode_ksplit_n(blocks, cus, 1 << 2); }
 // A decode-sized grouped GEMM runs streamed (one workgroup per CU, its blocks back to back, the next block's
 // first copies in flight during the current one's last steps) when the blocks it is expected to have, with
 // the K split decode_ksplit would choose, come to at most 4 per CU: there the blocks' empty-ring starts

@@ -235,27 +235,28 @@ int main() {
               moe::decode_ksplit(17, 256) == 1 && moe::decode_ksplit(0, 256) == 1 &&
               moe::decode_ksplit(100, 0) == 1,
           "decode_ksplit");
-    // the general rule: among the allowed splits, the fewest rounds per unit of work (5 % per extra range);
-    // with {1, 2} exactly the two-way rule 0.525 r2 < r1
+    // the down GEMM's rule: among the allowed splits the fewest rounds per unit of work, two ranges already at
+    // a tie with one, each range beyond two 5 % dearer
     for (int64_t b = 0; b < 5000; b += 7)
         for (int cus : {80, 256, 304}) {
-            const int64_t r1 = (b + cus - 1) / cus, r2 = (2 * b + cus - 1) / cus;
-            const int old = b > 0 && r1 >= 2 && 21 * r2 < 40 * r1 ? 2 : 1;
-            CHECK(moe::decode_ksplit(b, cus) == old, "decode_ksplit two-way b=%lld cus=%d", (long long)b, cus);
-            const int s = moe::decode_ksplit_n(b, cus, (1 << 2) | (1 << 3) | (1 << 4));
-            CHECK(s >= 1 && s <= moe::kMaxDownSplits, "decode_ksplit_n range");
-            if (s > 1) { // no allowed split is better, and it beats no split
+            const int64_t r1 = (b + cus - 1) / cus;
+            const int s = moe::decode_ksplit_down(b, cus, (1 << 2) | (1 << 3) | (1 << 4));
+            CHECK(s >= 1 && s <= moe::kMaxDownSplits, "decode_ksplit_down range");
+            CHECK(r1 >= 2 || s == 1, "decode_ksplit_down splits one round b=%lld", (long long)b);
+            if (s > 1) { // no worse than one range
                 const int64_t rs = (s * b + cus - 1) / cus;
-                CHECK(rs * (19 + s) < r1 * 20 * s, "decode_ksplit_n beats one range b=%lld", (long long)b);
+                CHECK(rs * (18 + s) <= r1 * 20 * s, "decode_ksplit_down beats one range b=%lld", (long long)b);
             }
-            CHECK(moe::decode_ksplit_n(b, cus, 0) == 1, "decode_ksplit_n without splits");
+            CHECK(moe::decode_ksplit_down(b, cus, 0) == 1, "decode_ksplit_down without splits");
+            CHECK(moe::decode_ksplit_down(b, cus, 1 << 2) == (r1 >= 2 && (2 * b + cus - 1) / cus <= 2 * r1 ? 2 : 1),
+                  "decode_ksplit_down two-way b=%lld", (long long)b);
         }
     // GLM-4.7-Flash decode's down GEMM (296 blocks): 3 ranges when 2 and 3 are allowed (the streamed kernel's
-    // whole ring periods of 24 K steps), 4 with 4 allowed; GLM-5 decode's (1968 blocks) stays whole
-    CHECK(moe::decode_ksplit_n(296, 256, (1 << 2) | (1 << 3)) == 3 &&
-              moe::decode_ksplit_n(296, 256, (1 << 2) | (1 << 3) | (1 << 4)) == 4 &&
-              moe::decode_ksplit_n(1968, 256, (1 << 2) | (1 << 3) | (1 << 4)) == 1,
-          "decode_ksplit_n GLM shapes");
+    // whole ring periods of 24 K steps), 4 with 4 allowed; GLM-5 decode's (1968 blocks) in two
+    CHECK(moe::decode_ksplit_down(296, 256, (1 << 2) | (1 << 3)) == 3 &&
+              moe::decode_ksplit_down(296, 256, (1 << 2) | (1 << 3) | (1 << 4)) == 4 &&
+              moe::decode_ksplit_down(1968, 256, (1 << 2) | (1 << 3) | (1 << 4)) == 2,
+          "decode_ksplit_down GLM shapes");
     CHECK(moe::down_split_max(16) == moe::kMaxDownSplits && moe::down_split_max(17) == 2, "down_split_max");
     // streamed decode GEMMs: GLM-4.7-Flash decode (42 groups: 504 gate/up, 336 down blocks) yes, GLM-5 decode
     // (102 groups: 1632 gate/up, 816 down blocks, K split in two) no
