@@ -332,6 +332,38 @@ def test_edge_shapes(moe, tune, shape, path):
     compare_out(out[same], ref["out"][same], what)
 
 
+STREAM_EDGE = [
+    # T, H, E, k, I, what: decode-sized shapes whose K steps make whole ring periods (the streamed GEMMs run)
+    (29, 1024, 24, 3, 512, "29 tokens, E 24, k 3"),
+    (7, 512, 72, 2, 1024, "7 tokens, E 72, k 2"),
+    (32, 1024, 40, 5, 512, "32 tokens, E 40, k 5"),
+]
+
+
+@pytest.mark.parametrize("ks", [0, 3])
+@pytest.mark.parametrize("shape", STREAM_EDGE, ids=[e[-1] for e in STREAM_EDGE])
+def test_streamed_edge_shapes(moe, tune, shape, ks):
+    # the streamed decode GEMMs away from the GLM shapes (tiles of every height up to 32 rows, the folded shared
+    # expert, the K split by size and the largest one): bit for bit the one-workgroup-per-block kernel, and
+    # within the bar of the oracle
+    T, H, E, k, I, what = shape
+    say("[streamed edge] %s ksplit knob %d" % (what, ks))
+    cfg = wl.MoEConfig(52, "stream_edge", T=T, H=H, E=E, k=k, I=I, Is=I, scale=2.5)
+    h = config_host(cfg)
+    d = to_device(h)
+    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3)
+    a = run_forward(moe, cfg, d)
+    tune(MOE_TUNE_RING=2)
+    b = run_forward(moe, cfg, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    out, ids, gates, counts = a
+    ref = oracle_forward_rows(h, k, cfg.scale, np.arange(T))
+    same, _, _ = compare_routing(ids, gates, ref, what)
+    assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    compare_out(out[same], ref["out"][same], what)
+
+
 @pytest.mark.parametrize("path", ["wide", "tall", "dma", "skinny"])
 def test_identical_tokens_one_giant_group(moe, tune, path):
     say("[giant group %s]" % path)
