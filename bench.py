@@ -175,13 +175,20 @@ def gate_up_bytes(cfg, active, folded):
     return groups * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * gate_up_rows(cfg, folded) * cfg.I
 
 
-def time_call(fn, steps, warmup):
-    """Mean ms of fn() over `steps` calls after `warmup`, HIP events on the current stream."""
+def time_call(fn, steps, warmup, min_warm_s=0.2):
+    """Mean ms of fn() over `steps` calls after `warmup` untimed calls, and at least `min_warm_s` seconds of
+    them (a workload timed right after the host generated its weights finds the GPU's clocks idle: a few
+    warmup calls of a 0.1 ms decode pass do not bring them up), HIP events on the current stream."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record()
     for _ in range(steps):
@@ -298,6 +305,33 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
         res[name] = r
         log("%s: %s" % (name, r))
         del w
+    torch.cuda.empty_cache()
+
+    # One GPU's share of the two multi-GPU layouts of the GLM-5 layer (nothing here uses a second GPU):
+    # expert parallelism over 8 GPUs at prefill, where a GPU holds 32 experts and receives the slots routed to
+    # them from 8 batches of 8192 tokens (65,536 rows, here uniformly spread: one slot per row, gate 1, through
+    # the routed entry point; the shared expert runs data-parallel elsewhere), and expert tensor parallelism
+    # over 8 GPUs at decode, where every GPU holds all 256 experts with I / 8 = 256 (the whole layer at that
+    # width, router included).
+    ep = wl.MoEConfig(60, "ep8_prefill_share", T=65536, H=6144, E=32, k=1, I=2048, Is=0, scale=1.0)
+    w = {n: to_dev_bf16(wl.weight(ep, n), device) for n in ("w1", "w3", "w2")}
+    x = to_dev_bf16(wl.tokens(ep), device)
+    ids = torch.from_numpy(np.random.default_rng(ep.seed).integers(0, ep.E, size=(ep.T, 1), dtype=np.int32)).to(device)
+    gates = torch.ones(ep.T, 1, dtype=torch.float32, device=device)
+    out = torch.empty(ep.T, ep.H, dtype=torch.float32, device=device)
+    ws = torch.empty(m.moe_workspace_bytes(ep.T, ep.H, ep.E, ep.k, ep.I, 0), dtype=torch.uint8, device=device)
+    ms = time_call(lambda: m.moe_forward_routed(x, ids, gates, w["w1"], w["w3"], w["w2"], None, None, None, out, ws),
+                   steps, warmup)
+    tf = 6 * ep.T * ep.k * ep.H * ep.I / (ms * 1e-3) / 1e12
+    res[ep.name] = {"rows": ep.T, "E": ep.E, "ms": ms, "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+    log("%s: %s" % (ep.name, res[ep.name]))
+    del w, x, out, ws
+    torch.cuda.empty_cache()
+    tp = wl.MoEConfig(61, "tp8_decode_share", T=16, H=6144, E=256, k=8, I=256, Is=256, scale=2.5)
+    w = {n: to_dev_bf16(wl.weight(tp, n), device) for n in WEIGHT_NAMES}
+    res[tp.name], _, _ = mixture(tp, layer_inputs(tp, w), decode_steps)
+    log("%s: %s" % (tp.name, res[tp.name]))
+    del w
     torch.cuda.empty_cache()
     return res
 
@@ -490,8 +524,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_next:
-        line["next"] = bench_next(m, wl, dev_w, host_w, device, max(3, args.steps // 2),
-                                  max(10, args.decode_steps // 4), args.warmup)
+        line["next"] = bench_next(m, wl, dev_w, host_w, device, max(3, args.steps // 2), args.decode_steps,
+                                  args.warmup)
     if not args.no_cpu_baseline:
         host = dict(host_tp)
         host.update(host_w)
