@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const Y* __restrict__ y, c
         g[tid] = gates[(size_t)t * k + tid];
         rr[tid] = slot_row[(size_t)t * k + tid];
     }
-    const int chunks = H / 8, stride = 256 * gridDim.y;
-    int c = blockIdx.y * 256 + tid;
+    const int chunks = H / 8, stride = (int)blockDim.x * gridDim.y;
+    int c = blockIdx.y * (int)blockDim.x + tid;
     // shared-expert row (each range's with a split) and residual of chunk c
     float4 sa[kMaxDownSplits], sb[kMaxDownSplits];
     Pack16 res{};
@@ -139,12 +139,16 @@ hipError_t launch_combine(const void* y, bool y_bf16, const float* gates, const 
         return hipErrorInvalidValue;
     if (T <= 0) return hipSuccess;
     // few tokens: spread each token's row over several workgroups so every thread has one chunk
-    const int ycols = T < 1024 ? (H / 8 + 255) / 256 : 1;
+    // few tokens: one-wave workgroups spread each token's row over many CUs, every thread one chunk (the
+    // slot loads of a token then come from as many CUs as the row has 512-column pieces); many tokens: a
+    // workgroup of 256 threads per token
+    const int threads = T < 1024 ? 64 : 256;
+    const int ycols = T < 1024 ? (H / 8 + threads - 1) / threads : 1;
     if (y_bf16)
-        combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(static_cast<const uint16_t*>(y), gates, slot_row, y_shared,
+        combine_kernel<<<dim3(T, ycols), threads, 0, stream>>>(static_cast<const uint16_t*>(y), gates, slot_row, y_shared,
                                                           resid, T, H, k, out, y2, y_shared2, ysplit, part_stride);
     else
-        combine_kernel<<<dim3(T, ycols), 256, 0, stream>>>(static_cast<const float*>(y), gates, slot_row, y_shared,
+        combine_kernel<<<dim3(T, ycols), threads, 0, stream>>>(static_cast<const float*>(y), gates, slot_row, y_shared,
                                                           resid, T, H, k, out, y2, y_shared2, ysplit, part_stride);
     return hipGetLastError();
 }
