@@ -5,7 +5,7 @@
 // per-expert offsets (an LDS prefix sum) and per-chunk bases, and lists the grouped-GEMM tiles (plan.h's
 // tile words, in the plain or the dealt order).
 // Pages: the routed experts receive (hidden, indices, weights) (nnterp encyclopedia glm_moe_dsa, support():
-// expert_indices and expert_weights are the experts' inputs); grouping rows by expert is how this build
+// expert_indices and expert_weights are the experts' inputs); grouping rows by expert is how this library
 // hands each expert its tokens.
 #include "common.h"
 #include "kernels.h"
