@@ -332,6 +332,31 @@ def test_edge_shapes(moe, tune, shape, path):
     compare_out(out[same], ref["out"][same], what)
 
 
+SMALL_ROUTER = [
+    # T, H, E, k: decode-sized router shapes of moe_forward (K-split logits of few experts, then the top-k)
+    (1, 64, 1, 1),      # one expert, one K range
+    (5, 2048, 24, 3),   # E not a multiple of 16
+    (16, 6144, 64, 8),  # the longest K ranges
+    (16, 2048, 64, 4),  # the GLM-4.7-Flash decode shape
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_ROUTER, ids=["T%d_H%d_E%d_k%d" % s for s in SMALL_ROUTER])
+def test_small_router_shapes(moe, shape):
+    # ids and gates of moe_forward at decode sizes against the oracle (exact apart from counted near-ties), and
+    # the layer's outputs within the bar
+    T, H, E, k = shape
+    say("[small router] T=%d H=%d E=%d k=%d" % shape)
+    cfg = wl.MoEConfig(53, "small_router", T=T, H=H, E=E, k=k, I=64, Is=64, scale=1.8)
+    h = config_host(cfg)
+    d = to_device(h)
+    out, ids, gates, counts = run_forward(moe, cfg, d)
+    ref = oracle_forward_rows(h, k, cfg.scale, np.arange(T))
+    same, _, _ = compare_routing(ids, gates, ref, "small router")
+    assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    compare_out(out[same], ref["out"][same], "small router")
+
+
 STREAM_EDGE = [
     # T, H, E, k, I, what: decode-sized shapes whose K steps make whole ring periods (the streamed GEMMs run)
     (29, 1024, 24, 3, 512, "29 tokens, E 24, k 3"),
