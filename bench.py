@@ -364,6 +364,42 @@ def profile_workload(m, wl, name, args, device):
     log("%s: %.4f ms/step, stages %s, active experts %d" % (name, ms, stages, active))
 
 
+ROUTINGS = ("one_tile", "two_tiles", "workload")
+
+
+def profile_routing(m, wl, kind, args, device):
+    """The GLM-5 prefill routed experts alone (no shared expert) through moe_forward_routed under a chosen
+    routing, for profiler runs: one_tile gives each of the 256 experts 256 rows (token t takes experts 8t ..
+    8t + 7 mod 256: one full tile each), two_tiles gives 128 experts 512 rows (mod 128: two full tiles each),
+    workload is the workload's own top-8 (216 experts, 1 to 963 rows). Gates are 1/8."""
+    import torch
+
+    cfg = wl.BY_NAME["glm5_prefill"]
+    log("generating the expert weights of %s" % cfg.name)
+    w = {n: to_dev_bf16(wl.weight(cfg, n), device) for n in ("w1", "w3", "w2")}
+    x = to_dev_bf16(wl.tokens(cfg), device)
+    t = torch.arange(cfg.T, device=device)[:, None]
+    j = torch.arange(cfg.k, device=device)[None, :]
+    if kind == "one_tile":
+        ids = ((cfg.k * t + j) % cfg.E).to(torch.int32).contiguous()
+    elif kind == "two_tiles":
+        ids = ((cfg.k * t + j) % (cfg.E // 2)).to(torch.int32).contiguous()
+    else:
+        wr = to_dev_bf16(wl.router_weight(cfg), device)
+        b = torch.from_numpy(wl.selection_bias(cfg)).to(device)
+        ids = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=device)
+        g = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=device)
+        m.moe_route(x, wr, b, cfg.k, cfg.scale, ids, g)
+    gates = torch.full((cfg.T, cfg.k), 1.0 / cfg.k, dtype=torch.float32, device=device)
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
+    ws = torch.empty(m.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, 0), dtype=torch.uint8, device=device)
+    counts = torch.bincount(ids.flatten().long(), minlength=cfg.E)
+    ms = time_call(lambda: m.moe_forward_routed(x, ids, gates, w["w1"], w["w3"], w["w2"], None, None, None, out, ws),
+                   args.steps, args.warmup)
+    log("routing %s: %d experts active, at most %d rows; %.4f ms/step (routed experts and combine)"
+        % (kind, int((counts > 0).sum()), int(counts.max()), ms))
+
+
 def cpu_baseline(cfg, host, budget_s, rounds=5):
     """The CPU oracle as it stands, token-sharded over the host's threads, on `rounds` equal slices of one
     seeded sample of the workload's tokens (about budget_s seconds in all); the value is the median rate of
@@ -417,6 +453,8 @@ def main():
                     help="run only this workload's timed steps and print its timings (for profiler runs): prefill, "
                          "decode, or any mixture or dense-MLP workload name (mid, glm5_skewed, glm47_prefill, "
                          "glm5_dense_decode, ...)")
+    ap.add_argument("--profile-routing", default=None, choices=ROUTINGS,
+                    help="profiler runs: only the GLM-5 prefill routed experts under the given routing")
     ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
                     help="set a knob of include/moe_tuning.h before measuring (e.g. MOE_TUNE_ORDER=1); the default "
                          "run sets none")
@@ -455,6 +493,9 @@ def main():
         m.moe_set_tuning(getattr(m, knob), int(value))
         log("tuning %s = %s" % (knob, value))
     device = torch.device("cuda", 0)
+    if args.profile_routing:
+        profile_routing(m, wl, args.profile_routing, args, device)
+        return
     if args.profile_only:
         profile_workload(m, wl, args.profile_only, args, device)
         return
