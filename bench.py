@@ -175,10 +175,11 @@ def gate_up_bytes(cfg, active, folded):
     return groups * 2 * cfg.H * cfg.I * 2 + 2 * cfg.T * cfg.H + 2 * gate_up_rows(cfg, folded) * cfg.I
 
 
-def time_call(fn, steps, warmup, min_warm_s=0.2):
+def time_call(fn, steps, warmup, min_warm_s=0.2, reps=3):
     """Mean ms of fn() over `steps` calls after `warmup` untimed calls, and at least `min_warm_s` seconds of
     them (a workload timed right after the host generated its weights finds the GPU's clocks idle: a few
-    warmup calls of a 0.1 ms decode pass do not bring them up), HIP events on the current stream."""
+    warmup calls of a 0.1 ms decode pass do not bring them up), HIP events on the current stream; the median
+    of `reps` such timed windows, back to back (one slow window, 30 ms at decode sizes, does not decide it)."""
     import torch
 
     for _ in range(warmup):
@@ -189,13 +190,16 @@ def time_call(fn, steps, warmup, min_warm_s=0.2):
         for _ in range(10):
             fn()
         torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(steps):
-        fn()
-    s1.record()
-    torch.cuda.synchronize()
-    return s0.elapsed_time(s1) / steps
+    means = []
+    for _ in range(reps):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        means.append(s0.elapsed_time(s1) / steps)
+    return float(np.median(means))
 
 
 def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
@@ -349,7 +353,7 @@ def profile_workload(m, wl, name, args, device):
         out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
         ws = torch.empty(m.moe_dense_mlp_workspace_bytes(cfg.T, cfg.H, cfg.Id), dtype=torch.uint8, device=device)
         steps = args.steps if cfg.T > 64 else args.decode_steps
-        ms = time_call(lambda: m.moe_dense_mlp(x, w["w1"], w["w3"], w["w2"], out, ws), steps, args.warmup)
+        ms = time_call(lambda: m.moe_dense_mlp(x, w["w1"], w["w3"], w["w2"], out, ws), steps, args.warmup, reps=1)
         log("%s: %.4f ms/step" % (name, ms))
         return
     if name not in wl.BY_NAME:
@@ -395,7 +399,7 @@ def profile_routing(m, wl, kind, args, device):
     ws = torch.empty(m.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, 0), dtype=torch.uint8, device=device)
     counts = torch.bincount(ids.flatten().long(), minlength=cfg.E)
     ms = time_call(lambda: m.moe_forward_routed(x, ids, gates, w["w1"], w["w3"], w["w2"], None, None, None, out, ws),
-                   args.steps, args.warmup)
+                   args.steps, args.warmup, reps=1)
     log("routing %s: %d experts active, at most %d rows; %.4f ms/step (routed experts and combine)"
         % (kind, int((counts > 0).sum()), int(counts.max()), ms))
 
