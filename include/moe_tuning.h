@@ -33,7 +33,8 @@ typedef enum moe_tune_knob {
     /* 0 by size (persistent routed GEMMs above the decode sizes), 1 one workgroup per block everywhere. */
     MOE_TUNE_PERSIST = 2,
     /* K split of decode-sized grouped GEMMs: 0 by the live block count, 1 never split, 2 always split in two,
-       3 the largest split each GEMM allows (gate/up 2; down up to 4 ranges at up to 16 tokens). */
+       3 the largest split each GEMM allows (gate/up 4 where four ranges are whole steps of the copy ring,
+       else 2; down up to 4 ranges at up to 16 tokens). */
     MOE_TUNE_KSPLIT = 3,
     /* Block order of the persistent routed GEMMs: 0 by size (experts in index order, each cut into chunks
        of up to 16 token tiles, contiguous XCD ranges); 1 the same with chunks of up to 128 tiles; dealt

@@ -376,7 +376,8 @@ moe_status forward_impl(const Request& q) {
         split.ksplit = ks_flag;
         split.ks_ntn[0] = moe::dma_ntn(true, I);
         split.ks_ntn[1] = moe::dma_ntn(false, H);
-        split.ks_allow[0] = 1 << 2;
+        const int nk1 = H / 64; // gate/up: two ranges, or four where they are whole ring periods
+        split.ks_allow[0] = (1 << 2) | (nk1 % 4 == 0 && (nk1 / 4) % 4 == 0 ? 1 << 4 : 0);
         split.ks_allow[1] = down_allow;
         split.cus = cus;
         split.ks_force = ks_on ? ks_knob : 0;
@@ -429,7 +430,7 @@ moe_status forward_impl(const Request& q) {
     const int h_rows = T * k + (grouped_shared ? T : 0);
     if (ks_gate_up) {
         r1.ksplit_dev = ks_flag;
-        r1.ks_allow = 1 << 2;
+        r1.ks_allow = split.ks_allow[0];
         r1.part = static_cast<float*>(at(L.ks_part));
         r1.part_rows = h_rows;
     }

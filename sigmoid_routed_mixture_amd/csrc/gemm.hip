@@ -1357,19 +1357,24 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
 __global__ __launch_bounds__(256) void reduce_swiglu_ksplit_kernel(const float* __restrict__ part,
                                                                    const int32_t* __restrict__ ksplit, int rows,
                                                                    int N, uint16_t* __restrict__ h) {
-    if (ksplit[0] != 2) return;
+    const int S = ksplit[0];
+    if (S < 2 || S > kMaxGateUpSplits) return;
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (int64_t)rows * N) return;
     const int64_t row = i / N, col = i % N;
-    const float* p0 = part + (size_t)row * 2 * N + col;
-    const float* p1 = p0 + (size_t)rows * 2 * N;
-    const float4 g0 = *reinterpret_cast<const float4*>(p0), u0 = *reinterpret_cast<const float4*>(p0 + N);
-    const float4 g1 = *reinterpret_cast<const float4*>(p1), u1 = *reinterpret_cast<const float4*>(p1 + N);
+    float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < S; ++sp) { // the K ranges in order
+        const float* p = part + ((size_t)sp * rows + row) * 2 * N + col;
+        const float4 gv = *reinterpret_cast<const float4*>(p), uv = *reinterpret_cast<const float4*>(p + N);
+        g[0] += gv.x; g[1] += gv.y; g[2] += gv.z; g[3] += gv.w;
+        u[0] += uv.x; u[1] += uv.y; u[2] += uv.z; u[3] += uv.w;
+    }
     uint2 v;
-    v.x = pack_bf16x2(swiglu(g0.x + g1.x, u0.x + u1.x), swiglu(g0.y + g1.y, u0.y + u1.y));
-    v.y = pack_bf16x2(swiglu(g0.z + g1.z, u0.z + u1.z), swiglu(g0.w + g1.w, u0.w + u1.w));
+    v.x = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+    v.y = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
     *reinterpret_cast<uint2*>(h + row * N + col) = v;
 }
+
 
 __global__ __launch_bounds__(256) void reduce_sum_kernel(const float* __restrict__ part, int S, int64_t n,
                                                          float* __restrict__ out) {
@@ -1441,7 +1446,7 @@ hipError_t launch_one(GemmPath path, const GemmArgs& a, int64_t grid_tiles, hipS
     if (KIND != GemmKind::Logits && !DENSE && path == GemmPath::Dma && a.ksplit_dev != nullptr) {
         for (int S = 2; S <= kMaxDownSplits; ++S)
             if ((a.ks_allow >> S) & 1) smax = S;
-        if ((a.ks_allow >> (kMaxDownSplits + 1)) != 0 || (KIND == GemmKind::GateUp && smax > 2))
+        if ((a.ks_allow >> (kMaxDownSplits + 1)) != 0 || (KIND == GemmKind::GateUp && smax > kMaxGateUpSplits))
             return hipErrorInvalidValue;
         if (a.part == nullptr || a.part_rows <= 0 || a.K < smax * kBK) return hipErrorInvalidValue;
         blocks *= smax; // room for the largest split

@@ -25,7 +25,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // kernel's two GEMMs, the work-balanced XCD split of their blocks (kXcds + 1 ints each, every XCD taking
 // at most cap[i] blocks). With `ctr` (8-byte aligned) it zeroes the 2 * kXcds 64-bit work counters of the
 // persistent DMA kernel (kXcds for each GEMM).
-// With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit and
+// With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit_gate_up and
 // decode_ksplit_down of the live blocks, ks_ntn[i] column tiles each, on `cus` compute units, among the splits
 // ks_allow[i] allows; ks_force > 0 forces one).
 // With `dealt` (and `bounds`) the tile list takes a dealt order of plan.h (DealtOrder) and `bounds` the exact
@@ -78,9 +78,9 @@ struct GemmArgs {
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
     const int32_t* ksplit_dev; // DMA kernel, grouped: the K split S the permutation chose, or null
-    int ks_allow;              // with ksplit_dev: the splits it may hold (bit S set; gate/up at most 2, down
-                               // at most kMaxDownSplits)
-    float* part;               // with a split: gate/up fp32 partials [2][part_rows][2N] (g, then u); down: the
+    int ks_allow;              // with ksplit_dev: the splits it may hold (bit S set; gate/up at most
+                               // kMaxGateUpSplits, down at most kMaxDownSplits)
+    float* part;               // with a split: gate/up fp32 partials [S][part_rows][2N] (g, then u); down: the
                                // fp32 rows of K ranges 2 .. S, [S - 1][part_rows][N] (range 1 goes to out)
     int part_rows;
     int out_bf16;              // grouped down GEMM: per-slot rows stored as bf16 (slot_rows_bf16), else fp32

@@ -186,15 +186,16 @@ __device__ int write_dealt_tiles(const XcdSplit& sp, int4* __restrict__ tiles, i
     return total;
 }
 
-// The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0): decode_ksplit for gate/up,
-// decode_ksplit_down among the down GEMM's allowed splits, or forced: ks_force 2 splits in two where that is
+// The K splits of a decode-sized launch's gate/up and down GEMMs (thread 0): decode_ksplit_gate_up and
+// decode_ksplit_down among each GEMM's allowed splits, or forced: ks_force 2 splits in two where that is
 // allowed, 3 takes the largest allowed split.
 __device__ __forceinline__ void write_ksplit(const XcdSplit& sp, int all_tiles) {
     if (sp.ksplit != nullptr && threadIdx.x == 0)
         for (int i = 0; i < 2; ++i) {
             const int allow = sp.ks_allow[i] | 2;
             const int64_t b = (int64_t)all_tiles * sp.ks_ntn[i];
-            int S = i == 0 ? ((allow >> 2) & 1 ? decode_ksplit(b, sp.cus) : 1) : decode_ksplit_down(b, sp.cus, allow);
+            int S = i == 0 ? ((allow >> 2) & 1 ? decode_ksplit_gate_up(b, sp.cus, (allow >> 4) & 1) : 1)
+                           : decode_ksplit_down(b, sp.cus, allow);
             if (sp.ks_force > 0) {
                 const int cap = sp.ks_force == 2 ? 2 : kMaxDownSplits;
                 S = 1;

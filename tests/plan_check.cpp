@@ -277,6 +277,19 @@ int main() {
           "expected_active");
     CHECK(moe::decode_ksplit((int64_t)(101 + 1) * 16, 256) == 2 && moe::decode_ksplit((int64_t)(41 + 1) * 12, 256) == 1,
           "decode gate/up split at GLM-5 / GLM-4.7-Flash");
+    // four ranges: only where two already pay, half-length blocks take at least 8 rounds and quarter-length
+    // ones round strictly better (GLM-5 decode, 81 groups x 16 column tiles: 11 rounds of halves, 21 of quarters)
+    CHECK(moe::decode_ksplit_gate_up(1296, 256, true) == 4 && moe::decode_ksplit_gate_up(1296, 256, false) == 2 &&
+              moe::decode_ksplit_gate_up(1152, 256, true) == 2 && moe::decode_ksplit_gate_up(444, 256, true) == 1 &&
+              moe::decode_ksplit_gate_up(600, 256, true) == 2 && moe::decode_ksplit_gate_up(0, 256, true) == 1,
+          "decode_ksplit_gate_up");
+    for (int64_t b = 1; b < 5000; b += 7)
+        for (int cus : {80, 256, 304}) {
+            const int s2 = moe::decode_ksplit(b, cus), s4 = moe::decode_ksplit_gate_up(b, cus, true);
+            const int64_t r2 = (2 * b + cus - 1) / cus, r4 = (4 * b + cus - 1) / cus;
+            CHECK(s4 == (s2 == 2 && r2 >= 8 && r4 < 2 * r2 ? 4 : s2) && moe::decode_ksplit_gate_up(b, cus, false) == s2,
+                  "gate/up split b=%lld cus=%d", (long long)b, cus);
+        }
     // block claims of the persistent kernel: any interleaving of front (home) and back (other XCDs) claims
     // hands every block of the range out exactly once, and later claims get none
     {
