@@ -202,39 +202,7 @@ def time_call(fn, steps, warmup, min_warm_s=0.2, reps=3):
     return float(np.median(means))
 
 
-def share_configs(wl):
-    """One GPU's share of the two multi-GPU layouts of the GLM-5 layer (nothing here uses a second GPU):
-    expert parallelism over 8 GPUs at prefill, where a GPU holds 32 experts and receives the slots routed to
-    them from 8 batches of 8192 tokens (65,536 rows, here uniformly spread: one slot per row, gate 1, through
-    the routed entry point; the shared expert runs data-parallel elsewhere), and expert tensor parallelism over
-    8 GPUs at decode, where every GPU holds all 256 experts with I / 8 = 256 (the whole layer at that width,
-    router included)."""
-    ep = wl.MoEConfig(60, "ep8_prefill_share", T=65536, H=6144, E=32, k=1, I=2048, Is=0, scale=1.0)
-    tp = wl.MoEConfig(61, "tp8_decode_share", T=16, H=6144, E=256, k=8, I=256, Is=256, scale=2.5)
-    return ep, tp
-
-
-def preload_weights(wl, device):
-    """The weights of every secondary workload, in device memory from the start, as a serving process holds
-    its layers' weights: allocated after the large buffers of other workloads have come and gone, the same
-    GLM-4.7-Flash decode pass measured 0.1717 ms against 0.1455 ms with weights allocated first (the device
-    memory behind a late allocation is fragmented), which would time the allocator rather than the layer."""
-    ep, tp = share_configs(wl)
-    c47 = wl.BY_NAME["glm47_decode"]
-    pre = {name: {n: to_dev_bf16(wl.weight(wl.BY_NAME[name], n), device) for n in WEIGHT_NAMES}
-           for name in ("tiny", "mid")}
-    pre.update({"glm47": {n: to_dev_bf16(wl.weight(c47, n), device) for n in WEIGHT_NAMES},
-           "tp8": {n: to_dev_bf16(wl.weight(tp, n), device) for n in WEIGHT_NAMES},
-           "ep8": {n: to_dev_bf16(wl.weight(ep, n), device) for n in ("w1", "w3", "w2")},
-           "dense": {}})
-    for cfg in wl.DENSE_CONFIGS:
-        if cfg.weight_seed not in pre["dense"]:
-            pre["dense"][cfg.weight_seed] = {k: to_dev_bf16(wl.dense_weight(cfg, k), device)
-                                             for k in ("w1", "w3", "w2")}
-    return pre
-
-
-def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
+def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup):
     """The other workloads and the entry points around the mixture, each timed on its own: tiny, mid and
     skewed, the GLM-4.7-Flash layer (decode and prefill), the block (RMSNorm + mixture + residual) and the
     routing override at the GLM-5 shapes, and the dense SwiGLU MLP of the dense-first blocks. Every mixture
@@ -278,7 +246,10 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
     # near the ridge: both fractions), skewed (32768 tokens, expert 0 takes every token)
     for name, n in (("tiny", decode_steps), ("mid", steps), ("glm5_skewed", max(2, steps // 2))):
         cfg = wl.BY_NAME[name]
-        w = dev_w if cfg.H == cfg_glm5_H and cfg.E == 256 else pre[name]
+        if cfg.H == cfg_glm5_H and cfg.E == 256:
+            w = dev_w
+        else:
+            w = {k: to_dev_bf16(wl.weight(cfg, k), device) for k in WEIGHT_NAMES}
         res[name], _, _ = mixture(cfg, layer_inputs(cfg, w), n)
         log("%s: %s" % (name, res[name]))
         del w
@@ -286,9 +257,12 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
 
     # GLM-4.7-Flash layer (H 2048, 64 experts top-4, I = Is = 1536, scale 1.8)
     c47d, c47p = wl.BY_NAME["glm47_decode"], wl.BY_NAME["glm47_prefill"]
+    log("generating GLM-4.7-Flash expert weights")
+    w47 = {n: to_dev_bf16(wl.weight(c47d, n), device) for n in WEIGHT_NAMES}
     for cfg, n in ((c47d, decode_steps), (c47p, steps)):
-        res[cfg.name], _, _ = mixture(cfg, layer_inputs(cfg, pre["glm47"]), n)
+        res[cfg.name], _, _ = mixture(cfg, layer_inputs(cfg, w47), n)
         log("%s: %s" % (cfg.name, res[cfg.name]))
+    del w47
 
     # block pass and routing override at the GLM-5 shapes, against the plain mixture on the same tokens
     for name, n in (("glm5_prefill", steps), ("glm5_decode", decode_steps)):
@@ -320,7 +294,7 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
     for name, n in (("glm5_dense_prefill", steps), ("glm5_dense_decode", decode_steps),
                     ("glm47_dense_prefill", steps)):
         cfg = wl.DENSE_BY_NAME[name]
-        w = pre["dense"][cfg.weight_seed]
+        w = {k: to_dev_bf16(wl.dense_weight(cfg, k), device) for k in ("w1", "w3", "w2")}
         x = to_dev_bf16(wl.dense_tokens(cfg), device)
         out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
         ws = torch.empty(m.moe_dense_mlp_workspace_bytes(cfg.T, cfg.H, cfg.Id), dtype=torch.uint8, device=device)
@@ -334,12 +308,17 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
             r.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
         res[name] = r
         log("%s: %s" % (name, r))
-        del x, out, ws
+        del w
     torch.cuda.empty_cache()
 
-    # one GPU's share of the expert-parallel prefill and the expert-tensor-parallel decode (share_configs)
-    ep, tp = share_configs(wl)
-    w = pre["ep8"]
+    # One GPU's share of the two multi-GPU layouts of the GLM-5 layer (nothing here uses a second GPU):
+    # expert parallelism over 8 GPUs at prefill, where a GPU holds 32 experts and receives the slots routed to
+    # them from 8 batches of 8192 tokens (65,536 rows, here uniformly spread: one slot per row, gate 1, through
+    # the routed entry point; the shared expert runs data-parallel elsewhere), and expert tensor parallelism
+    # over 8 GPUs at decode, where every GPU holds all 256 experts with I / 8 = 256 (the whole layer at that
+    # width, router included).
+    ep = wl.MoEConfig(60, "ep8_prefill_share", T=65536, H=6144, E=32, k=1, I=2048, Is=0, scale=1.0)
+    w = {n: to_dev_bf16(wl.weight(ep, n), device) for n in ("w1", "w3", "w2")}
     x = to_dev_bf16(wl.tokens(ep), device)
     ids = torch.from_numpy(np.random.default_rng(ep.seed).integers(0, ep.E, size=(ep.T, 1), dtype=np.int32)).to(device)
     gates = torch.ones(ep.T, 1, dtype=torch.float32, device=device)
@@ -350,10 +329,13 @@ def bench_next(m, wl, dev_w, host_w, device, steps, decode_steps, warmup, pre):
     tf = 6 * ep.T * ep.k * ep.H * ep.I / (ms * 1e-3) / 1e12
     res[ep.name] = {"rows": ep.T, "E": ep.E, "ms": ms, "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
     log("%s: %s" % (ep.name, res[ep.name]))
-    del x, out, ws
+    del w, x, out, ws
     torch.cuda.empty_cache()
-    res[tp.name], _, _ = mixture(tp, layer_inputs(tp, pre["tp8"]), decode_steps)
+    tp = wl.MoEConfig(61, "tp8_decode_share", T=16, H=6144, E=256, k=8, I=256, Is=256, scale=2.5)
+    w = {n: to_dev_bf16(wl.weight(tp, n), device) for n in WEIGHT_NAMES}
+    res[tp.name], _, _ = mixture(tp, layer_inputs(tp, w), decode_steps)
     log("%s: %s" % (tp.name, res[tp.name]))
+    del w
     torch.cuda.empty_cache()
     return res
 
@@ -366,7 +348,7 @@ def profile_workload(m, wl, name, args, device):
     name = {"prefill": "glm5_prefill", "decode": "glm5_decode"}.get(name, name)
     if name in wl.DENSE_BY_NAME:
         cfg = wl.DENSE_BY_NAME[name]
-        w = pre["dense"][cfg.weight_seed]
+        w = {k: to_dev_bf16(wl.dense_weight(cfg, k), device) for k in ("w1", "w3", "w2")}
         x = to_dev_bf16(wl.dense_tokens(cfg), device)
         out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device=device)
         ws = torch.empty(m.moe_dense_mlp_workspace_bytes(cfg.T, cfg.H, cfg.Id), dtype=torch.uint8, device=device)
@@ -527,7 +509,6 @@ def main():
     t0 = time.perf_counter()
     host_w = {n: wl.weight(cfg_p, n) for n in WEIGHT_NAMES}
     dev_w = {n: to_dev_bf16(a, device) for n, a in host_w.items()}
-    pre = None if args.no_next else preload_weights(wl, device)
     torch.cuda.synchronize()
     log("weights ready in %.1f s" % (time.perf_counter() - t0))
     two = args.two_streams
@@ -589,7 +570,7 @@ def main():
     }
     if not args.no_next:
         line["next"] = bench_next(m, wl, dev_w, host_w, device, max(3, args.steps // 2), args.decode_steps,
-                                  args.warmup, pre)
+                                  args.warmup)
     if not args.no_cpu_baseline:
         host = dict(host_tp)
         host.update(host_w)
