@@ -49,7 +49,14 @@ typedef enum moe_tune_knob {
        expected, else one workgroup per block), 1 the two-step ring of larger batches, 2 the three-step ring
        with one workgroup per block, 3 the three-step ring streamed wherever the launch allows it. */
     MOE_TUNE_RING = 6,
-    MOE_TUNE_KNOBS = 7 /* number of knobs */
+    /* Router top-k and permutation of the mixture at up to 16 tokens: 0 by size (one launch: the workgroup
+       that routes the last token permutes them all), 1 two launches, as above 16 tokens. */
+    MOE_TUNE_ROUTE_PERMUTE = 7,
+    /* Stream-K in the streamed decode GEMMs (one workgroup per CU, each taking one contiguous share of all
+       blocks' K steps, where the launch has at least as many blocks as CUs and no split is forced): 0 by size
+       (the down GEMM), 1 never (whole blocks or the K split's equal ranges), 2 the down and the gate/up GEMM. */
+    MOE_TUNE_STREAMK = 8,
+    MOE_TUNE_KNOBS = 9 /* number of knobs */
 } moe_tune_knob;
 
 /* Sets a knob. MOE_ERR_INVALID_ARG for an unknown knob or a value outside the knob's range (nothing

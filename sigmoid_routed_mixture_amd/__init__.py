@@ -92,8 +92,8 @@ EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_permute_workspace_bytes", "moe_r
                     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes")
 # Knobs of include/moe_tuning.h (tests and benchmarks only; 0 = the size rules).
 (MOE_TUNE_GEMM_PATH, MOE_TUNE_XCD_SPLIT, MOE_TUNE_PERSIST, MOE_TUNE_KSPLIT, MOE_TUNE_ORDER, MOE_TUNE_SHARED,
- MOE_TUNE_RING) = range(7)
-MOE_TUNE_KNOBS = 7
+ MOE_TUNE_RING, MOE_TUNE_ROUTE_PERMUTE, MOE_TUNE_STREAMK) = range(9)
+MOE_TUNE_KNOBS = 9
 GEMM_PATHS = {"auto": 0, "wide": 1, "tall": 2, "dma": 3, "skinny": 4}
 
 
@@ -149,7 +149,8 @@ class tuned:
     `with tuned(MOE_TUNE_GEMM_PATH=3): ...`."""
 
     _names = {"MOE_TUNE_GEMM_PATH": 0, "MOE_TUNE_XCD_SPLIT": 1, "MOE_TUNE_PERSIST": 2, "MOE_TUNE_KSPLIT": 3,
-              "MOE_TUNE_ORDER": 4, "MOE_TUNE_SHARED": 5, "MOE_TUNE_RING": 6}
+              "MOE_TUNE_ORDER": 4, "MOE_TUNE_SHARED": 5, "MOE_TUNE_RING": 6,
+              "MOE_TUNE_ROUTE_PERMUTE": 7, "MOE_TUNE_STREAMK": 8}
 
     def __init__(self, **knobs):
         self.knobs = {self._names[k]: v for k, v in knobs.items()}

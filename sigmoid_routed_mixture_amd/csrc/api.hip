@@ -106,7 +106,7 @@ moe_status device_scratch(void** out) {
 // Overrides of the size rules (include/moe_tuning.h), read once per call: 0 everywhere unless a test or
 // benchmark set one.
 std::atomic<int> g_tuning[MOE_TUNE_KNOBS];
-constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 3, 4, 1, 3};
+constexpr int kTuneMax[MOE_TUNE_KNOBS] = {4, 1, 1, 3, 4, 1, 3, 1, 2};
 
 int tuning(moe_tune_knob k) { return g_tuning[k].load(std::memory_order_relaxed); }
 
@@ -319,12 +319,19 @@ moe_status forward_impl(const Request& q) {
         MOE_HIP(moe::launch_rmsnorm(q.resid, q.gamma, q.eps, T, H, xn, s0), "rmsnorm");
         xin = xn;
     }
-    if (!given) {
-        const int S = moe::router_splits(T, H, E);
+    // up to kRouterSmallT tokens the router's top-k and the permutation share one launch (its ticket: the
+    // first int of the permutation's chunk scratch, which a single chunk does not use)
+    const int router_S = moe::router_splits(T, H, E);
+    const bool route_permute = !given && T <= moe::kRouterSmallT && tuning(MOE_TUNE_ROUTE_PERMUTE) == 0;
+    int32_t* ticket = route_permute ? static_cast<int32_t*>(at(L.chunk_base)) : nullptr;
+    if (route_permute)
+        MOE_HIP(moe::launch_router_logits_small(xin, q.w_router, T, H, E, static_cast<float*>(at(L.partial)),
+                                                router_S, ticket, s0),
+                "router logits");
+    else if (!given)
         MOE_HIP(moe::launch_router(xin, q.w_router, q.bias, T, H, E, k, q.scale, ids_out, gates_out, nullptr,
-                                   static_cast<float*>(at(L.partial)), S, s0),
+                                   static_cast<float*>(at(L.partial)), router_S, s0),
                 "router");
-    }
     MOE_TRY(mark(1));
     const int64_t grid_tiles = moe::max_tiles(T, E, k, BM) + (grouped_shared ? moe::shared_tiles(T, BM) : 0);
     moe::XcdSplit split{};
@@ -382,14 +389,27 @@ moe_status forward_impl(const Request& q) {
         split.cus = cus;
         split.ks_force = ks_on ? ks_knob : 0;
         // the gate/up split needs a reduction launch: only when the experts the batch is expected to reach
-        // would split (the down GEMM's halves are added by the combine, with no launch of their own)
+        // would split (the down GEMM's planes are added by the combine, with no launch of their own).
+        // Stream-K only in streamed launches: the down GEMM's by default, the gate/up GEMM's with knob value 2
+        // (and then only with its reduction enqueued): it pays for neither the reduction nor the partials
+        // there (plan.h, decode_streamk)
         const int64_t expect = (moe::expected_active(T, E, k) + moe::shared_tiles(T, BM)) * split.ks_ntn[0];
-        ks_gate_up = ks_on || moe::decode_ksplit(expect, cus) == 2;
+        const int sk_knob = ks_on ? 1 : tuning(MOE_TUNE_STREAMK);
+        ks_gate_up = ks_on || moe::decode_ksplit(expect, cus) == 2 ||
+                     (sk_knob == 2 && deep_gate_up == 2 && moe::decode_streamk(expect, cus));
+        split.ks_streamk[0] = sk_knob == 2 && deep_gate_up == 2 && ks_gate_up ? 1 : 0;
+        split.ks_streamk[1] = sk_knob != 1 && deep_down == 2 ? 1 : 0;
     }
-    MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
-                                static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, grouped_shared ? T : 0, split,
-                                s0),
-            "permute");
+    if (route_permute)
+        MOE_HIP(moe::launch_route_permute_few(static_cast<const float*>(at(L.partial)), router_S, q.bias, T, E, k,
+                                              q.scale, ids_out, gates_out, nullptr, ticket, counts, offsets, row_token,
+                                              slot_row, tiles, ntiles, BM, grouped_shared ? T : 0, split, s0),
+                "route and permute");
+    else
+        MOE_HIP(moe::launch_permute(ids, T, E, k, counts, offsets, row_token, slot_row,
+                                    static_cast<int32_t*>(at(L.chunk_base)), tiles, ntiles, BM, grouped_shared ? T : 0,
+                                    split, s0),
+                "permute");
     MOE_TRY(mark(2));
     // The shared expert needs no routing: with a second stream it forks here, after the router and the
     // permutation (so it cannot delay them), and overlaps the routed experts.

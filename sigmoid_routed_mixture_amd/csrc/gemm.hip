@@ -921,11 +921,16 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
 
     int S = 1;
     int64_t live;
+    bool sk = false; // stream-K: this workgroup takes one contiguous share of every block's K steps
+    int64_t p_end = 0;
     if (DENSE) {
         S = a.ksplit > 1 ? a.ksplit : 1;
         live = (int64_t)ntn * S; // at most 32 rows: one token tile
     } else {
-        if (a.ksplit_dev != nullptr) S = device_split(a.ksplit_dev);
+        if (a.ksplit_dev != nullptr) {
+            S = device_split(a.ksplit_dev);
+            sk = S == 2 && a.ksplit_dev[2] == 1;
+        }
         const int nt = min(a.ntiles[0], kStreamMaxTiles);
         for (int i = tid; i < nt; i += kDThreads) {
             const int4 e = a.tiles[i];
@@ -937,6 +942,10 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         if (KIND == GemmKind::GateUp)
             for (int i = tid; i < min(a.rt_rows, kStreamMaxRows); i += kDThreads) rt[i] = a.row_token[i];
         live = (int64_t)nt * ntn * S;
+        // stream-K needs every block cut at most once (each workgroup's share at least one block: as many
+        // blocks as workgroups) and whole ring periods; else the even split in two, which writes the same
+        // two planes
+        sk = sk && nk_all % 4 == 0 && (int64_t)nt * ntn >= (int64_t)gridDim.x && gridDim.x % kXcds == 0;
         __syncthreads();
     }
     const int nk = nk_all / S;
@@ -962,6 +971,53 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         return block_from<kDRows>(a, ntn, Lb, make_int4(e[0], e[1], e[2], e[3]), ti, ntile) && ti.rows <= 32;
     };
 
+    // A piece of work: K steps [sb, sb + n) of one block, written to partial plane `plane` (the K split's
+    // range index); `zero`: the piece is a whole block of a stream-K launch, which also writes zeros to the
+    // other plane (the reduction adds both planes of every row). `next` is the cursor of the piece after it.
+    // Even split: the cursor is the one-shot block index v (the workgroup's blocks are v, v + grid, ...).
+    // Stream-K: the cursor is a ring period (4 K steps) of the live blocks' periods in the one-shot order
+    // without the XCD interleave, P per block; the workgroup in place `pos` takes periods
+    // [pos T / G, (pos + 1) T / G) of the T in all, the places of one XCD's workgroups consecutive, so an
+    // XCD's blocks are one contiguous run of the order, as with the even split. A block cut between two
+    // workgroups gives its first piece plane 0 and its second plane 1.
+    const int P = nk_all / 4;
+    int64_t cursor = blockIdx.x;
+    if (sk) {
+        const int64_t G = gridDim.x, T4 = (live / S) * P;
+        const int64_t pos = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+        cursor = pos * T4 / G;
+        p_end = (pos + 1) * T4 / G;
+    }
+    struct Piece {
+        TileInfo ti;
+        int ntile, plane, sb, n;
+        bool zero;
+        int64_t next;
+    };
+    auto piece_at = [&](int64_t c, Piece& pc) -> bool {
+        if (!sk) {
+            if (!block_of(c, pc.ti, pc.ntile, pc.plane)) return false;
+            pc.sb = pc.plane * nk;
+            pc.n = nk;
+            pc.zero = false;
+            pc.next = c + gridDim.x;
+            return true;
+        }
+        if (c >= p_end) return false;
+        const int64_t Lb = c / P;
+        const int ps = (int)(c - Lb * P);
+        const int pe = (int)min((int64_t)P, p_end - Lb * P);
+        const int* e = tl + 4 * (Lb / ntn);
+        if (!block_from<kDRows>(a, ntn, Lb, make_int4(e[0], e[1], e[2], e[3]), pc.ti, pc.ntile) || pc.ti.rows > 32)
+            return false;
+        pc.plane = ps == 0 ? 0 : 1;
+        pc.sb = 4 * ps;
+        pc.n = 4 * (pe - ps);
+        pc.zero = ps == 0 && pe == P;
+        pc.next = Lb * P + pe;
+        return true;
+    };
+
     // copy source of a block: weight resources and per-lane offsets as in dma_tile, the token rows of waves
     // 4-7 those of waves 0-3
     struct Src {
@@ -971,7 +1027,7 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         uint32_t xoff;
         int sb; // first K step of the block's range
     };
-    auto source = [&](const TileInfo& ti, int ntile, int ks) {
+    auto source = [&](const TileInfo& ti, int ntile, int sb) {
         Src c;
         c.w0 = weight_row(a.w_a, a.ws_a, ti, N, 0, K);
         c.w1 = KIND == GemmKind::GateUp ? weight_row(a.w_b, a.ws_b, ti, N, 0, K) : c.w0;
@@ -987,7 +1043,7 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         int row = ti.off + ti.m0 + m;
         if (KIND == GemmKind::GateUp && !DENSE) row = ti.shared ? ti.m0 + m : rt[row];
         c.xoff = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(ls ^ dswz(r)) * 16u;
-        c.sb = ks * nk;
+        c.sb = sb;
         return c;
     };
     auto copy = [&](const Src& c, uint16_t* wl, uint16_t* xl, int st) {
@@ -1045,10 +1101,11 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
     };
     // fp32 rows (down) or bf16 h / fp32 partials (gate/up) of a finished block, straight from the accumulators:
     // lane holds features 4 kg .. 4 kg + 3 of weight block i for token 16 wn + rl
-    auto finish = [&](const TileInfo& ti, int ntile, int ks) {
+    auto finish = [&](const TileInfo& ti, int ntile, int ks, bool zero) {
         const int m = brow + rl;
         if (m >= ti.rows) return;
         const size_t row = (size_t)ti.off + ti.m0 + m;
+        const f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (KIND == GemmKind::DownF32) {
             float* yout = DENSE && S > 1 ? a.part + (size_t)ks * a.part_rows * N
                                          : (ks == 0 ? static_cast<float*>(a.out)
@@ -1064,6 +1121,7 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + col) = v;
                 } else {
                     *reinterpret_cast<f32x4*>(yout + row * N + col) = acc[i];
+                    if (zero) *reinterpret_cast<f32x4*>(a.part + row * N + col) = z4; // plane 1
                 }
             }
         } else {
@@ -1076,6 +1134,11 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
                     float* prow = a.part + (size_t)ks * a.part_rows * 2 * N + row * 2 * N;
                     *reinterpret_cast<f32x4*>(prow + col) = acc[i];
                     *reinterpret_cast<f32x4*>(prow + N + col) = acc[i + 2];
+                    if (zero) { // plane 1
+                        float* zrow = a.part + (size_t)a.part_rows * 2 * N + row * 2 * N;
+                        *reinterpret_cast<f32x4*>(zrow + col) = z4;
+                        *reinterpret_cast<f32x4*>(zrow + N + col) = z4;
+                    }
                 } else {
                     const f32x4 g = acc[i], u = acc[i + 2];
                     uint2 v;
@@ -1087,12 +1150,11 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         }
     };
 
-    int64_t v = blockIdx.x;
-    TileInfo ti;
-    int ntile = 0, ks = 0;
-    if (!block_of(v, ti, ntile, ks)) return;
-    Src cur = source(ti, ntile, ks);
-    // the first block's ring: steps 0 to 3 (nk >= 4); the first barrier waits for X0 and W0
+    Piece pc;
+    if (!piece_at(cursor, pc)) return;
+    Src cur = source(pc.ti, pc.ntile, pc.sb);
+    // the first piece's ring: steps 0 to 3 (every piece has a multiple of 4 steps); the first barrier waits
+    // for X0 and W0
     copy(cur, ws0, xs0, 0);
     copy(cur, ws1, xs1, 1);
     copy(cur, ws2, xs2, 2);
@@ -1101,22 +1163,20 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
     __builtin_amdgcn_s_barrier();
     read(f0a, f0b, ws0, xs0, 0);
     for (;;) {
-        const int64_t vn = v + gridDim.x;
-        TileInfo tn;
-        int ntn2 = 0, ksn = 0;
-        const bool has = block_of(vn, tn, ntn2, ksn);
-        // this block's steps 0 .. nk - 5, copying its steps 4 .. nk - 1
-        for (int s = 0; s + 8 <= nk; s += 4) {
+        Piece pn;
+        const bool has = piece_at(pc.next, pn);
+        // this piece's steps 0 .. n - 5, copying its steps 4 .. n - 1
+        for (int s = 0; s + 8 <= pc.n; s += 4) {
             dstep(ws0, xs0, ws1, xs1, cur, s + 4);
             dstep(ws1, xs1, ws2, xs2, cur, s + 5);
             dstep(ws2, xs2, ws3, xs3, cur, s + 6);
             dstep(ws3, xs3, ws0, xs0, cur, s + 7);
         }
-        // its last four steps copy the next block's steps 0 .. 3, or (last block) repeat its own last step
+        // its last four steps copy the next piece's steps 0 .. 3, or (last piece) repeat its own last step
         Src nxt = cur;
-        int z = nk - 1, dz = 0;
+        int z = pc.n - 1, dz = 0;
         if (has) {
-            nxt = source(tn, ntn2, ksn);
+            nxt = source(pn.ti, pn.ntile, pn.sb);
             z = 0;
             dz = 1;
         }
@@ -1124,15 +1184,12 @@ __device__ __forceinline__ void dma_stream(const GemmArgs& a, int ntn, uint16_t*
         dstep(ws1, xs1, ws2, xs2, nxt, z + dz);
         dstep(ws2, xs2, ws3, xs3, nxt, z + 2 * dz);
         dstep(ws3, xs3, ws0, xs0, nxt, z + 3 * dz);
-        // the first-half fragments of the next block's step 0 are in f0a / f0b now
-        finish(ti, ntile, ks);
+        // the first-half fragments of the next piece's step 0 are in f0a / f0b now
+        finish(pc.ti, pc.ntile, pc.plane, pc.zero);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!has) break;
-        v = vn;
-        ti = tn;
-        ntile = ntn2;
-        ks = ksn;
+        pc = pn;
         cur = nxt;
     }
     __builtin_amdgcn_s_waitcnt(0x0070); // no copy into LDS may outlive the workgroup

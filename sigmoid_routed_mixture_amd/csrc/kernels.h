@@ -16,6 +16,11 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
                          float scale, int32_t* ids, float* gates, float* logits, float* partial, int S,
                          hipStream_t stream);
 
+// The logits alone of up to kRouterSmallT tokens (router_small_kernel: fp32 partials [S, T, E]); with
+// `ticket` its first workgroup also zeroes that int for launch_route_permute_few.
+hipError_t launch_router_logits_small(const uint16_t* x, const uint16_t* wr, int T, int H, int E, float* partial,
+                                     int S, int32_t* ticket, hipStream_t stream);
+
 // Permutation: per-chunk expert histograms, the prefix sums (and, when `tiles` is non-null, the list of
 // BM-row grouped-GEMM tiles, kTileEntryBytes each), then the stable scatter of slots into expert-contiguous
 // rows.
@@ -27,7 +32,10 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* bia
 // persistent DMA kernel (kXcds for each GEMM).
 // With `ksplit` it writes the K splits of the gate/up and down GEMMs (two ints: decode_ksplit_gate_up and
 // decode_ksplit_down of the live blocks, ks_ntn[i] column tiles each, on `cus` compute units, among the splits
-// ks_allow[i] allows; ks_force > 0 forces one).
+// ks_allow[i] allows; ks_force > 0 forces one), then two stream-K flags: 1 where ks_streamk[i] allows it,
+// nothing is forced, the split in two is allowed and the GEMM has at least `cus` live blocks (its split is
+// then 2: the streamed kernel cuts each block at most once, the other kernels in halves, into the same two
+// planes).
 // With `dealt` (and `bounds`) the tile list takes a dealt order of plan.h (DealtOrder) and `bounds` the exact
 // XCD ranges of that order for both GEMMs (when the chunks fit kMaxDealtChunks; else the plain order and
 // split). The plain order cuts groups into chunks of at most plain_cap tiles.
@@ -41,6 +49,7 @@ struct XcdSplit {
     int ks_allow[2]; // splits each GEMM may take: bit S set for S allowed (1 always is)
     int cus;
     int ks_force;    // 0 by the rule, 2 split in two, 3 the largest allowed split
+    int ks_streamk[2]; // the GEMM's launch is streamed and may take stream-K (the gate/up reduction is enqueued)
     int dealt;
     int plain_cap;
     int spread_shared; // plain order: the shared group's tiles in kXcds chunks spread through the list
@@ -48,6 +57,16 @@ struct XcdSplit {
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_row, int32_t* chunk_scratch, int4* tiles,
                           int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split, hipStream_t stream);
+
+// Top-k of up to kRouterSmallT tokens from the partials launch_router_logits_small wrote (summed in split
+// order, as launch_router does), then the single-chunk permutation of launch_permute, in one launch: one
+// workgroup per token; the last to finish (counted on `ticket`, which the logits launch zeroed) permutes
+// every token's ids. Writes what launch_router and launch_permute write, bit for bit.
+hipError_t launch_route_permute_few(const float* partial, int S, const float* bias, int T, int E, int k, float scale,
+                                    int32_t* ids, float* gates, float* logits, int32_t* ticket, int32_t* counts,
+                                    int32_t* offsets, int32_t* row_token, int32_t* slot_row, int4* tiles,
+                                    int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split,
+                                    hipStream_t stream);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E].
 hipError_t launch_gather_rows(const uint16_t* x, const int32_t* row_token, const int32_t* offsets, int E, int T,
@@ -77,7 +96,8 @@ struct GemmArgs {
                                   // form (one workgroup per CU claiming blocks), or null for one block each
     int ksplit;                // logits, and dense weight-streaming GEMMs: K ranges, each writing its own fp32
                                // partial ([dense_rows, N]; gate/up: [dense_rows, 2N], g then u)
-    const int32_t* ksplit_dev; // DMA kernel, grouped: the K split S the permutation chose, or null
+    const int32_t* ksplit_dev; // DMA kernel, grouped: the K split S the permutation chose, or null; [2] is
+                               // the stream-K flag (the streamed kernel's cut of each block in two planes)
     int ks_allow;              // with ksplit_dev: the splits it may hold (bit S set; gate/up at most
                                // kMaxGateUpSplits, down at most kMaxDownSplits)
     float* part;               // with a split: gate/up fp32 partials [S][part_rows][2N] (g, then u); down: the

@@ -10,6 +10,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -17,12 +18,14 @@ namespace {
 constexpr int kChunk = kPermChunk;
 static_assert(kChunk == 256, "one thread per token of a chunk");
 
+// Bit matrix of the chunk of tokens [t0, t0 + 256): bit (t - t0) of expert e's row is set when token t
+// chose e.
 __device__ __forceinline__ void build_mask(uint32_t (*mask)[8], const int32_t* __restrict__ ids, int T, int E,
-                                           int k) {
+                                           int k, int t0) {
     const int tid = threadIdx.x;
     for (int i = tid; i < kMaxE * 8; i += 256) mask[i >> 3][i & 7] = 0u;
     __syncthreads();
-    const int t = blockIdx.x * kChunk + tid;
+    const int t = t0 + tid;
     if (t < T) {
         for (int j = 0; j < k; ++j) {
             const int e = ids[(size_t)t * k + j];
@@ -35,7 +38,7 @@ __device__ __forceinline__ void build_mask(uint32_t (*mask)[8], const int32_t* _
 __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                          int32_t* __restrict__ chunk_counts) {
     __shared__ uint32_t mask[kMaxE][8];
-    build_mask(mask, ids, T, E, k);
+    build_mask(mask, ids, T, E, k, blockIdx.x * kChunk);
     const int e = threadIdx.x;
     if (e < E) {
         int c = 0;
@@ -202,7 +205,9 @@ __device__ __forceinline__ void write_ksplit(const XcdSplit& sp, int all_tiles) 
                 for (int v = 2; v <= cap; ++v)
                     if ((allow >> v) & 1) S = v;
             }
-            sp.ksplit[i] = S;
+            const int sk = sp.ks_force == 0 && sp.ks_streamk[i] && ((allow >> 2) & 1) && decode_streamk(b, sp.cus);
+            sp.ksplit[i] = sk ? 2 : S;
+            sp.ksplit[2 + i] = sk;
         }
 }
 
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ row_token,
                                                            int32_t* __restrict__ slot_row) {
     __shared__ uint32_t mask[kMaxE][8];
-    build_mask(mask, ids, T, E, k);
+    build_mask(mask, ids, T, E, k, blockIdx.x * kChunk);
     const int tid = threadIdx.x;
     const int t = blockIdx.x * kChunk + tid;
     if (t >= T) return;
@@ -347,17 +352,16 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 }
 
 // The whole permutation in one workgroup when all tokens fit one chunk (decode): histogram, offsets and
-// tile list, then the scatter, with the bit matrix kept in LDS between them.
-__global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
-                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                          int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                          int BM, int shared_rows, XcdSplit split,
-                                                          int32_t* __restrict__ row_token,
-                                                          int32_t* __restrict__ slot_row) {
+// tile list, then the scatter, with the bit matrix kept in LDS between them. Every thread of the 256-thread
+// workgroup calls it (it holds barriers).
+__device__ void permute_single(const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ counts,
+                               int32_t* __restrict__ offsets, int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                               int BM, int shared_rows, const XcdSplit& split, int32_t* __restrict__ row_token,
+                               int32_t* __restrict__ slot_row) {
     __shared__ uint32_t mask[kMaxE][8];
     __shared__ int sh[256];
     __shared__ int offs[kMaxE];
-    build_mask(mask, ids, T, E, k);
+    build_mask(mask, ids, T, E, k, 0);
     const int tid = threadIdx.x;
     int n = 0;
     if (tid < E) {
@@ -390,6 +394,60 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
         row_token[row] = t;
         slot_row[(size_t)t * k + j] = row;
     }
+}
+
+__global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int4* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                          int BM, int shared_rows, XcdSplit split,
+                                                          int32_t* __restrict__ row_token,
+                                                          int32_t* __restrict__ slot_row) {
+    permute_single(ids, T, E, k, counts, offsets, tiles, ntiles, BM, shared_rows, split, row_token, slot_row);
+}
+
+// Decode: the router's top-k and the permutation in one launch. Workgroup t sums token t's S partial logits
+// in split order (one thread per expert, every load in flight at once) and one wave routes the token, as
+// the router's few-token top-k kernel does. The wave then publishes the token's ids (an agent-scope fence
+// before its ticket: the workgroups may run on different XCDs, each with its own L2) and takes a ticket;
+// the workgroup that takes the last one (T - 1) fences again and runs the single-chunk permutation over
+// every token's ids. The logits kernel zeroed the ticket, so exactly one workgroup permutes.
+__global__ __launch_bounds__(256) void route_permute_few_kernel(
+    const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E, int k, float scale,
+    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ logits, int32_t* __restrict__ ticket,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
+    int32_t* __restrict__ ntiles, int BM, int shared_rows, XcdSplit split, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_row) {
+    __shared__ float zs[kMaxE];
+    __shared__ int last;
+    const int t = blockIdx.x;
+    const int e = threadIdx.x;
+    if (e < E) {
+        const size_t stride = (size_t)T * E;
+        const float* p = partial + (size_t)t * E + e;
+        float v[kRouterMaxSplits];
+#pragma unroll
+        for (int i = 0; i < kRouterMaxSplits; ++i)
+            if (i < S) v[i] = p[(size_t)i * stride];
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRouterMaxSplits; ++i)
+            if (i < S) z += v[i];
+        zs[e] = z;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        float z4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) z4[q] = lane + 64 * q < E ? zs[lane + 64 * q] : 0.f;
+        topk_token(z4, t, E, k, scale, bias, ids, gates, logits);
+        __threadfence(); // this token's ids reach every XCD before its ticket
+        if (lane == 0) last = atomicAdd(ticket, 1) == T - 1 ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last) return; // uniform over the workgroup
+    __threadfence();   // every token's ids, as published before their tickets
+    permute_single(ids, T, E, k, counts, offsets, tiles, ntiles, BM, shared_rows, split, row_token, slot_row);
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
@@ -430,6 +488,17 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     perm_scatter_kernel<<<chunks, 256, 0, stream>>>(ids, T, E, k, offsets, chunk_scratch, row_token, slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_permute_few(const float* partial, int S, const float* bias, int T, int E, int k, float scale,
+                                    int32_t* ids, float* gates, float* logits, int32_t* ticket, int32_t* counts,
+                                    int32_t* offsets, int32_t* row_token, int32_t* slot_row, int4* tiles,
+                                    int32_t* ntiles, int BM, int shared_rows, const XcdSplit& split,
+                                    hipStream_t stream) {
+    route_permute_few_kernel<<<T, 256, 0, stream>>>(partial, S, bias, T, E, k, scale, ids, gates, logits, ticket,
+                                                    counts, offsets, tiles, ntiles, BM, shared_rows, split, row_token,
+                                                    slot_row);
     return hipGetLastError();
 }
 

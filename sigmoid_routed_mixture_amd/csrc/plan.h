@@ -248,6 +248,13 @@ constexpr int decode_ksplit_gate_up(int64_t blocks, int cus, bool allow4) {
     const int64_t r2 = (2 * blocks + cus - 1) / cus, r4 = (4 * blocks + cus - 1) / cus;
     return r2 >= 8 && r4 < 2 * r2 ? 4 : 2;
 }
+// Stream-K at decode: a streamed launch (below) of b live blocks, b at least the number of CUs (so every
+// workgroup's share of the blocks' K steps is at least one block long and each block is cut at most once),
+// gives each workgroup one contiguous share of the ring periods of all blocks: every CU streams the same
+// number of weight bytes, where whole blocks or even splits leave the last round part-empty (GLM-4.7-Flash
+// decode: 444 gate/up blocks, 1.73 rounds; 296 down blocks in three ranges, 3.47). The cut blocks write two
+// fp32 planes that the gate/up reduction and the combine add, as for the split in two.
+constexpr bool decode_streamk(int64_t blocks, int cus) { return cus > 0 && blocks >= cus; }
 // A decode-sized grouped GEMM runs streamed (one workgroup per CU, its blocks back to back, the next block's
 // first copies in flight during the current one's last steps) when the blocks it is expected to have, with
 // the K split decode_ksplit would choose, come to at most 4 per CU: there the blocks' empty-ring starts
@@ -266,7 +273,8 @@ struct Layout {
     size_t total;
 };
 // with_norm adds a [T, H] bf16 region for the RMS-normalised stream of the block entry point.
-// ks_flag / ks_part / ks_part_down: the device's K-split choices (gate/up, down: two ints), the gate/up
+// ks_flag / ks_part / ks_part_down: the device's K-split choices (gate/up, down: two ints, then their two
+// stream-K flags), the gate/up
 // partials [2][T·k + T][2I] fp32 and the rows of the down GEMM's ranges 2 .. S, [down_split_max(T) - 1]
 // [T·k + T][H] fp32, of a decode-sized launch (ksplit_possible), else not present.
 Layout forward_layout(int T, int H, int E, int k, int I, int Is, bool with_norm = false);

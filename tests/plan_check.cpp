@@ -82,7 +82,7 @@ int main() {
                                       (!fold && k >= 8 && !moe::ksplit_possible(T, H, E, k, I, Is)),
                                   "bf16 per-slot rows (T=%d E=%d k=%d)", T, E, k);
                             if (L.ks_flag != size_t(-1)) {
-                                rs.push_back({L.ks_flag, 8, "ks_flag"});
+                                rs.push_back({L.ks_flag, 16, "ks_flag"});
                                 rs.push_back({L.ks_part, 2 * rows * I * 2 * 4, "ks_part"});
                                 rs.push_back({L.ks_part_down, (size_t)(moe::down_split_max(T) - 1) * rows * H * 4,
                                               "ks_part_down"});

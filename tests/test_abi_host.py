@@ -217,7 +217,7 @@ def test_tuning_knobs_set_get_and_reject_out_of_range(lib):
     # include/moe_tuning.h: process-wide knobs, 0 = the size rules; bad knobs or values change nothing
     lib.moe_set_tuning.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.moe_get_tuning.argtypes = [ctypes.c_int]
-    maxima = {0: 4, 1: 1, 2: 1, 3: 3, 4: 4, 5: 1, 6: 3}
+    maxima = {0: 4, 1: 1, 2: 1, 3: 3, 4: 4, 5: 1, 6: 3, 7: 1, 8: 2}
     for knob, top in maxima.items():
         assert lib.moe_get_tuning(knob) == 0
         for v in range(top + 1):
@@ -227,8 +227,8 @@ def test_tuning_knobs_set_get_and_reject_out_of_range(lib):
         assert lib.moe_set_tuning(knob, -1) == INVALID
         assert lib.moe_get_tuning(knob) == top
         assert lib.moe_set_tuning(knob, 0) == OK
-    assert lib.moe_set_tuning(7, 0) == INVALID
-    assert lib.moe_get_tuning(7) == -1 and lib.moe_get_tuning(-1) == -1
+    assert lib.moe_set_tuning(9, 0) == INVALID
+    assert lib.moe_get_tuning(9) == -1 and lib.moe_get_tuning(-1) == -1
 
 
 def test_library_reads_no_environment():

@@ -216,6 +216,7 @@ def test_decode_copy_ring_does_not_change_results(moe, tune, name, T):
     # for bit, and so does the three-step ring with one workgroup per block
     say("[copy ring] %s T=%d" % (name, T))
     cfg, h, d = case(name)
+    tune(MOE_TUNE_STREAMK=1)  # whole blocks in every ring (stream-K cuts blocks where the ring streams)
     a = run_forward(moe, cfg, d, T=T)
     for ring in (1, 2, 3):
         tune(MOE_TUNE_RING=ring)
@@ -233,7 +234,7 @@ def test_streamed_decode_gemms(moe, tune, name, T, ks):
     # bit for bit what one workgroup per block computes, and within the bar of the oracle
     say("[streamed] %s T=%d ksplit knob %d" % (name, T, ks))
     cfg, h, d = case(name)
-    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3)
+    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3, MOE_TUNE_STREAMK=1)
     a = run_forward(moe, cfg, d, T=T)
     tune(MOE_TUNE_RING=2)
     b = run_forward(moe, cfg, d, T=T)
@@ -242,6 +243,53 @@ def test_streamed_decode_gemms(moe, tune, name, T, ks):
     ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(T))
     same, _, _ = compare_routing(a[1], a[2], ref, name)
     compare_out(a[0][same], ref["out"][same], "%s streamed T=%d" % (name, T))
+
+
+STREAMK = [
+    # workload or shape, batch, what
+    ("glm47_decode", 16, "GLM-4.7-Flash decode (its default: both GEMMs streamed with stream-K)"),
+    ("glm5_decode", 16, "GLM-5 decode, streamed by the ring knob (about 5 blocks per CU)"),
+    ((24, 2048, 96, 6, 1024), 24, "E 96, k 6, I 1024: gate/up K of 32 steps, down K of 16"),
+    ((16, 2048, 64, 8, 1536), 16, "E 64, k 8, I 1536: down K of 24 steps (6 ring periods)"),
+]
+
+
+@pytest.mark.parametrize("knob", [0, 2])
+@pytest.mark.parametrize("case_", STREAMK, ids=[c[-1].split(":")[0] for c in STREAMK])
+def test_streamk_decode_gemms(moe, tune, case_, knob):
+    # streamed decode GEMMs with stream-K (each workgroup one contiguous share of all blocks' K steps, the
+    # blocks cut between two workgroups summed from two fp32 planes by the combine, and with knob value 2 the
+    # gate/up GEMM's too, by its reduction): deterministic, within the bar of the oracle on every token, and
+    # not bitwise the whole-block result (so the cut blocks really ran)
+    name, T, what = case_
+    say("[stream-K, knob %d] %s T=%d" % (knob, what, T))
+    if isinstance(name, str):
+        cfg, h, d = case(name)
+    else:
+        Tc, H, E, k, I = name
+        cfg = wl.MoEConfig(54, "streamk", T=Tc, H=H, E=E, k=k, I=I, Is=I, scale=2.5)
+        h = config_host(cfg)
+        d = to_device(h)
+    tune(MOE_TUNE_RING=3, MOE_TUNE_STREAMK=knob)
+    a = run_forward(moe, cfg, d, T=T)
+    b = run_forward(moe, cfg, d, T=T)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y), "stream-K is not deterministic"
+    tune(MOE_TUNE_STREAMK=1)
+    c = run_forward(moe, cfg, d, T=T)
+    assert np.array_equal(a[1], c[1]) and np.array_equal(a[3], c[3])  # routing untouched
+    # both GEMMs have at least as many blocks as CUs (the folded shared expert is one more group), so both
+    # take stream-K
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = int((a[3] > 0).sum()) + 1
+    blocks = (groups * 2 * cfg.I // 256, groups * ((cfg.H + 255) // 256))
+    say("  %d groups: %d gate/up and %d down blocks on %d CUs" % (groups, blocks[0], blocks[1], cus))
+    assert min(blocks) >= cus, "the shape has too few blocks for stream-K"
+    assert not np.array_equal(a[0], c[0]), "stream-K did not run (outputs bitwise the whole-block ones)"
+    ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(T))
+    same, _, _ = compare_routing(a[1], a[2], ref, what)
+    compare_out(a[0][same], ref["out"][same], "%s stream-K" % what)
+    compare_out(c[0][same], ref["out"][same], "%s whole blocks" % what)
 
 
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
@@ -357,6 +405,52 @@ def test_small_router_shapes(moe, shape):
     compare_out(out[same], ref["out"][same], "small router")
 
 
+def forward_into(m, cfg, d, T, ws):
+    """moe_forward of the first T tokens on the caller's workspace `ws` (sized for any T up to its own)."""
+    out = torch.empty(T, cfg.H, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    m.moe_forward(d["x"][:T], d["wr"], d["b"], d["w1"], d["w3"], d["w2"], d.get("ws1"), d.get("ws3"), d.get("ws2"),
+                  cfg.k, cfg.scale, out, ws, ids, gates, counts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ids.cpu().numpy(), gates.cpu().numpy(), counts.cpu().numpy()
+
+
+ROUTE_PERMUTE = ["glm5_decode", "glm47_decode"] + ["T%d_H%d_E%d_k%d" % s for s in SMALL_ROUTER]
+
+
+@pytest.mark.parametrize("name", ROUTE_PERMUTE)
+def test_route_permute_one_launch_matches_two(moe, tune, name):
+    # up to 16 tokens the router's top-k and the permutation run as one launch whose last workgroup permutes
+    # every token: bit for bit the two launches, over several batch sizes in a row on one workspace (each
+    # call's logits kernel zeroes the ticket the last workgroup is found by; the first call finds whatever
+    # the fresh workspace held), and within the bar of the oracle
+    if name in wl.BY_NAME:
+        cfg, h, d = case(name)
+    else:
+        T, H, E, k = next(s for s in SMALL_ROUTER if "T%d_H%d_E%d_k%d" % s == name)
+        cfg = wl.MoEConfig(53, "small_router", T=T, H=H, E=E, k=k, I=64, Is=64, scale=1.8)
+        h = config_host(cfg)
+        d = to_device(h)
+    sizes = [cfg.T, 1, max(1, cfg.T // 2), 3, cfg.T]
+    say("[route+permute] %s, batches %s" % (name, sizes))
+    nbytes = moe.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.Is)
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    for T in sizes:
+        tune(MOE_TUNE_ROUTE_PERMUTE=0)
+        a = forward_into(moe, cfg, d, T, ws)
+        tune(MOE_TUNE_ROUTE_PERMUTE=1)
+        b = forward_into(moe, cfg, d, T, ws)
+        for x, y, what in zip(a, b, ("out", "ids", "gates", "counts")):
+            assert np.array_equal(x, y), "%s, T=%d: %s differs between one launch and two" % (name, T, what)
+    out, ids, gates, counts = a
+    ref = oracle_forward_rows(h, cfg.k, cfg.scale, np.arange(cfg.T))
+    same, _, _ = compare_routing(ids, gates, ref, name)
+    assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=cfg.E))
+    compare_out(out[same], ref["out"][same], name)
+
+
 STREAM_EDGE = [
     # T, H, E, k, I, what: decode-sized shapes whose K steps make whole ring periods (the streamed GEMMs run)
     (29, 1024, 24, 3, 512, "29 tokens, E 24, k 3"),
@@ -376,7 +470,7 @@ def test_streamed_edge_shapes(moe, tune, shape, ks):
     cfg = wl.MoEConfig(52, "stream_edge", T=T, H=H, E=E, k=k, I=I, Is=I, scale=2.5)
     h = config_host(cfg)
     d = to_device(h)
-    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3)
+    tune(MOE_TUNE_KSPLIT=ks, MOE_TUNE_RING=3, MOE_TUNE_STREAMK=1)
     a = run_forward(moe, cfg, d)
     tune(MOE_TUNE_RING=2)
     b = run_forward(moe, cfg, d)
