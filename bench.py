@@ -73,26 +73,38 @@ class Runner:
             self.m.moe_forward_profiled(*args, events, **kw)
 
     def time(self, steps, warmup):
+        """Mean ms per pass over `steps` timed passes, and the stages of a pass. The timed window records HIP
+        events only around the gate/up launch (self.gate_up_ms, the roofline kernel's launch time, and
+        self.step_ms from each pass's start): every recorded event costs the stream a few microseconds. The
+        split into all six stages comes from a second window of as many passes, after the timed one, with
+        an event at every stage boundary."""
         import torch
 
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
-        for row in ev:  # materialise the HIP events before the timed region
+        gu = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for row in ev + gu:  # materialise the HIP events before the timed region
             for e in row:
                 e.record()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
         for i in range(steps):
-            self.step(events=ev[i])
+            self.step(events=[gu[i][0], None, None, gu[i][1], gu[i][2], None, None])
         end.record()
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
+        self.gate_up_ms = float(np.mean([gu[i][1].elapsed_time(gu[i][2]) for i in range(steps)]))
+        # pass i: from its start to the next pass's start (the last one to the window's end)
+        marks = [gu[i][0] for i in range(steps)] + [end]
+        self.step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+        for i in range(steps):
+            self.step(events=ev[i])
+        torch.cuda.synchronize()
         stages = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                   for j, name in enumerate(STAGES)}
-        self.step_ms = [ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)]
         return ms, stages
 
 
@@ -520,19 +532,20 @@ def main():
         r = Runner(m, cfg, dev_w, host_t, device, two)
         ms, stages = r.time(steps, args.warmup)
         active = int((r.counts.cpu().numpy() > 0).sum())
-        results[cfg.name] = (ms, stages, active, host_t, float(np.median(r.step_ms)))
-        log("%s: %.4f ms/step, stages %s, active experts %d" % (cfg.name, ms, stages, active))
+        results[cfg.name] = (ms, stages, active, host_t, float(np.median(r.step_ms)), r.gate_up_ms)
+        log("%s: %.4f ms/step, gate/up launch %.4f ms, stages %s, active experts %d" % (cfg.name, ms, r.gate_up_ms,
+                                                                                       stages, active))
         del r
         torch.cuda.empty_cache()
 
-    ms_p, st_p, act_p, host_tp, med_p = results[cfg_p.name]
-    ms_d, st_d, act_d, _, med_d = results[cfg_d.name]
-    gu_ms = st_p["gate_up"]
+    ms_p, st_p, act_p, host_tp, med_p, gu_p = results[cfg_p.name]
+    ms_d, st_d, act_d, _, med_d, gu_d = results[cfg_d.name]
+    gu_ms = gu_p
     fold_p, fold_d = shared_folded(cfg_p, m, two), shared_folded(cfg_d, m, two)
     achieved = gate_up_flops(cfg_p, fold_p) / (gu_ms * 1e-3) / 1e12
     layer_tflops = cfg_p.flops() / (ms_p * 1e-3) / 1e12
     dec_gbs = layer_bytes(cfg_d, act_d) / (ms_d * 1e-3) / 1e9
-    dec_gu_gbs = gate_up_bytes(cfg_d, act_d, fold_d) / (st_d["gate_up"] * 1e-3) / 1e9
+    dec_gu_gbs = gate_up_bytes(cfg_d, act_d, fold_d) / (gu_d * 1e-3) / 1e9
 
     line = {
         "metric": METRIC,

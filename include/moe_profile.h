@@ -8,8 +8,10 @@
  *   events[1] after the router                events[5] after the routed down grouped GEMM
  *   events[2] after the permutation           events[6] after the combine (the end of the layer)
  *   events[3] after the shared expert (when it runs on `stream`)
- * hipEventElapsedTime between consecutive events gives each stage's device time. The events stay owned
- * by the caller. With stream_shared non-null the shared expert runs on that stream, forked after the
+ * hipEventElapsedTime between consecutive events gives each stage's device time. A null entry records
+ * nothing at its boundary (each recorded event costs the stream a few microseconds, which a decode-sized
+ * pass notices; a benchmark that wants one stage's time passes only the two events around it). The events
+ * stay owned by the caller. With stream_shared non-null the shared expert runs on that stream, forked after the
  * permutation: events[2] to events[3] is then empty and its time overlaps the routed GEMMs.
  * Pages: as moe_forward (open-model-atlas GLM-5 "MoE transformer block", "All 43 steps").
  */

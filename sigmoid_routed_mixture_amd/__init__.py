@@ -240,10 +240,11 @@ def moe_forward_noalloc(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, 
 def moe_forward_profiled(x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out, workspace, events,
                          topk_ids=None, topk_gates=None, expert_counts=None, stream=None, stream_shared=None):
     """moe_forward that also records seven torch.cuda.Event objects (timing enabled, already recorded once so
-    their HIP events exist) at the stage boundaries; see include/moe_profile.h."""
+    their HIP events exist) at the stage boundaries; see include/moe_profile.h. An entry may be None: that
+    boundary is not recorded."""
     if len(events) != 7:
         raise ValueError("moe_forward_profiled takes 7 events")
-    handles = (ctypes.c_void_p * 7)(*[e.cuda_event for e in events])
+    handles = (ctypes.c_void_p * 7)(*[None if e is None else e.cuda_event for e in events])
     _forward(_lib.moe_forward_profiled, (handles,), x, w_router, bias, w1, w3, w2, ws1, ws3, ws2, k, scale, out,
              workspace, topk_ids, topk_gates, expert_counts, stream, stream_shared)
 

@@ -308,7 +308,7 @@ moe_status forward_impl(const Request& q) {
     if (two_streams) MOE_TRY(device_events(&ev));
 
     auto mark = [&](int i) -> moe_status {
-        if (q.events == nullptr) return MOE_OK;
+        if (q.events == nullptr || q.events[i] == nullptr) return MOE_OK;
         return from_hip(hipEventRecord(static_cast<hipEvent_t>(q.events[i]), s0), "hipEventRecord (profile)");
     };
     MOE_TRY(mark(0));
