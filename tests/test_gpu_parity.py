@@ -292,6 +292,31 @@ def test_streamk_decode_gemms(moe, tune, case_, knob):
     compare_out(c[0][same], ref["out"][same], "%s whole blocks" % what)
 
 
+@pytest.mark.parametrize("name", ["tiny", "glm47_decode"])
+def test_profiled_entry_matches_forward(moe, name):
+    # moe_forward_profiled computes what moe_forward computes, with events at every stage boundary or only
+    # around the gate/up launch (null entries record nothing), and its stage intervals add up to the pass
+    say("[profiled] %s" % name)
+    cfg, h, d = case(name)
+    a = run_forward(moe, cfg, d)
+    for pick in (range(7), (0, 3, 4)):
+        ev = [torch.cuda.Event(enable_timing=True) if i in pick else None for i in range(7)]
+        for e in ev:
+            if e is not None:
+                e.record()
+        torch.cuda.synchronize()
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.float32, device="cuda")
+        ws = torch.empty(moe.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.Is), dtype=torch.uint8,
+                         device="cuda")
+        moe.moe_forward_profiled(d["x"], d["wr"], d["b"], d["w1"], d["w3"], d["w2"], d["ws1"], d["ws3"], d["ws2"],
+                                 cfg.k, cfg.scale, out, ws, ev)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), a[0])
+        marks = [e for e in ev if e is not None]
+        spans = [marks[i].elapsed_time(marks[i + 1]) for i in range(len(marks) - 1)]
+        assert min(spans) >= 0.0
+
+
 @pytest.mark.parametrize("name", ["mid", "glm47_prefill"])
 def test_persistent_grid_does_not_change_results(moe, tune, name):
     # one workgroup per CU claiming blocks from the XCD counters (and from the back of other XCDs' ranges
